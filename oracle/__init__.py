@@ -1,0 +1,158 @@
+"""CPU oracle of the ReLU-gated sparse FFN forward (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY: this package may be imported only by ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``.
+The product path (the HIP library and its binding) never imports, links or
+runs it, and it imports nothing from the product path.
+
+The arithmetic lives in ``tw_oracle.c`` (plain sequential double loops, each
+function citing the passage of "Sparser, Faster, Lighter Transformer Language
+Models Review" it follows).  This wrapper only widens bfloat16 bit patterns
+to double (exact) and marshals numpy arrays.
+
+Pinned by the ``-m "not gpu"`` tests: a hand-worked example
+(``tests/golden/handworked_4x4x8.txt``), exact brute force with Python
+integers on small integer matrices, one-hot token rows, the row-wide ELL and
+lossless special cases, exact density 0 and 1, the invariants (each active
+entry appears exactly once, counts sum to the number of non-zeros, the
+sparse evaluation equals the dense one bit for bit), and planted mistakes
+that each of these must catch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "tw_oracle.c")
+LIBRARY = os.path.join(_HERE, "libtw_oracle.so")
+
+CFLAGS = ["-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(src: str = SOURCE, out: str = LIBRARY, extra=()) -> str:
+    """Compile the oracle with gcc (no HIP involved)."""
+    cmd = ["gcc", *CFLAGS, *extra, src, "-o", out + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64, exactly."""
+    b = np.asarray(bits)
+    if b.dtype == np.float64:
+        return np.ascontiguousarray(b)
+    if b.dtype != np.uint16:
+        raise TypeError(f"expected uint16 bf16 bits or float64, got {b.dtype}")
+    f32 = (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return np.ascontiguousarray(f32, dtype=np.float64)
+
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int32)
+_U8 = ctypes.POINTER(ctypes.c_uint8)
+_int = ctypes.c_int
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+class Oracle:
+    """Handle on one build of the oracle library."""
+
+    def __init__(self, path: str = LIBRARY):
+        if path == LIBRARY and not os.path.exists(path):
+            build()
+        self.path = path
+        self.lib = ctypes.CDLL(path)
+        L = self.lib
+        L.tw_oracle_threads.restype = _int
+        L.tw_oracle_gate.argtypes = [_D, _D, _int, _int, _int, _D]
+        L.tw_oracle_pack.argtypes = [_D, _int, _int, _int, _int, _int, _I, _I, _D, _U8, _I, _I]
+        L.tw_oracle_dense_ffn.argtypes = [_D, _D, _D, _D, _int, _int, _int, _D]
+        L.tw_oracle_sparse_ffn.argtypes = [_D, _D, _D, _D, _int, _int, _int, _int, _int,
+                                           _I, _I, _D, _D]
+        for f in ("tw_oracle_gate", "tw_oracle_pack", "tw_oracle_dense_ffn",
+                  "tw_oracle_sparse_ffn"):
+            getattr(L, f).restype = None
+
+    def threads(self) -> int:
+        return int(self.lib.tw_oracle_threads())
+
+    def gate(self, x, wg_t) -> np.ndarray:
+        """z = x W_g as float64 [M, N]."""
+        x, wg = widen_bf16(x), widen_bf16(wg_t)
+        M, K = x.shape
+        N = wg.shape[0]
+        assert wg.shape == (N, K)
+        z = np.empty((M, N), dtype=np.float64)
+        self.lib.tw_oracle_gate(_p(x, _D), _p(wg, _D), M, K, N, _p(z, _D))
+        return z
+
+    def pack(self, z, T: int, C: int, R_max: int) -> dict:
+        """TwELL packing + overflow routing of any gate matrix z [M, N].
+
+        ``z`` may be the oracle's own float64 gate or a float32 gate produced
+        elsewhere; float32 is widened exactly, so packed values keep its bits.
+        """
+        z = np.ascontiguousarray(np.asarray(z), dtype=np.float64)
+        M, N = z.shape
+        if T <= 0 or N % T or not (1 <= C <= T) or R_max < 0:
+            raise ValueError("bad T / C / R_max")
+        NT = N // T
+        cnt = np.empty((M, NT), dtype=np.int32)
+        idx = np.empty((M, NT, C), dtype=np.int32)
+        val = np.empty((M, NT, C), dtype=np.float64)
+        flag = np.empty(M, dtype=np.uint8)
+        ovf = np.full(max(R_max, 1), -1, dtype=np.int32)
+        count = np.zeros(1, dtype=np.int32)
+        self.lib.tw_oracle_pack(_p(z, _D), M, N, T, C, R_max, _p(cnt, _I), _p(idx, _I),
+                                _p(val, _D), _p(flag, _U8), _p(ovf, _I), _p(count, _I))
+        c = int(count[0])
+        return {"cnt": cnt, "idx": idx, "val": val, "flag": flag,
+                "ovf_rows": ovf[: min(c, R_max)].copy(), "ovf_count": c}
+
+    def dense_ffn(self, x, wg_t, wu_t, wd) -> np.ndarray:
+        """y = (ReLU(x W_g) * (x W_u)) W_d as float64 [M, K]."""
+        x, wg, wu, w_d = (widen_bf16(a) for a in (x, wg_t, wu_t, wd))
+        M, K = x.shape
+        N = wg.shape[0]
+        assert wg.shape == wu.shape == w_d.shape == (N, K)
+        y = np.empty((M, K), dtype=np.float64)
+        self.lib.tw_oracle_dense_ffn(_p(x, _D), _p(wg, _D), _p(wu, _D), _p(w_d, _D),
+                                     M, K, N, _p(y, _D))
+        return y
+
+    def sparse_ffn(self, x, wg_t, wu_t, wd, T: int, C: int, packed: dict) -> np.ndarray:
+        """y from a TwELL packing (dense recompute for overflow rows)."""
+        x, wg, wu, w_d = (widen_bf16(a) for a in (x, wg_t, wu_t, wd))
+        M, K = x.shape
+        N = wg.shape[0]
+        cnt = np.ascontiguousarray(packed["cnt"], dtype=np.int32)
+        idx = np.ascontiguousarray(packed["idx"], dtype=np.int32)
+        val = np.ascontiguousarray(packed["val"], dtype=np.float64)
+        assert cnt.shape == (M, N // T) and idx.shape == val.shape == (M, N // T, C)
+        y = np.empty((M, K), dtype=np.float64)
+        self.lib.tw_oracle_sparse_ffn(_p(x, _D), _p(wg, _D), _p(wu, _D), _p(w_d, _D),
+                                      M, K, N, T, C, _p(cnt, _I), _p(idx, _I), _p(val, _D),
+                                      _p(y, _D))
+        return y
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``tw_oracle.c`` (built on first use)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default

@@ -1,0 +1,81 @@
+"""Planted mistakes in the oracle must each be caught by some pin.
+
+Every mutant is a copy of ``oracle/tw_oracle.c`` with one plausible mistake
+(a dropped term, a wrong comparison, a wrong index, a transposed operand, a
+swapped matrix, a wrong order), compiled into its own library on the CPU.
+The pins of ``oracle_pins.py`` run against it and at least one must fail;
+otherwise the pins would not notice that kind of mistake in the real oracle.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+with open(oracle.SOURCE) as _f:
+    _SRC = _f.read()
+
+# (name, exact text in tw_oracle.c, replacement) or (name, [text, repl], [text, repl], ...)
+# Every mutant keeps all memory accesses in bounds.
+MUTANTS = [
+    ("dot drops last term", "for (int k = 0; k < K; ++k)\n        s += a[k] * b[k];",
+     "for (int k = 0; k < K - 1; ++k)\n        s += a[k] * b[k];"),
+    ("zero counted active", "if (g > 0.0) {\n                    if (n < C)",
+     "if (g >= 0.0) {\n                    if (n < C)"),
+    ("relu keeps negatives", "return v > 0.0 ? v : 0.0;", "return v;"),
+    ("tile-local index", "idx[tile * C + n] = j;", "idx[tile * C + n] = j - t * T;"),
+    ("count clipped to capacity", "cnt[tile] = n;", "cnt[tile] = n < C ? n : C;"),
+    ("overflow at capacity", "if (n > C)\n                over = 1;",
+     "if (n >= C)\n                over = 1;"),
+    ("routing list descending", "for (int m = 0; m < M; ++m) {\n        if (flag[m]) {",
+     "for (int m = M - 1; m >= 0; --m) {\n        if (flag[m]) {"),
+    ("count clipped to R_max", "*ovf_count = r;", "*ovf_count = r < R_max ? r : R_max;"),
+    ("up uses gate weights",
+     "const double u = dot(xm, wu_t + (size_t)j * K, K);\n        const double h = u * g;\n        const double *wdj",
+     "const double u = dot(xm, wg_t + (size_t)j * K, K);\n        const double h = u * g;\n        const double *wdj"),
+    ("h adds instead of multiplies",
+     "const double h = u * g;\n        const double *wdj = wd + (size_t)j * K;\n        for (int k = 0; k < K; ++k)\n            ym[k] += h * wdj[k];\n    }\n}",
+     "const double h = u + g;\n        const double *wdj = wd + (size_t)j * K;\n        for (int k = 0; k < K; ++k)\n            ym[k] += h * wdj[k];\n    }\n}"),
+    ("down weights read transposed",
+     "for (int k = 0; k < K; ++k)\n            ym[k] += h * wdj[k];\n    }\n}",
+     "for (int k = 0; k < K; ++k)\n            ym[k] += h * wd[(size_t)k * N + j];\n    }\n}"),
+    ("gate row stride", "z[(size_t)m * N + j] = dot(x + (size_t)m * K, wg_t + (size_t)j * K, K);",
+     "z[(size_t)m * N + j] = dot(x + (size_t)m, wg_t + (size_t)j * K, K);"),
+    ("sparse drops last slot", "for (int s = 0; s < cnt[tile]; ++s) {",
+     "for (int s = 0; s + 1 < cnt[tile]; ++s) {"),
+    ("sparse ignores gate value", "const double g = val[tile * C + s];",
+     "const double g = 1.0;"),
+    # overflow rows evaluated from their truncated packing instead of the
+    # dense backup (the slot loop is clamped so the mutant stays in bounds)
+    ("no dense backup", ["if (over) {\n            dense_row", "if (0) {\n            dense_row"],
+     ["for (int s = 0; s < cnt[tile]; ++s) {", "for (int s = 0; s < cnt[tile] && s < C; ++s) {"]),
+    ("sparse sign flip", "const double h = u * g;\n                const double *wdj",
+     "const double h = -u * g;\n                const double *wdj"),
+]
+
+
+def _edits(m):
+    if isinstance(m[1], str):
+        return [(m[1], m[2])]
+    return [tuple(e) for e in m[1:]]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, mutant):
+    name = mutant[0]
+    text = _SRC
+    for orig, repl in _edits(mutant):
+        assert text.count(orig) == 1, f"mutation anchor for '{name}' not unique in tw_oracle.c"
+        text = text.replace(orig, repl)
+    src = tmp_path / "mutant.c"
+    src.write_text(text)
+    lib = oracle.build(str(src), str(tmp_path / "libmutant.so"))
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake '{name}'"
