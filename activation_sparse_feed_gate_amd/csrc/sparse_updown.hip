@@ -1,0 +1,225 @@
+// sparse_updown.hip -- fused sparse up + down projection over a TwELL gate.
+//
+// Method: "Sparser, Faster, Lighter Transformer Language Models Review",
+// section 3-5 equation: for token row m, y_m is the sum over its active
+// hidden indices n of (h_g)_{m,n} * (x_m . W_u[:, n]) * W_d[n, :].  Only the
+// up column and the down row of an active neuron are read, the up
+// activation is a scalar formed in the kernel, and neither h_u nor h is ever
+// written to memory.
+//
+// gfx950 design
+// - One workgroup (4 wavefronts) per token row.  The row's tile counts are
+//   read once; a row with any tile over capacity is left to the dense
+//   backup.  A block-wide scan of the counts gives every packed entry a flat
+//   position, and entry f goes to wave f % 4, so the active neurons of a
+//   heavy row are shared by four waves.
+// - Within a wave, lane l owns the 16-byte chunks l, l+64, ... of a K-row:
+//   the gathers of W_u^T[j] and W_d[j] are fully coalesced 1 KB wave loads,
+//   x_m stays in registers for the whole row, and y_m accumulates in fp32
+//   registers.  Entries are taken four at a time so that eight row loads are
+//   in flight before the first dot product needs its data.
+// - The dot product is reduced across the wave with DPP (no LDS), its
+//   product with g is the scalar h_j, and h_j * W_d[j] is added lane-wise.
+// - The four partial y rows are summed in LDS in a fixed order (the result
+//   does not depend on timing) and written once, coalesced.
+#include "tw_device.hpp"
+#include "tw_internal.hpp"
+
+namespace tw {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <int KCH>
+__global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wu_t,
+    const uint16_t *__restrict__ wd, int K, int N, int NT, int C,
+    const float *__restrict__ tw_val,
+    const int32_t *__restrict__ tw_idx, const int32_t *__restrict__ tw_cnt,
+    float *__restrict__ y) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];  // [kWaves][K] fp32
+    __shared__ int s_off[kThreads + 1];
+    __shared__ int s_wtot[kWaves];
+
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+
+    const int c = tid < NT ? tw_cnt[(size_t)m * NT + tid] : 0;
+    if (__syncthreads_or(c > C)) return;  // overflow row: dense backup
+
+    // exclusive scan of the tile counts -> flat entry offsets
+    int incl = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) s_wtot[wave] = incl;
+    __syncthreads();
+    int wb = 0;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q)
+        if (q < wave) wb += s_wtot[q];
+    s_off[tid] = wb + incl - c;
+    if (tid == kThreads - 1) s_off[kThreads] = wb + incl;
+    __syncthreads();
+    const int nnz = s_off[kThreads];
+
+    const int KC = K >> 3;  // 16-byte chunks per K-row
+    float *yrow = y + (size_t)m * K;
+    if (nnz == 0) {
+        for (int q = tid; q < 2 * KC; q += kThreads)
+            st16(yrow + 4 * q, u32x4{0u, 0u, 0u, 0u});
+        return;
+    }
+
+    u32x4 xr[KCH];
+#pragma unroll
+    for (int ch = 0; ch < KCH; ++ch) {
+        const int q = lane + 64 * ch;
+        xr[ch] = q < KC ? ld16(x + (size_t)m * K + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float yacc[KCH][8];
+#pragma unroll
+    for (int ch = 0; ch < KCH; ++ch)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yacc[ch][e] = 0.0f;
+
+    // entries of this wave: f = wave + 4 * e, e < ne
+    const int ne = (nnz - wave + kWaves - 1) / kWaves;
+    for (int e0 = 0; e0 < ne; e0 += 64) {
+        // lane resolves entry e0 + lane: tile by binary search over s_off
+        int jl = 0;
+        float gl = 0.0f;
+        if (e0 + lane < ne) {
+            const int f = wave + kWaves * (e0 + lane);
+            int lo = 0, hi = NT;
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_off[mid] <= f) lo = mid;
+                else hi = mid;
+            }
+            const size_t q = ((size_t)m * NT + lo) * C + (f - s_off[lo]);
+            // an index outside [0, N) can only come from a corrupt packing;
+            // clamp it so that the gathers stay inside the weights
+            jl = min((unsigned)tw_idx[q], (unsigned)(N - 1));
+            gl = tw_val[q];
+        }
+        const int nb = min(64, ne - e0);
+        for (int b = 0; b < nb; b += 4) {
+            int j[4];
+            float g[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = b + u < nb;
+                const int src = ok ? b + u : b;
+                j[u] = __builtin_amdgcn_readlane(jl, src);
+                g[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), src))
+                          : 0.0f;
+            }
+            u32x4 wu[4][KCH], wv[4][KCH];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint16_t *pu = wu_t + (size_t)j[u] * K;
+                const uint16_t *pd = wd + (size_t)j[u] * K;
+#pragma unroll
+                for (int ch = 0; ch < KCH; ++ch) {
+                    const int q = lane + 64 * ch;
+                    const bool in = q < KC;
+                    wu[u][ch] = in ? ld16(pu + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+                    wv[u][ch] = in ? ld16(pd + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            float p[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float s = 0.0f;
+#pragma unroll
+                for (int ch = 0; ch < KCH; ++ch)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        s += bf_lo(xr[ch][w]) * bf_lo(wu[u][ch][w]);
+                        s += bf_hi(xr[ch][w]) * bf_hi(wu[u][ch][w]);
+                    }
+                p[u] = s;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) p[u] = wave_sum(p[u]) * g[u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int ch = 0; ch < KCH; ++ch)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        yacc[ch][2 * w] += p[u] * bf_lo(wv[u][ch][w]);
+                        yacc[ch][2 * w + 1] += p[u] * bf_hi(wv[u][ch][w]);
+                    }
+        }
+    }
+
+    float *s_y = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int ch = 0; ch < KCH; ++ch) {
+        const int q = lane + 64 * ch;
+        if (q < KC) {
+            float *d = s_y + (size_t)wave * K + 8 * q;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d[e] = yacc[ch][e];
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < 2 * KC; q += kThreads) {
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = s_y[4 * q + e];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) v += s_y[(size_t)w * K + 4 * q + e];
+            r[e] = v;
+        }
+        st16(yrow + 4 * q, u32x4{__float_as_uint(r[0]), __float_as_uint(r[1]),
+                                 __float_as_uint(r[2]), __float_as_uint(r[3])});
+    }
+}
+
+template <int KCH>
+hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
+                    int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
+                    const int32_t *tw_cnt, float *y, hipStream_t s) {
+    const size_t lds = (size_t)kWaves * K * sizeof(float);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_updown_kernel<KCH>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kWaves * 4096 * 4);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(sparse_updown_kernel<KCH>, dim3(M), dim3(kThreads), lds, s, x, wu_t, wd, K,
+                       N, NT, C, tw_val, tw_idx, tw_cnt, y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
+                                int M, int K, int N, int T, int C, const float *tw_val,
+                                const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
+                                hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    const int NT = N / T;
+    switch ((K + 511) / 512) {
+    case 1: return launch_k<1>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    case 2: return launch_k<2>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    case 3: return launch_k<3>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    case 4: return launch_k<4>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    case 5: return launch_k<5>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    case 6: return launch_k<6>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    case 7: return launch_k<7>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    default: return launch_k<8>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    }
+}
+
+}  // namespace tw

@@ -1,0 +1,201 @@
+// tw_api.cpp -- the C ABI declared in include/tw.h: argument validation,
+// workspace carving, kernel launches on the caller's stream.
+#include "tw.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "tw_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tw_status fail(tw_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Shape checks shared by the TwELL entry points.
+tw_status check_shape(int M, int K, int N, int T, int C, int R_max) {
+    if (M < 0 || K <= 0 || N <= 0) return fail(TW_EINVAL, "M=%d K=%d N=%d: need M >= 0, K, N > 0", M, K, N);
+    if (T != 128 && T != 256) return fail(TW_EUNSUPPORTED, "tile width T=%d: supported 128, 256", T);
+    if (N % T) return fail(TW_EINVAL, "N=%d is not a multiple of T=%d", N, T);
+    if (N / T > 256) return fail(TW_EUNSUPPORTED, "N/T=%d tiles per row: at most 256", N / T);
+    if (C < 1 || C > T) return fail(TW_EINVAL, "capacity C=%d outside [1, T=%d]", C, T);
+    if (K % 128) return fail(TW_EUNSUPPORTED, "K=%d: must be a multiple of 128", K);
+    if (K > 4096) return fail(TW_EUNSUPPORTED, "K=%d: at most 4096", K);
+    if (R_max < 0 || R_max > M) return fail(TW_EINVAL, "R_max=%d outside [0, M=%d]", R_max, M);
+    return TW_OK;
+}
+
+size_t pack_ws(int M, int N) {
+    return round_up((size_t)tw::gate_col_blocks(N) * tw::row_words(M) * 4, 256);
+}
+size_t sparse_ws(int R_max, int N) { return round_up((size_t)R_max * N * 2, 256); }
+
+tw_status record(void *const *events, int i, hipStream_t s) {
+    if (!events) return TW_OK;
+    hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[i]), s);
+    if (e != hipSuccess) return fail(TW_EHIP, "hipEventRecord(events[%d]): %s", i, hipGetErrorString(e));
+    return TW_OK;
+}
+
+tw_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(TW_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return TW_OK;
+}
+
+#define TW_TRY(expr)                      \
+    do {                                  \
+        tw_status st_ = (expr);           \
+        if (st_ != TW_OK) return st_;     \
+    } while (0)
+
+#define TW_NEED(p)                                                                   \
+    do {                                                                             \
+        if (!(p)) return fail(TW_EINVAL, "%s is NULL", #p);                          \
+        if (!aligned16(p)) return fail(TW_EINVAL, "%s is not 16-byte aligned", #p);  \
+    } while (0)
+
+// Buffers sized by M may be NULL when M == 0.
+#define TW_NEED_M(p)                                                                 \
+    do {                                                                             \
+        if (M > 0 || (p)) TW_NEED(p);                                                \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *tw_status_str(int status) {
+    switch (status) {
+    case TW_OK: return "TW_OK";
+    case TW_EINVAL: return "TW_EINVAL";
+    case TW_EUNSUPPORTED: return "TW_EUNSUPPORTED";
+    case TW_EHIP: return "TW_EHIP";
+    default: return "TW_UNKNOWN";
+    }
+}
+
+const char *tw_last_error(void) { return g_err; }
+
+size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max) {
+    char saved[sizeof g_err];
+    std::snprintf(saved, sizeof saved, "%s", g_err);
+    const tw_status st = check_shape(M, K, N, T, C, R_max);
+    std::snprintf(g_err, sizeof g_err, "%s", saved);
+    if (st != TW_OK) return 0;
+    size_t a = pack_ws(M, N), b = sparse_ws(R_max, N);
+    return (a > b ? a : b) + 256;
+}
+
+size_t tw_ffn_workspace_bytes(int M, int K, int N) {
+    if (M < 0 || K <= 0 || N <= 0) return 0;
+    return round_up((size_t)M * N * 2, 256) + 256;
+}
+
+tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int T,
+                       int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                       int32_t *ovf_rows, int32_t *ovf_count, int R_max, float *z_debug,
+                       void *ws, size_t ws_bytes, void *stream, void *const *events) {
+    TW_TRY(check_shape(M, K, N, T, C, R_max));
+    TW_NEED_M(x);
+    TW_NEED(wg_t);
+    TW_NEED_M(tw_val);
+    TW_NEED_M(tw_idx);
+    TW_NEED_M(tw_cnt);
+    TW_NEED(ovf_rows);
+    TW_NEED(ovf_count);
+    TW_NEED(ws);
+    if (z_debug && !aligned16(z_debug)) return fail(TW_EINVAL, "z_debug is not 16-byte aligned");
+    const size_t need = tw_workspace_bytes(M, K, N, T, C, R_max);
+    if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *oflag = static_cast<uint32_t *>(ws);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_gate_twell(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, oflag,
+                                          z_debug, s),
+                    "gate_twell launch"));
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_col_blocks(N), tw::row_words(M), R_max,
+                                           ovf_rows, ovf_count, s),
+                    "ovf_compact launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t,
+                            const uint16_t *wd, int M, int K, int N, int T, int C,
+                            const float *tw_val, const int32_t *tw_idx, const int32_t *tw_cnt,
+                            const int32_t *ovf_rows, const int32_t *ovf_count, int R_max,
+                            float *y, void *ws, size_t ws_bytes, void *stream,
+                            void *const *events) {
+    TW_TRY(check_shape(M, K, N, T, C, R_max));
+    TW_NEED_M(x);
+    TW_NEED(wg_t);
+    TW_NEED(wu_t);
+    TW_NEED(wd);
+    TW_NEED_M(tw_val);
+    TW_NEED_M(tw_idx);
+    TW_NEED_M(tw_cnt);
+    TW_NEED(ovf_rows);
+    TW_NEED(ovf_count);
+    TW_NEED_M(y);
+    TW_NEED(ws);
+    const size_t need = tw_workspace_bytes(M, K, N, T, C, R_max);
+    if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint16_t *h = static_cast<uint16_t *>(ws);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx, tw_cnt,
+                                             y, s),
+                    "sparse_updown launch"));
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_gateup(x, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, s),
+                    "fallback gate+up launch"));
+    TW_TRY(record(events, 2, s));
+    TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, s),
+                    "fallback down launch"));
+    TW_TRY(record(events, 3, s));
+    return TW_OK;
+}
+
+tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t,
+                     const uint16_t *wd, int M, int K, int N, float *y, void *ws,
+                     size_t ws_bytes, void *stream, void *const *events) {
+    if (M < 0 || K <= 0 || N <= 0) return fail(TW_EINVAL, "M=%d K=%d N=%d: need M >= 0, K, N > 0", M, K, N);
+    if (N % 128) return fail(TW_EUNSUPPORTED, "N=%d: must be a multiple of 128", N);
+    if (K % 128) return fail(TW_EUNSUPPORTED, "K=%d: must be a multiple of 128", K);
+    TW_NEED_M(x);
+    TW_NEED(wg_t);
+    TW_NEED(wu_t);
+    TW_NEED(wd);
+    TW_NEED_M(y);
+    TW_NEED(ws);
+    const size_t need = tw_ffn_workspace_bytes(M, K, N);
+    if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint16_t *h = static_cast<uint16_t *>(ws);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_gateup(x, wg_t, wu_t, K, N, nullptr, nullptr, M, h, s),
+                    "dense gate+up launch"));
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, s), "dense down launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// tw_internal.hpp -- launchers of the gfx950 kernels behind the C ABI.
+// Every launcher only enqueues work on `s` and returns the launch status; the
+// C ABI layer validates all arguments before calling them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tw {
+
+// Gate GEMM macro tile: 256 token rows x 256 hidden columns.
+constexpr int kGateBM = 256;
+constexpr int kGateBN = 256;
+
+inline int gate_col_blocks(int N) { return (N + kGateBN - 1) / kGateBN; }
+inline int row_words(int M) { return (M + 31) / 32; }
+
+hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
+                             int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                             uint32_t *oflag, float *z_debug, hipStream_t s);
+
+hipError_t launch_ovf_compact(const uint32_t *oflag, int NB, int MW, int R_max,
+                              int32_t *ovf_rows, int32_t *ovf_count, hipStream_t s);
+
+hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
+                                int M, int K, int N, int T, int C, const float *tw_val,
+                                const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
+                                hipStream_t s);
+
+// h[r][n] = bf16(ReLU(x_r . wg_t[n]) * (x_r . wu_t[n])) for r < rows, where
+// x_r is x[rowlist[r]] (rowlist != nullptr, rows = min(*count, R_cap)) or
+// x[r] (rowlist == nullptr, rows = R_cap).
+hipError_t launch_gateup(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t,
+                         int K, int N, const int32_t *rowlist, const int32_t *count,
+                         int R_cap, uint16_t *h, hipStream_t s);
+
+// y[row_r][k] = sum_n h[r][n] * wd[n][k] (fp32) for r < rows, with row_r =
+// rowlist[r] or r as above.
+hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
+                       const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
+                       hipStream_t s);
+
+}  // namespace tw

@@ -1,0 +1,203 @@
+"""Python binding of the HIP library ``libtw.so`` (C ABI in ``include/tw.h``).
+
+Argument marshalling only: every step of the forward runs in the library's
+gfx950 kernels.  PyTorch provides device memory and the current HIP stream.
+Importing this module fails loudly when the library has not been built
+(``python -m activation_sparse_feed_gate_amd.build``); there is no fallback.
+
+Low-level functions carry the C names and take preallocated tensors:
+``tw_pack_gate``, ``tw_sparse_ffn_fwd``, ``tw_ffn_fwd``, ``tw_workspace_bytes``,
+``tw_ffn_workspace_bytes``.  ``pack_gate``, ``sparse_ffn`` and ``ffn``
+allocate their outputs and return them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library links against
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libtw.so")
+
+if not os.path.exists(LIBRARY):
+    raise ImportError(
+        f"{LIBRARY} is missing: build it with `python -m activation_sparse_feed_gate_amd.build`")
+
+_lib = ctypes.CDLL(LIBRARY)
+
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+_lib.tw_status_str.restype = ctypes.c_char_p
+_lib.tw_status_str.argtypes = [_i]
+_lib.tw_last_error.restype = ctypes.c_char_p
+_lib.tw_last_error.argtypes = []
+_lib.tw_workspace_bytes.restype = _sz
+_lib.tw_workspace_bytes.argtypes = [_i] * 6
+_lib.tw_ffn_workspace_bytes.restype = _sz
+_lib.tw_ffn_workspace_bytes.argtypes = [_i] * 3
+_lib.tw_pack_gate.restype = _i
+_lib.tw_pack_gate.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
+                              _vp, _sz, _vp, _vp]
+_lib.tw_sparse_ffn_fwd.restype = _i
+_lib.tw_sparse_ffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                   _vp, _i, _vp, _vp, _sz, _vp, _vp]
+_lib.tw_ffn_fwd.restype = _i
+_lib.tw_ffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp, _vp]
+
+TW_OK, TW_EINVAL, TW_EUNSUPPORTED, TW_EHIP = 0, 1, 2, 3
+
+
+class TwError(RuntimeError):
+    """A non-OK status from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.tw_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {_lib.tw_status_str(status).decode()}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != TW_OK:
+        raise TwError(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous device tensors")
+    return t.data_ptr()
+
+
+def _dtype(t, dt, name):
+    if t.dtype != dt:
+        raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _events(events):
+    if events is None:
+        return None
+    arr = (ctypes.c_void_p * len(events))(*[int(e) for e in events])
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+# ----------------------------------------------------------------- C names --
+def tw_workspace_bytes(M, K, N, T, C, R_max) -> int:
+    return int(_lib.tw_workspace_bytes(M, K, N, T, C, R_max))
+
+
+def tw_ffn_workspace_bytes(M, K, N) -> int:
+    return int(_lib.tw_ffn_workspace_bytes(M, K, N))
+
+
+def tw_pack_gate(x, wg_t, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_max, ws,
+                 z_debug=None, stream=None, events=None) -> None:
+    M, K = x.shape
+    N = wg_t.shape[0]
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(wg_t, torch.bfloat16, "wg_t")
+    ev = _events(events)
+    st = _lib.tw_pack_gate(_ptr(x), _ptr(wg_t), M, K, N, T, C, _ptr(tw_val), _ptr(tw_idx),
+                           _ptr(tw_cnt), _ptr(ovf_rows), _ptr(ovf_count), R_max, _ptr(z_debug),
+                           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
+                           ev[0] if ev else None)
+    _check(st, "tw_pack_gate")
+
+
+def tw_sparse_ffn_fwd(x, wg_t, wu_t, wd, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count,
+                      R_max, y, ws, stream=None, events=None) -> None:
+    M, K = x.shape
+    N = wg_t.shape[0]
+    for t, n in ((x, "x"), (wg_t, "wg_t"), (wu_t, "wu_t"), (wd, "wd")):
+        _dtype(t, torch.bfloat16, n)
+    _dtype(y, torch.float32, "y")
+    ev = _events(events)
+    st = _lib.tw_sparse_ffn_fwd(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), M, K, N, T, C,
+                                _ptr(tw_val), _ptr(tw_idx), _ptr(tw_cnt), _ptr(ovf_rows),
+                                _ptr(ovf_count), R_max, _ptr(y), _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream),
+                                ev[0] if ev else None)
+    _check(st, "tw_sparse_ffn_fwd")
+
+
+def tw_ffn_fwd(x, wg_t, wu_t, wd, y, ws, stream=None, events=None) -> None:
+    M, K = x.shape
+    N = wg_t.shape[0]
+    for t, n in ((x, "x"), (wg_t, "wg_t"), (wu_t, "wu_t"), (wd, "wd")):
+        _dtype(t, torch.bfloat16, n)
+    _dtype(y, torch.float32, "y")
+    ev = _events(events)
+    st = _lib.tw_ffn_fwd(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), M, K, N, _ptr(y), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream(stream), ev[0] if ev else None)
+    _check(st, "tw_ffn_fwd")
+
+
+# ------------------------------------------------------------- allocating --
+def alloc_pack(M, N, T, C, R_max, device="cuda"):
+    """Output buffers of tw_pack_gate."""
+    NT = N // T
+    return {
+        "tw_val": torch.empty((M, NT, C), dtype=torch.float32, device=device),
+        "tw_idx": torch.empty((M, NT, C), dtype=torch.int32, device=device),
+        "tw_cnt": torch.empty((M, NT), dtype=torch.int32, device=device),
+        "ovf_rows": torch.empty((max(R_max, 1),), dtype=torch.int32, device=device),
+        "ovf_count": torch.empty((1,), dtype=torch.int32, device=device),
+    }
+
+
+def workspace(M, K, N, T, C, R_max, device="cuda"):
+    n = tw_workspace_bytes(M, K, N, T, C, R_max)
+    if n == 0:
+        raise ValueError("unsupported shape for the TwELL path")
+    return torch.empty((n,), dtype=torch.uint8, device=device)
+
+
+def pack_gate(x, wg_t, T, C, R_max=None, z_debug=False, ws=None):
+    """Gate GEMM + ReLU + TwELL packing; returns the packing as a dict."""
+    M, K = x.shape
+    N = wg_t.shape[0]
+    R_max = M if R_max is None else R_max
+    out = alloc_pack(M, N, T, C, R_max, x.device)
+    ws = workspace(M, K, N, T, C, R_max, x.device) if ws is None else ws
+    z = torch.empty((M, N), dtype=torch.float32, device=x.device) if z_debug else None
+    tw_pack_gate(x, wg_t, T, C, out["tw_val"], out["tw_idx"], out["tw_cnt"], out["ovf_rows"],
+                 out["ovf_count"], R_max, ws, z_debug=z)
+    if z_debug:
+        out["z"] = z
+    out.update(T=T, C=C, R_max=R_max)
+    return out
+
+
+def sparse_ffn(x, wg_t, wu_t, wd, packed, ws=None):
+    """Sparse up+down (and dense fallback) from a packing; returns y fp32."""
+    M, K = x.shape
+    N = wg_t.shape[0]
+    T, C, R_max = packed["T"], packed["C"], packed["R_max"]
+    y = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    ws = workspace(M, K, N, T, C, R_max, x.device) if ws is None else ws
+    tw_sparse_ffn_fwd(x, wg_t, wu_t, wd, T, C, packed["tw_val"], packed["tw_idx"],
+                      packed["tw_cnt"], packed["ovf_rows"], packed["ovf_count"], R_max, y, ws)
+    return y
+
+
+def ffn(x, wg_t, wu_t, wd, ws=None):
+    """Dense gated FFN over all rows; returns y fp32."""
+    M, K = x.shape
+    N = wg_t.shape[0]
+    y = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty((tw_ffn_workspace_bytes(M, K, N),), dtype=torch.uint8, device=x.device)
+    tw_ffn_fwd(x, wg_t, wu_t, wd, y, ws)
+    return y
+
+
+def library_path() -> str:
+    return LIBRARY

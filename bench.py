@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the TwELL sparse gated-FFN forward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic
+tokens: ``tw_pack_gate`` (gate GEMM + ReLU + TwELL packing, overflow list)
+then ``tw_sparse_ffn_fwd`` (fused sparse up+down, dense fallback for the
+overflow rows).  Inputs are resident in HBM before the timed region.  The
+dense gated FFN ``tw_ffn_fwd`` is timed the same way at the same shape for
+the speedup.  Per-kernel durations come from HIP events recorded on the
+launch stream between the library's kernels.
+
+Prints one JSON line (rank 0, one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-FFN fwd tokens/s + %HBM/%MFMA roofline; speedup vs dense FFN @99% sparse"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            out.append(e.value)
+        return out
+
+    def ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(f.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def _src_sha(name: str) -> str:
+    path = os.path.join(ROOT, "activation_sparse_feed_gate_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, src: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, only
+    when they were taken on the current kernel source and this workload."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("src_sha") != _src_sha(src) or rec.get("workload") != workload:
+        return None
+    return float(rec["bytes_per_launch"])
+
+
+def cpu_baseline(d, w, budget_s: float):
+    """The oracle's own TwELL forward (gate, packing, sparse evaluation with
+    the dense recompute of overflow rows) on an evenly strided row sample."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.default()
+    wg, wu, wd = (oracle.widen_bf16(d[k]) for k in ("wg_t", "wu_t", "wd"))
+
+    def run(rows):
+        xs = oracle.widen_bf16(d["x"][rows])
+        t = time.perf_counter()
+        z = orc.gate(xs, wg)
+        p = orc.pack(z, w.T, w.C, len(rows))
+        orc.sparse_ffn(xs, wg, wu, wd, w.T, w.C, p)
+        return time.perf_counter() - t
+
+    pilot = np.linspace(0, w.M - 1, min(w.M, 64)).astype(np.int64)
+    per_row = run(pilot) / len(pilot)
+    n = int(min(w.M, max(64, budget_s / max(per_row, 1e-9))))
+    rows = np.linspace(0, w.M - 1, n).astype(np.int64)
+    secs = run(rows)
+    return {"value": len(rows) / secs, "unit": "tokens/s", "cores": orc.threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {w.M} token rows, evenly strided; float64 gate, "
+                      f"TwELL packing, sparse up+down with dense recompute of overflow rows; "
+                      f"{secs:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ffn-0.5b")
+    ap.add_argument("--density", type=float, default=None, help="override the target density")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): the path is data-parallel over tokens with no exchange, so N GPUs "
+              f"run N independent copies; no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from activation_sparse_feed_gate_amd import synth, tw
+
+    w = synth.WORKLOADS[args.workload]
+    if args.density is not None:
+        w = w.with_(density=args.density)
+    M, K, N, T, C = w.M, w.K, w.N, w.T, w.C
+    R_max = M  # room for every row: timing never needs the retry
+    d = synth.make_inputs(w)
+
+    def dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+            torch.bfloat16).cuda()
+
+    x, wg, wu, wdn = dev(d["x"]), dev(d["wg_t"]), dev(d["wu_t"]), dev(d["wd"])
+    bufs = tw.alloc_pack(M, N, T, C, R_max)
+    ws = tw.workspace(M, K, N, T, C, R_max)
+    y = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    yd = torch.empty((M, K), dtype=torch.float32, device="cuda")
+    wsd = torch.empty((tw.tw_ffn_workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    hev = HipEvents()
+
+    def step(evp=None, evs=None):
+        tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"],
+                        bufs["ovf_rows"], bufs["ovf_count"], R_max, ws, stream=stream,
+                        events=evp)
+        tw.tw_sparse_ffn_fwd(x, wg, wu, wdn, T, C, bufs["tw_val"], bufs["tw_idx"],
+                             bufs["tw_cnt"], bufs["ovf_rows"], bufs["ovf_count"], R_max, y, ws,
+                             stream=stream, events=evs)
+
+    def dense(ev=None):
+        tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd, stream=stream, events=ev)
+
+    for _ in range(args.warmup):
+        step()
+        dense()
+    torch.cuda.synchronize()
+
+    # realized sparsity of this batch (deterministic; outside the timed region)
+    cnt = bufs["tw_cnt"].cpu().numpy().astype(np.int64)
+    ovf = (cnt > C).any(axis=1)
+    nnz = cnt.sum(axis=1)
+    R = int(ovf.sum())
+    sparse_nnz = int(nnz[~ovf].sum())
+
+    # ---- timed: the sparse path ----
+    Ks = args.steps
+    evp = [hev.create(3) for _ in range(Ks)]
+    evs = [hev.create(4) for _ in range(Ks)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(Ks):
+        step(evp[s], evs[s])
+    torch.cuda.synchronize()
+    t_sparse = (time.perf_counter() - t0) / Ks
+
+    # ---- timed: the dense comparator ----
+    evd = [hev.create(3) for _ in range(Ks)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(Ks):
+        dense(evd[s])
+    torch.cuda.synchronize()
+    t_dense = (time.perf_counter() - t0) / Ks
+
+    def avg(evl, i):
+        return sum(hev.ms(e[i], e[i + 1]) for e in evl) / len(evl) * 1e-3  # seconds
+
+    kern = {
+        "gate_twell": avg(evp, 0),
+        "ovf_compact": avg(evp, 1),
+        "sparse_updown": avg(evs, 0),
+        "fallback_gateup": avg(evs, 1),
+        "fallback_down": avg(evs, 2),
+    }
+    kern_dense = {"dense_gateup": avg(evd, 0), "dense_down": avg(evd, 1)}
+    for l in (evp, evs, evd):
+        for e in l:
+            hev.destroy(e)
+
+    NT = N // T
+    sparse_bytes = (sparse_nnz * (4 * K + 8) + int((~ovf).sum()) * (2 * K + 4 * K + 4 * NT)
+                    + R * 4 * NT)
+    work = {  # algorithmic work per launch: (amount, bound, unit)
+        "gate_twell": (2.0 * M * K * N, "mfma"),
+        "sparse_updown": (float(sparse_bytes), "hbm"),
+        "fallback_gateup": (4.0 * R * K * N, "mfma"),
+        "fallback_down": (2.0 * R * K * N, "mfma"),
+        "dense_gateup": (4.0 * M * K * N, "mfma"),
+        "dense_down": (2.0 * M * K * N, "mfma"),
+    }
+    srcs = {"gate_twell": "gate_twell.hip", "sparse_updown": "sparse_updown.hip",
+            "fallback_gateup": "dense_ffn.hip", "fallback_down": "dense_ffn.hip",
+            "dense_gateup": "dense_ffn.hip", "dense_down": "dense_ffn.hip"}
+
+    def roof(name, secs):
+        amount, bound = work[name]
+        if bound == "mfma":
+            a = amount / secs / 1e12
+            r = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                 "frac": a / PEAK_BF16_TFLOPS}
+        else:
+            a = amount / secs / 1e9
+            r = {"bound": "hbm", "achieved": a, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": a / PEAK_HBM_GBS}
+        r["kernel"] = name
+        r["avg_us"] = secs * 1e6
+        r["traffic"] = _traffic(name, srcs[name], w.name)
+        return r
+
+    path_kernels = ["gate_twell", "sparse_updown", "fallback_gateup", "fallback_down"]
+    dominant = max(path_kernels, key=lambda k: kern[k])
+    stages = {k: roof(k, kern[k]) for k in path_kernels if kern[k] > 0}
+    stages.update({k: roof(k, v) for k, v in kern_dense.items()})
+
+    out = {
+        "metric": METRIC,
+        "value": M / t_sparse,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": Ks,
+        "warmup": args.warmup,
+        "ms_per_step": t_sparse * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "K": K, "N": N, "T": T, "C": C,
+                   "density": w.density, "sigma_s": w.sigma_s, "seed": w.seed, "R_max": R_max},
+        "roofline": roof(dominant, kern[dominant]),
+        "speedup_vs_dense": t_dense / t_sparse,
+        "dense": {"ms_per_step": t_dense * 1e3, "value": M / t_dense},
+        "kernels_us": {k: v * 1e6 for k, v in {**kern, **kern_dense}.items()},
+        "stages": stages,
+        "realized": {"density": float(nnz.sum()) / (M * N), "overflow_rows": R,
+                     "nnz_per_sparse_row": sparse_nnz / max(1, int((~ovf).sum())),
+                     "max_nnz_sparse_row": int(nnz[~ovf].max(initial=0))},
+        "device": torch.cuda.get_device_properties(0).name,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

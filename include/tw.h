@@ -1,0 +1,164 @@
+/*
+ * tw.h -- C ABI of the TwELL sparse gated-FFN forward for AMD MI355X (gfx950).
+ *
+ * The block computed is the ReLU-gated feed-forward layer of "Sparser,
+ * Faster, Lighter Transformer Language Models Review", section 1-1:
+ *
+ *     h_u = x W_u,   h_g = ReLU(x W_g),   h = h_u (elementwise) h_g,   y = h W_d
+ *
+ * with x [M, K] (M tokens, model dimension K) and an expanded hidden
+ * dimension N.  Its inference path (section 2-2, "gate matmul plus TwELL
+ * epilogue -> fused sparse up and down") is split over two calls:
+ *
+ *   tw_pack_gate       gate GEMM whose epilogue applies the ReLU and packs the
+ *                      active entries of every (token row, column tile) in the
+ *                      tile-wise ELLPACK layout of section 3-4, and builds the
+ *                      list of rows that overflow a tile's capacity
+ *                      (the dense-backup routing of sections 3-6 and 4-3);
+ *   tw_sparse_ffn_fwd  per-token sparse up+down (section 3-5 equation) for the
+ *                      rows that fit, and the dense path for the listed rows.
+ *
+ * tw_ffn_fwd is the dense gated FFN over all rows, the comparator the sparse
+ * path is measured against.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 values travel as raw uint16_t bit patterns.
+ * - Every pointer argument except `stream` is a device pointer to memory the
+ *   caller owns; the library allocates and frees nothing and keeps no state
+ *   between calls, so calls on different streams may run concurrently as
+ *   long as their output and workspace buffers are distinct.
+ * - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *   void*; NULL is the default stream).  Nothing synchronises the host.
+ * - Argument and shape errors are detected on the host before any work is
+ *   enqueued and return TW_EINVAL or TW_EUNSUPPORTED; no output is touched
+ *   then.  A failed kernel launch returns TW_EHIP.  tw_last_error() gives a
+ *   message for the last failure of the calling thread.
+ * - Device buffers must be 16-byte aligned.  When M == 0 the buffers whose
+ *   size is a multiple of M may be NULL.
+ * - Optional `events`: NULL, or an array of hipEvent_t (passed as void*)
+ *   with one more entry than the call launches kernels.  events[0] is
+ *   recorded on `stream` before the first kernel and events[i+1] after
+ *   kernel i, so per-kernel durations can be read with
+ *   hipEventElapsedTime.  tw_pack_gate launches 2 kernels, tw_sparse_ffn_fwd
+ *   3 and tw_ffn_fwd 2.
+ *
+ * Weight layout (one layout serves every path): wg_t, wu_t and wd are all
+ * [N][K] row-major bf16.  wg_t and wu_t hold W_g and W_u transposed, so the
+ * weights of hidden neuron j (column j of W_g / W_u) are row j, contiguous;
+ * wd is W_d itself, whose row j is what neuron j adds to the output.
+ *
+ * Supported shapes: M >= 0, K a positive multiple of 128 and at most 4096,
+ * N a positive multiple of T, T in {128, 256}, N / T <= 256, 1 <= C <= T,
+ * 0 <= R_max <= M.
+ */
+#ifndef TW_H
+#define TW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tw_status {
+    TW_OK = 0,
+    TW_EINVAL = 1,        /* null pointer, bad size, misaligned buffer     */
+    TW_EUNSUPPORTED = 2,  /* valid but outside the supported shapes above  */
+    TW_EHIP = 3           /* a HIP runtime call or kernel launch failed    */
+} tw_status;
+
+/* Static name of a status code. */
+const char *tw_status_str(int status);
+
+/* Message describing the last non-OK status returned on the calling thread
+ * (empty string if none). */
+const char *tw_last_error(void);
+
+/* Bytes of device workspace tw_pack_gate and tw_sparse_ffn_fwd need for
+ * this shape (one buffer of this size serves both); 0 for arguments that
+ * the entry points would reject. */
+size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max);
+
+/*
+ * Gate GEMM + ReLU + TwELL packing + overflow routing.
+ *
+ * Computes z = x W_g in fp32 (bf16 products, fp32 accumulation) and, for
+ * every token row m and column tile t (columns [t*T, (t+1)*T)):
+ *   tw_cnt[m][t]          number of columns j in the tile with z[m][j] > 0
+ *                         (strictly positive; the true count, even above C)
+ *   tw_idx[m][t][s]       the s-th such j, ascending, as a global column
+ *   tw_val[m][t][s]       z[m][j] (fp32) for that j
+ * for s < min(tw_cnt[m][t], C); slots from min(cnt, C) to C-1 are left
+ * untouched.  These are the packed values, original hidden indices and
+ * per-(row, tile) counts of section 3-4 (h_v, h_I, h_nz).
+ *
+ * A row with any tile holding more than C active columns overflows and is
+ * routed whole to the dense path (sections 3-6 and 4-3): ovf_rows receives
+ * the overflowing rows in ascending order, at most R_max of them, and
+ * *ovf_count their true number.  *ovf_count > R_max means that the rows past
+ * the first R_max will not be recomputed: read ovf_count after the stream
+ * has run and retry with a larger R_max (or C) -- the retry of section 4-3.
+ *
+ *   x        [M][K]          bf16, token rows
+ *   wg_t     [N][K]          bf16, W_g transposed
+ *   tw_val   [M][N/T][C]     fp32 out
+ *   tw_idx   [M][N/T][C]     int32 out
+ *   tw_cnt   [M][N/T]        int32 out
+ *   ovf_rows [max(R_max,1)]  int32 out
+ *   ovf_count[1]             int32 out
+ *   z_debug  [M][N]          fp32 out, or NULL; receives z itself (the same
+ *                            values the packing used) -- for tests
+ *   ws       workspace of ws_bytes >= tw_workspace_bytes(M, K, N, T, C, R_max)
+ */
+tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t,
+                       int M, int K, int N, int T, int C,
+                       float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                       int32_t *ovf_rows, int32_t *ovf_count, int R_max,
+                       float *z_debug, void *ws, size_t ws_bytes,
+                       void *stream, void *const *events);
+
+/*
+ * Sparse up+down for the rows that fit, dense path for the overflow list.
+ *
+ * For every row m with no tile over capacity (every tw_cnt[m][t] <= C), with
+ * the packed (j, g) pairs of tw_pack_gate:
+ *     y[m][:] = sum over packed (j, g) of (x[m] . Wu_t[j]) * g * Wd[j][:]
+ * (section 3-5 equation; the up activation is a scalar per active neuron,
+ * fp32 throughout).  A row with no active neuron gets y = 0.
+ * For r < min(*ovf_count, R_max), the row m = ovf_rows[r] gets the dense
+ * gated FFN of section 1-1 instead (h rounded to bf16 before W_d, fp32
+ * accumulation).  Rows that overflow but lie past R_max are left untouched.
+ *
+ *   x, wg_t, wu_t, wd       as above ([M][K] and [N][K] bf16)
+ *   tw_val, tw_idx, tw_cnt  the packing written by tw_pack_gate
+ *   ovf_rows, ovf_count     the routing written by tw_pack_gate (device)
+ *   y        [M][K]         fp32 out
+ */
+tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
+                            const uint16_t *wu_t, const uint16_t *wd,
+                            int M, int K, int N, int T, int C,
+                            const float *tw_val, const int32_t *tw_idx,
+                            const int32_t *tw_cnt, const int32_t *ovf_rows,
+                            const int32_t *ovf_count, int R_max,
+                            float *y, void *ws, size_t ws_bytes,
+                            void *stream, void *const *events);
+
+/*
+ * Dense gated FFN over all M rows (section 1-1 equation): the gate and up
+ * projections in one MFMA GEMM whose epilogue forms h = ReLU(g) * u rounded
+ * to bf16, then the down projection into fp32 y [M][K].
+ * The workspace holds h [M][N] bf16: ws_bytes >= tw_ffn_workspace_bytes.
+ */
+size_t tw_ffn_workspace_bytes(int M, int K, int N);
+tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
+                     const uint16_t *wu_t, const uint16_t *wd,
+                     int M, int K, int N, float *y, void *ws, size_t ws_bytes,
+                     void *stream, void *const *events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TW_H */

@@ -1,0 +1,119 @@
+"""Comparison of the HIP path with the CPU oracle (test infrastructure).
+
+Rules (the tolerances the hot path is held to):
+- packing is bit-exact when the oracle packs the very gate values the GPU
+  packed (the GPU's own fp32 z): counts, indices, values, overflow list and
+  count;
+- the GPU gate itself agrees with the oracle's float64 gate within the
+  standard dot-product bound 2 * gamma_K * sum_k |x_k w_k| (bf16 products
+  are exact in fp32; gamma_K = K u / (1 - K u), u = 2^-24);
+- against the oracle's own gate, per tile the GPU count lies between the
+  counts of z_ref > 1e-3 and z_ref > -1e-3, the index sets agree outside the
+  band |z_ref| < 1e-3, and the overflow status agrees on every row whose
+  status the band cannot change;
+- the output satisfies max |y - y_ref| <= 1e-2 * max |y_ref| + 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+BAND = 1e-3
+
+
+def to_dev(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bf16 device tensor (bit-preserving)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(device)
+
+
+def upload(d: dict, device="cuda") -> dict:
+    return {k: to_dev(d[k], device) for k in ("x", "wg_t", "wu_t", "wd")}
+
+
+def run_path(tw, dev: dict, T: int, C: int, R_max: int, z_debug=True, dense=True) -> dict:
+    """Run pack + sparse (+ dense) through the C ABI; results to host numpy."""
+    p = tw.pack_gate(dev["x"], dev["wg_t"], T, C, R_max, z_debug=z_debug)
+    y = tw.sparse_ffn(dev["x"], dev["wg_t"], dev["wu_t"], dev["wd"], p)
+    yd = tw.ffn(dev["x"], dev["wg_t"], dev["wu_t"], dev["wd"]) if dense else None
+    torch.cuda.synchronize()
+    out = {k: p[k].cpu().numpy() for k in ("tw_val", "tw_idx", "tw_cnt", "ovf_rows")}
+    out["ovf_count"] = int(p["ovf_count"].cpu()[0])
+    if z_debug:
+        out["z"] = p["z"].cpu().numpy()
+    out["y"] = y.cpu().numpy()
+    if dense:
+        out["y_dense"] = yd.cpu().numpy()
+    return out
+
+
+def check_packing_bitexact(g: dict, T: int, C: int, R_max: int, rows=None) -> None:
+    """The oracle packer applied to the GPU's own fp32 gate reproduces the
+    GPU packing exactly (all rows, or the given rows for counts/slots)."""
+    z = g["z"]
+    M = z.shape[0]
+    ref = oracle.default().pack(z.astype(np.float64), T, C, R_max)
+    assert np.array_equal(g["tw_cnt"], ref["cnt"]), "counts differ"
+    used = np.arange(C)[None, None, :] < np.minimum(ref["cnt"], C)[:, :, None]
+    assert np.array_equal(np.where(used, g["tw_idx"], -1), np.where(used, ref["idx"], -1)), \
+        "indices differ"
+    gv = g["tw_val"].astype(np.float64)
+    assert np.array_equal(np.where(used, gv, 0.0).view(np.uint64),
+                          np.where(used, ref["val"], 0.0).view(np.uint64)), "values differ"
+    assert g["ovf_count"] == ref["ovf_count"], (g["ovf_count"], ref["ovf_count"])
+    n = min(ref["ovf_count"], R_max)
+    assert np.array_equal(g["ovf_rows"][:n], ref["ovf_rows"][:n]), "overflow list differs"
+    assert M == g["tw_cnt"].shape[0]
+
+
+def check_gate_bound(z_gpu_rows: np.ndarray, z_ref_rows: np.ndarray, x_rows, wg_t) -> None:
+    """|z_gpu - z_ref| <= 2 gamma_K sum_k |x_k w_k| on the given rows."""
+    xa = np.abs(oracle.widen_bf16(x_rows))
+    wa = np.abs(oracle.widen_bf16(wg_t))
+    K = xa.shape[1]
+    u = 2.0 ** -24
+    gamma = K * u / (1 - K * u)
+    bound = 2 * gamma * (xa @ wa.T)
+    err = np.abs(z_gpu_rows.astype(np.float64) - z_ref_rows)
+    assert np.all(err <= bound), f"gate error {err.max()} above bound"
+
+
+def check_index_parity(g: dict, rows: np.ndarray, z_ref_rows: np.ndarray, T: int, C: int) -> None:
+    """GPU packing vs the oracle's own gate on sampled rows, outside the band."""
+    M_s, N = z_ref_rows.shape
+    NT = N // T
+    zt = z_ref_rows.reshape(M_s, NT, T)
+    lo = (zt > BAND).sum(axis=2)
+    hi = (zt > -BAND).sum(axis=2)
+    cnt = g["tw_cnt"][rows]
+    assert np.all((cnt >= lo) & (cnt <= hi)), "count outside the band's range"
+    firm = np.abs(z_ref_rows) >= BAND
+    for r_i, m in enumerate(rows):
+        for t in range(NT):
+            n = min(int(cnt[r_i, t]), C)
+            ids = g["tw_idx"][m, t, :n]
+            assert np.all(np.diff(ids) > 0), "indices not ascending"
+            assert np.all((ids >= t * T) & (ids < (t + 1) * T)), "index outside its tile"
+            if hi[r_i, t] <= C:  # the whole tile's active set was stored
+                cols = np.arange(t * T, (t + 1) * T)
+                want = set(cols[(z_ref_rows[r_i, t * T:(t + 1) * T] > 0) & firm[r_i, t * T:(t + 1) * T]])
+                got = set(ids.tolist())
+                assert want <= got, "a firmly active column is missing"
+                extra = got - want
+                assert all(abs(z_ref_rows[r_i, j]) < BAND for j in extra), "a firmly inactive column was packed"
+    # overflow status on determined rows
+    over_gpu = np.isin(rows, g["ovf_rows"][: min(g["ovf_count"], len(g["ovf_rows"]))]) | \
+        (g["tw_cnt"][rows] > C).any(axis=1)
+    surely_over = (lo > C).any(axis=1)
+    surely_not = (hi <= C).all(axis=1)
+    assert np.all(over_gpu[surely_over]), "row that must overflow did not"
+    assert not np.any(over_gpu[surely_not]), "row that cannot overflow did"
+
+
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what="y") -> float:
+    err = float(np.abs(y_gpu.astype(np.float64) - y_ref).max(initial=0.0))
+    tol = 1e-2 * float(np.abs(y_ref).max(initial=0.0)) + 1e-3
+    assert err <= tol, f"{what}: max error {err} > tolerance {tol}"
+    return err

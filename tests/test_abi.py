@@ -1,0 +1,98 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tw.h")
+
+
+@pytest.fixture(scope="module")
+def tw():
+    from activation_sparse_feed_gate_amd import build as b
+
+    srcs = [os.path.join(b.CSRC, s) for s in b.SOURCES] + [HEADER]
+    lib = b.LIBRARY
+    if not os.path.exists(lib) or any(os.path.getmtime(s) > os.path.getmtime(lib) for s in srcs):
+        b.build()
+    from activation_sparse_feed_gate_amd import tw as mod
+
+    return mod
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tw_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared()
+    for n in ("tw_pack_gate", "tw_sparse_ffn_fwd", "tw_ffn_fwd", "tw_workspace_bytes"):
+        assert n in names
+
+
+def test_exports_every_declared_symbol(tw):
+    out = subprocess.run(["nm", "-D", "--defined-only", tw.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in declared():
+        assert n in exported, n
+        assert hasattr(tw._lib, n)
+
+
+def test_status_strings(tw):
+    assert tw._lib.tw_status_str(0) == b"TW_OK"
+    assert tw._lib.tw_status_str(1) == b"TW_EINVAL"
+    assert tw._lib.tw_status_str(2) == b"TW_EUNSUPPORTED"
+    assert tw._lib.tw_status_str(3) == b"TW_EHIP"
+
+
+def test_workspace_bytes(tw):
+    assert tw.tw_workspace_bytes(4096, 1024, 4096, 128, 8, 512) > 512 * 4096 * 2
+    assert tw.tw_workspace_bytes(4096, 1024, 4096, 64, 8, 512) == 0
+    assert tw.tw_workspace_bytes(4096, 1000, 4096, 128, 8, 512) == 0
+    assert tw.tw_workspace_bytes(4096, 1024, 4096, 128, 0, 512) == 0
+    assert tw.tw_workspace_bytes(4096, 1024, 4096, 128, 8, 5000) == 0
+    assert tw.tw_ffn_workspace_bytes(64, 256, 1024) >= 64 * 1024 * 2
+
+
+# Fake, 16-byte-aligned device addresses: every case below must be rejected
+# on the host before any of them is dereferenced or any HIP call is made.
+P = 0x100000
+
+
+def _pack(tw, M=64, K=256, N=1024, T=128, C=16, R=64, ws=1 << 20, **ptrs):
+    a = dict(x=P, wg=P, val=P, idx=P, cnt=P, ovf=P, n=P, z=None, w=P)
+    a.update(ptrs)
+    return tw._lib.tw_pack_gate(a["x"], a["wg"], M, K, N, T, C, a["val"], a["idx"], a["cnt"],
+                                a["ovf"], a["n"], R, a["z"], a["w"], ws, None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=64), 2), (dict(T=512, N=1024), 2), (dict(N=1000), 1), (dict(C=0), 1),
+    (dict(C=129), 1), (dict(K=192), 2), (dict(K=8192), 2), (dict(R=65), 1), (dict(R=-1), 1),
+    (dict(M=-1), 1), (dict(K=0), 1), (dict(x=None), 1), (dict(wg=None), 1), (dict(val=None), 1),
+    (dict(n=None), 1), (dict(w=None), 1), (dict(x=P + 8), 1), (dict(z=P + 4), 1), (dict(ws=16), 1),
+    (dict(N=128 * 300), 2),
+])
+def test_pack_rejects(tw, kw, code):
+    assert _pack(tw, **kw) == code
+    assert tw._lib.tw_last_error()
+
+
+def test_sparse_and_dense_reject(tw):
+    L = tw._lib
+    assert L.tw_sparse_ffn_fwd(P, P, P, P, 64, 256, 1024, 128, 16, P, P, P, P, P, 64, None, P,
+                               1 << 20, None, None) == 1
+    assert L.tw_sparse_ffn_fwd(P, P, P, P, 64, 256, 1024, 100, 16, P, P, P, P, P, 64, P, P,
+                               1 << 20, None, None) == 2
+    assert L.tw_sparse_ffn_fwd(P, P, P, P, 64, 256, 1024, 128, 16, P, P, P, P, P, 64, P, P,
+                               8, None, None) == 1
+    assert L.tw_ffn_fwd(P, P, P, P, 64, 256, 1000, P, P, 1 << 24, None, None) == 2
+    assert L.tw_ffn_fwd(P, P, P, None, 64, 256, 1024, P, P, 1 << 24, None, None) == 1
+    assert L.tw_ffn_fwd(P, P, P, P, 64, 256, 1024, P, P, 16, None, None) == 1

@@ -1,0 +1,152 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Small shapes are compared on every row; the full-size workloads are compared
+on all rows for the packing (the oracle re-packs the GPU's own gate) and on
+sampled rows -- evenly spaced, overflowing and the heaviest sparse rows --
+for the gate, the index sets and the output.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import parity
+from activation_sparse_feed_gate_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def tw():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from activation_sparse_feed_gate_amd import tw as mod
+
+    return mod
+
+
+def _full_check(tw, w, R_max=None, dense=True):
+    """Every row against the oracle: packing, gate bound, index parity, y."""
+    print(f"case {w} R_max={R_max}", flush=True)
+    d = synth.make_inputs(w)
+    R_max = w.M if R_max is None else R_max
+    g = parity.run_path(tw, parity.upload(d), w.T, w.C, R_max, dense=dense)
+    parity.check_packing_bitexact(g, w.T, w.C, R_max)
+    orc = oracle.default()
+    z_ref = orc.gate(d["x"], d["wg_t"])
+    rows = np.arange(w.M)
+    parity.check_gate_bound(g["z"], z_ref, d["x"], d["wg_t"])
+    parity.check_index_parity(g, rows, z_ref, w.T, w.C)
+    y_ref = orc.dense_ffn(d["x"], d["wg_t"], d["wu_t"], d["wd"])
+    covered = np.ones(w.M, dtype=bool)
+    if g["ovf_count"] > R_max:  # rows past R_max are left for the retry
+        flagged = (g["tw_cnt"] > w.C).any(axis=1)
+        listed = np.zeros(w.M, dtype=bool)
+        listed[g["ovf_rows"][:R_max]] = True
+        covered = ~flagged | listed
+    parity.check_y(g["y"][covered], y_ref[covered], "sparse y")
+    if dense:
+        parity.check_y(g["y_dense"], y_ref, "dense y")
+    return g, d
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),                                   # tiny: 64 x 256 x 1024, T=128, C=16
+    dict(C=12), dict(C=4), dict(C=1),         # some / all rows overflow
+    dict(T=256, C=16), dict(T=256, C=40),     # tile spanning two waves
+    dict(M=300, K=384, N=1152, T=128, C=8, density=0.02, sigma_s=0.5),  # ragged M, half column block
+    dict(M=513, K=512, N=2048, T=256, C=12, density=0.01, sigma_s=0.7, seed=3),
+    dict(M=1, K=128, N=128, T=128, C=3, density=0.1),
+])
+def test_tiny_all_rows(tw, kw):
+    _full_check(tw, W["tiny"].with_(**kw))
+
+
+@pytest.mark.parametrize("kw", [
+    dict(density=0.0), dict(density=1.0, C=128), dict(density=1.0, C=16),
+    dict(density=1.0, T=256, C=256),
+])
+def test_density_extremes(tw, kw):
+    g, _ = _full_check(tw, W["tiny"].with_(**kw))
+    if kw["density"] == 0.0:
+        assert not g["tw_cnt"].any() and g["ovf_count"] == 0 and not g["y"].any()
+    elif kw["C"] == kw.get("T", 128):
+        assert (g["tw_cnt"] == kw.get("T", 128)).all() and g["ovf_count"] == 0
+    else:
+        assert g["ovf_count"] == 64
+
+
+def test_capacity_retry(tw):
+    """Too small a dense backup: the true count comes back, and a retry with
+    enough room gives the full result (the retry of the static-capacity
+    scheme)."""
+    w = W["tiny"].with_(C=4)
+    d = synth.make_inputs(w)
+    dev = parity.upload(d)
+    g = parity.run_path(tw, dev, w.T, w.C, 5, dense=False)
+    assert g["ovf_count"] > 5
+    need = g["ovf_count"]
+    g2 = parity.run_path(tw, dev, w.T, w.C, need, dense=False)
+    y_ref = oracle.default().dense_ffn(d["x"], d["wg_t"], d["wu_t"], d["wd"])
+    parity.check_y(g2["y"], y_ref)
+
+
+def test_empty_batch(tw):
+    import torch
+
+    w = W["tiny"].with_(M=0)
+    d = synth.make_inputs(w)
+    dev = parity.upload(d)
+    p = tw.pack_gate(dev["x"], dev["wg_t"], w.T, w.C, 0)
+    y = tw.sparse_ffn(dev["x"], dev["wg_t"], dev["wu_t"], dev["wd"], p)
+    torch.cuda.synchronize()
+    assert int(p["ovf_count"].cpu()[0]) == 0 and y.numel() == 0
+
+
+def test_deterministic(tw):
+    w = W["tiny"].with_(M=512, C=6, sigma_s=0.5, density=0.03)
+    d = synth.make_inputs(w)
+    dev = parity.upload(d)
+    a = parity.run_path(tw, dev, w.T, w.C, w.M)
+    b = parity.run_path(tw, dev, w.T, w.C, w.M)
+    for k in ("tw_cnt", "ovf_rows", "y", "y_dense", "z"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
+    used = np.arange(w.C)[None, None, :] < np.minimum(a["tw_cnt"], w.C)[:, :, None]
+    assert np.array_equal(np.where(used, a["tw_idx"], 0), np.where(used, b["tw_idx"], 0))
+
+
+def _sample_rows(g, M, C, n_even=32, n_ovf=16, n_heavy=16):
+    rows = set(np.linspace(0, M - 1, n_even).astype(int).tolist())
+    nov = min(g["ovf_count"], len(g["ovf_rows"]))
+    ov = g["ovf_rows"][:nov]
+    rows |= set(ov[np.linspace(0, nov - 1, min(n_ovf, nov)).astype(int)].tolist()) if nov else set()
+    tot = np.where((g["tw_cnt"] > C).any(axis=1), -1, g["tw_cnt"].sum(axis=1))
+    rows |= set(np.argsort(-tot, kind="stable")[:n_heavy].tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name,dens", [("ffn-0.5b", None), ("ffn-1b", None), ("ffn-2b", None),
+                                       ("ffn-ovf", None), ("ffn-2b", 0.0), ("ffn-2b", 0.05)])
+def test_full_size(tw, name, dens):
+    w = W[name] if dens is None else W[name].with_(density=dens)
+    print(f"case {w}", flush=True)
+    d = synth.make_inputs(w)
+    g = parity.run_path(tw, parity.upload(d), w.T, w.C, w.M)
+    parity.check_packing_bitexact(g, w.T, w.C, w.M)
+    rows = _sample_rows(g, w.M, w.C)
+    orc = oracle.default()
+    z_ref = orc.gate(d["x"][rows], d["wg_t"])
+    parity.check_gate_bound(g["z"][rows], z_ref, d["x"][rows], d["wg_t"])
+    parity.check_index_parity(g, rows, z_ref, w.T, w.C)
+    y_ref = orc.dense_ffn(d["x"][rows], d["wg_t"], d["wu_t"], d["wd"])
+    parity.check_y(g["y"][rows], y_ref, "sparse y")
+    parity.check_y(g["y_dense"][rows], y_ref, "dense y")
+    # properties on every row: overflow rows are exactly the listed ones, and
+    # rows without an active neuron produce exact zeros
+    flagged = (g["tw_cnt"] > w.C).any(axis=1)
+    assert np.array_equal(np.nonzero(flagged)[0], g["ovf_rows"][: g["ovf_count"]])
+    empty = g["tw_cnt"].sum(axis=1) == 0
+    assert not g["y"][empty].any()
