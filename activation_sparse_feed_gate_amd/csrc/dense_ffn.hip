@@ -7,272 +7,407 @@
 // through a dense path on the matrix cores instead of being clipped).
 //
 // gfx950 design
-// - gate+up: one GEMM with two B operands.  Macro tile 256 rows x 128
-//   hidden columns, 4 waves in 2 x 2, each wave 128 x 64 outputs of both g
-//   and u (2 x 4 x 2 blocks of v_mfma_f32_32x32x16_bf16).  The epilogue forms
-//   h = ReLU(g) * u and rounds it to bf16; neither g nor u is stored.
-// - down: A = h [rows][N] (reduction-contiguous), B = W_d [N][K] whose
-//   reduction index is the row index.  Each thread loads 4 rows x 8 columns
-//   of W_d, transposes them in registers and writes them to LDS as 8 rows of
-//   4 reduction elements, so the LDS tile has the same swizzled,
-//   reduction-contiguous layout as every other operand.  Macro tile 128 x 128.
-// - Both kernels take an optional row list (the overflow list) with a
-//   device-side count: x rows are gathered through it and y rows scattered
-//   through it; workgroups past the count exit at once, so the grid can be
-//   sized for the capacity without a host round trip.
+// - Both GEMMs stream their operands from global memory straight into LDS
+//   through the 4-stage ring of tw_gemm.hpp (32 reduction elements a stage).
+// - gate+up: one GEMM with two B operands, so x is read once for both; the
+//   epilogue forms h = ReLU(g) * u and rounds it to bf16 (g and u are never
+//   stored).  Workgroups loop over tiles: the overflow path sizes its grid
+//   for the capacity and finds the actual number of rows on the device.
+// - down: A = h [rows][N] (reduction-contiguous), B = W_d [N][K], whose
+//   reduction index is its row index.  W_d rows land in LDS in their natural
+//   layout and the MFMA B fragments are read with ds_read_b64_tr_b16, the
+//   gfx950 LDS read that transposes 16-bit elements across a 16-lane group.
+// - With few rows (the overflow path) the down GEMM also splits the
+//   reduction over N so that every CU has work; each split writes a partial
+//   tile and a small kernel sums the partials in split order (the result
+//   does not depend on timing).  A device-scope fence per workgroup instead
+//   would write back the whole L2 of its XCD each time.
+// - Rows come either directly or through a row list with a device-side
+//   count (the overflow list): x rows are gathered and y rows scattered
+//   through it.
 #include "tw_device.hpp"
+#include "tw_gemm.hpp"
 #include "tw_internal.hpp"
 
 namespace tw {
 namespace {
 
-constexpr int kThreads = 256;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int rows_of(const int32_t *count, int R_cap) {
+    return count ? min(*count, R_cap) : R_cap;
+}
 
 // ------------------------------ gate + up ---------------------------------
-constexpr int kGuBM = 256, kGuBN = 128;
-constexpr int kGuA = kGuBM * kRowBytes;  // 32 KB
-constexpr int kGuB = kGuBN * kRowBytes;  // 16 KB
-constexpr int kGuStage = kGuA + 2 * kGuB;
-constexpr int kGuLds = 2 * kGuStage;     // 128 KB
+template <int BM, int BN, int WM, int WN>
+struct GU {
+    static constexpr int NW = WM * WN, NTH = NW * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+    static constexpr int FA = TM / 32, FB = TN / 32;  // 32-blocks per wave
+    static constexpr int SR = BM + 2 * BN;            // stage rows: A, then W_g, then W_u
+    static constexpr int NI = SR / (16 * NW);         // direct loads per wave and stage
+    static constexpr int STAGE = SR * kPRow;
+    static constexpr int LDS = kPStages * STAGE;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
+    static_assert(SR % (16 * NW) == 0 && BM % 16 == 0 && BN % 16 == 0, "stage rows");
+};
 
-__global__ __launch_bounds__(kThreads) void gateup_kernel(
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t,
     const uint16_t *__restrict__ wu_t, int K, int N, const int32_t *__restrict__ rowlist,
     const int32_t *__restrict__ count, int R_cap, uint16_t *__restrict__ h) {
+    using P = GU<BM, BN, WM, WN>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int rows = count ? min(*count, R_cap) : R_cap;
-    const int m0 = blockIdx.y * kGuBM;
-    if (m0 >= rows) return;
-    const int n0 = blockIdx.x * kGuBN;
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int r0 = tid >> 3, kc0 = tid & 7;
-
-    int aoff[8], goff[4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = min(m0 + r0 + 32 * i, rows - 1);
-        const int xr = rowlist ? rowlist[r] : r;
-        aoff[i] = xr * K + kc0 * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) goff[i] = (n0 + r0 + 32 * i) * K + kc0 * 8;
-
-    u32x4 ra[8], rg[4], ru[4];
-    auto load = [&](int k) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ra[i] = ld16(x + aoff[i] + k);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rg[i] = ld16(wg_t + goff[i] + k);
-            ru[i] = ld16(wu_t + goff[i] + k);
-        }
-    };
-    auto store = [&](char *st) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) lds_st16(st, lds_off(r0 + 32 * i, kc0), ra[i]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            lds_st16(st + kGuA, lds_off(r0 + 32 * i, kc0), rg[i]);
-            lds_st16(st + kGuA + kGuB, lds_off(r0 + 32 * i, kc0), ru[i]);
-        }
-    };
-    load(0);
-    store(smem);
-    __syncthreads();
-
-    f32x16 ag[4][2], au[4][2];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            ag[a][b] = f32x16{};
-            au[a][b] = f32x16{};
-        }
-    const int KT = K / kBK;
-    const int frow = lane & 31;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) load((kt + 1) * kBK);
-        const char *st = smem + cur * kGuStage;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int kc = 2 * s + (lane >> 5);
-            u32x4 fa[4], fg[2], fu[2];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) fa[a] = lds_ld16(st, lds_off(wm * 128 + a * 32 + frow, kc));
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                fg[b] = lds_ld16(st + kGuA, lds_off(wn * 64 + b * 32 + frow, kc));
-                fu[b] = lds_ld16(st + kGuA + kGuB, lds_off(wn * 64 + b * 32 + frow, kc));
-            }
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    ag[a][b] = mfma32(fa[a], fg[b], ag[a][b]);
-                    au[a][b] = mfma32(fa[a], fu[b], au[a][b]);
-                }
-        }
-        if (more) store(smem + (cur ^ 1) * kGuStage);
-        __syncthreads();
-    }
-
+    const int rows = rows_of(count, R_cap);
+    const int nrb = (rows + BM - 1) / BM;
+    const int ntiles = nrb * (N / BN);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31;
+    const int KT = K / kPK;
+
+    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+        const int rb = t % nrb, cb = t / nrb;  // neighbours in t share weight columns
+        const int m0 = rb * BM, n0 = cb * BN;
+        const uint16_t *src[P::NI];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = m0 + wm * 128 + a * 32 + mfma32_row(i, lane);
-            if (r < rows) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b) {
-                    const float g = ag[a][b][i];
-                    const float hv = (g > 0.0f ? g : 0.0f) * au[a][b][i];
-                    h[(size_t)r * N + n0 + wn * 64 + b * 32 + l32] = (uint16_t)f32_to_bf16(hv);
-                }
+        for (int j = 0; j < P::NI; ++j) {
+            const int sr = (wave * P::NI + j) * 16 + (lane >> 2);
+            if (sr < BM) {
+                const int r = min(m0 + sr, rows - 1);
+                src[j] = x + (size_t)(rowlist ? rowlist[r] : r) * K;
+            } else if (sr < BM + BN) {
+                src[j] = wg_t + (size_t)(n0 + sr - BM) * K;
+            } else {
+                src[j] = wu_t + (size_t)(n0 + sr - BM - BN) * K;
             }
         }
+        auto issue = [&](int kt) {
+            char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
+#pragma unroll
+            for (int j = 0; j < P::NI; ++j) {
+                const int row0 = (wave * P::NI + j) * 16;
+                dma_rows16(src[j], kt * kPK, lane, row0, st + row0 * kPRow);
+            }
+        };
+        f32x16 ag[P::FA][P::FB], au[P::FA][P::FB];
+#pragma unroll
+        for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) {
+                ag[a][b] = f32x16{};
+                au[a][b] = f32x16{};
+            }
+        issue(0);
+        if (KT > 1) issue(1);
+        if (KT > 2) issue(2);
+        for (int kt = 0; kt < KT; ++kt) {
+            if (kt + 2 < KT) wait_vmcnt<2 * P::NI>();
+            else if (kt + 1 < KT) wait_vmcnt<P::NI>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            if (kt + 3 < KT) issue(kt + 3);
+            const char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 fa[P::FA], fg[P::FB], fu[P::FB];
+#pragma unroll
+                for (int a = 0; a < P::FA; ++a) fa[a] = frag(st, wm * P::TM + a * 32, s, lane);
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b) {
+                    fg[b] = frag(st, BM + wn * P::TN + b * 32, s, lane);
+                    fu[b] = frag(st, BM + BN + wn * P::TN + b * 32, s, lane);
+                }
+#pragma unroll
+                for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+                    for (int b = 0; b < P::FB; ++b) {
+                        ag[a][b] = mfma32(fa[a], fg[b], ag[a][b]);
+                        au[a][b] = mfma32(fa[a], fu[b], au[a][b]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = m0 + wm * P::TM + a * 32 + mfma32_row(i, lane);
+                if (r < rows) {
+#pragma unroll
+                    for (int b = 0; b < P::FB; ++b) {
+                        const float g = ag[a][b][i];
+                        const float hv = (g > 0.0f ? g : 0.0f) * au[a][b][i];
+                        h[(size_t)r * N + n0 + wn * P::TN + b * 32 + l32] =
+                            (uint16_t)f32_to_bf16(hv);
+                    }
+                }
+            }
+        __syncthreads();  // the next tile refills the ring
+    }
+}
+
+// Number of reduction splits of the overflow-path down GEMM: enough for
+// `grid` work items over `tiles` output tiles, at most 16, dividing the
+// NS stages of the reduction.  Both the GEMM and the reduction of its
+// partial tiles evaluate it from the same device-side row count.
+__device__ __forceinline__ int split_count(int tiles, int grid, int NS) {
+    if (tiles <= 0) return 1;
+    int S = grid / tiles;
+    S = S < 1 ? 1 : (S > 16 ? 16 : S);
+    while (NS % S) --S;
+    return S;
 }
 
 // --------------------------------- down -----------------------------------
-constexpr int kDnBM = 128, kDnBN = 128;
-constexpr int kDnA = kDnBM * kRowBytes;  // 16 KB
-constexpr int kDnB = kDnBN * kRowBytes;  // 16 KB
-constexpr int kDnStage = kDnA + kDnB;
-constexpr int kDnLds = 2 * kDnStage;     // 64 KB
+template <int BM, int BN, int WM, int WN>
+struct DN {
+    static constexpr int NW = WM * WN, NTH = NW * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FA = TM / 32, FB = TN / 32;
+    static constexpr int BROW = BN * 2;                 // bytes of one W_d row slice
+    static constexpr int A_BYTES = BM * kPRow;
+    static constexpr int B_BYTES = kPK * BROW;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = kPStages * STAGE;
+    static constexpr int NIA = BM / (16 * NW);          // A direct loads per wave and stage
+    static constexpr int BR_PER = 1024 / BROW;          // W_d rows per 1 KB direct load
+    static constexpr int NIB = kPK / BR_PER / NW;       // B direct loads per wave and stage
+    static constexpr int NI = NIA + NIB;
+    static_assert(BN == 128, "W_d slice layout assumes 16 chunks per row");
+    static_assert(BM % (16 * NW) == 0 && (kPK / BR_PER) % NW == 0, "stage split");
+};
 
-__global__ __launch_bounds__(kThreads) void down_kernel(
+// W_d slice rows in a stage: 16 chunks of 16 bytes, chunk c at c ^ bsw(row).
+// A transposing fragment read touches 4 consecutive rows x 4 chunks in each
+// half-wave; XOR by 4 (row % 4) puts those 16 chunks in 16 different chunk
+// positions, i.e. all 64 banks once.
+__device__ __forceinline__ int bsw(int row) { return 4 * (row & 3); }
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(WM * WN * 64) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ wd, int K, int N,
     const int32_t *__restrict__ rowlist, const int32_t *__restrict__ count, int R_cap,
-    float *__restrict__ y) {
+    float *__restrict__ y, float *__restrict__ partial) {
+    using P = DN<BM, BN, WM, WN>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    const int rows = count ? min(*count, R_cap) : R_cap;
-    const int m0 = blockIdx.y * kDnBM;
-    if (m0 >= rows) return;
-    const int k0 = blockIdx.x * kDnBN;  // output columns
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    // A (h rows): chunk kc0 of tile rows r0 + 32 i, i < 4
-    const int r0 = tid >> 3, kc0 = tid & 7;
-    int aoff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) aoff[i] = min(m0 + r0 + 32 * i, rows - 1) * N + kc0 * 8;
-    // B (W_d): rows n = 4 nq .. 4 nq + 3 of the stage, columns k0 + 8 ko .. + 7
-    const int nq = tid & 15, ko = tid >> 4;
-    const int boff = (4 * nq) * K + k0 + 8 * ko;
-
-    u32x4 ra[4], rb[4];
-    auto load = [&](int n) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ra[i] = ld16(h + aoff[i] + n);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rb[i] = ld16(wd + boff + (n + i) * K);
-    };
-    auto store = [&](char *st) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) lds_st16(st, lds_off(r0 + 32 * i, kc0), ra[i]);
-        // transpose 4 (n) x 8 (k) -> 8 LDS rows (k) of 4 reduction elements (n)
-        char *sb = st + kDnA;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int w = kk >> 1;
-            uint32_t e[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) e[i] = (kk & 1) ? (rb[i][w] >> 16) : (rb[i][w] & 0xffffu);
-            const u32x2 v{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-            const int row = 8 * ko + kk;
-            *reinterpret_cast<u32x2 *>(sb + lds_off(row, nq >> 1) + (nq & 1) * 8) = v;
-        }
-    };
-    load(0);
-    store(smem);
-    __syncthreads();
-
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-    const int NTK = N / kBK;
-    const int frow = lane & 31;
-    for (int kt = 0; kt < NTK; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < NTK;
-        if (more) load((kt + 1) * kBK);
-        const char *st = smem + cur * kDnStage;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int kc = 2 * s + (lane >> 5);
-            u32x4 fa[2], fb[2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a) fa[a] = lds_ld16(st, lds_off(wm * 64 + a * 32 + frow, kc));
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                fb[b] = lds_ld16(st + kDnA, lds_off(wn * 64 + b * 32 + frow, kc));
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
-        }
-        if (more) store(smem + (cur ^ 1) * kDnStage);
-        __syncthreads();
-    }
-
+    const int rows = rows_of(count, R_cap);
+    const int nrb = (rows + BM - 1) / BM;
+    const int ncb = K / BN;
+    const int tiles = nrb * ncb;
+    const int NS = N / kPK;  // stages over the whole reduction
+    const int S = partial ? split_count(tiles, gridDim.x, NS) : 1;  // reduction splits
+    const int work = tiles * S;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
     const int l32 = lane & 31;
+    const int g4 = (lane >> 4) & 3, i16 = lane & 15;
+
+    for (int wi = blockIdx.x; wi < work; wi += gridDim.x) {
+        const int tile = wi % tiles, sp = wi / tiles;
+        const int rb = tile % nrb, cb = tile / nrb;
+        const int m0 = rb * BM, k0 = cb * BN;
+        const int kt0 = sp * (NS / S), kt1 = kt0 + NS / S;
+
+        const uint16_t *asrc[P::NIA];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int j = 0; j < P::NIA; ++j) {
+            const int sr = (wave * P::NIA + j) * 16 + (lane >> 2);
+            asrc[j] = h + (size_t)min(m0 + sr, rows - 1) * N;
+        }
+        // B: this lane's row within a 1 KB load and its swizzled chunk
+        const int brl = lane >> 4;  // 0..3
+        auto issue = [&](int kt) {
+            char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = m0 + wm * 64 + a * 32 + mfma32_row(i, lane);
-            if (r < rows) {
-                const int yr = rowlist ? rowlist[r] : r;
+            for (int j = 0; j < P::NIA; ++j) {
+                const int row0 = (wave * P::NIA + j) * 16;
+                dma_rows16(asrc[j], kt * kPK, lane, row0, st + row0 * kPRow);
+            }
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    y[(size_t)yr * K + k0 + wn * 64 + b * 32 + l32] = acc[a][b][i];
+            for (int j = 0; j < P::NIB; ++j) {
+                const int row = (wave * P::NIB + j) * P::BR_PER + brl;
+                const int c = (lane & 15) ^ bsw(row);
+                const uint16_t *src = wd + (size_t)(kt * kPK + row) * K + k0 + c * 8;
+                __builtin_amdgcn_global_load_lds(
+                    static_cast<const void *>(src),
+                    (lds_void *)(st + P::A_BYTES + (row - brl) * P::BROW), 16, 0, 0);
+            }
+        };
+        f32x16 acc[P::FA][P::FB];
+#pragma unroll
+        for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) acc[a][b] = f32x16{};
+        const int n_st = kt1 - kt0;
+        issue(kt0);
+        if (n_st > 1) issue(kt0 + 1);
+        if (n_st > 2) issue(kt0 + 2);
+        for (int kt = kt0; kt < kt1; ++kt) {
+            if (kt + 2 < kt1) wait_vmcnt<2 * P::NI>();
+            else if (kt + 1 < kt1) wait_vmcnt<P::NI>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            if (kt + 3 < kt1) issue(kt + 3);
+            const char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
+            const char *bt = st + P::A_BYTES;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 fa[P::FA], fb[P::FB];
+#pragma unroll
+                for (int a = 0; a < P::FA; ++a) fa[a] = frag(st, wm * P::TM + a * 32, s, lane);
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b) {
+                    // lane (g4, i16) supplies row 16 s + 8 (g4 / 2) + 4 hh + i16 / 4,
+                    // columns c0 + 4 (i16 % 4) ..+3 and receives column c0 + i16
+                    const int c0 = wn * P::TN + b * 32 + 16 * (g4 & 1) + 4 * (i16 & 3);
+                    i16x4 v[2];
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int row = 16 * s + 8 * (g4 >> 1) + 4 * hh + (i16 >> 2);
+                        const uint32_t off = row * P::BROW + (((c0 >> 3) ^ bsw(row)) << 4) +
+                                             (c0 & 7) * 2;
+                        v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) i16x4 *)(bt + off));
+                    }
+                    fb[b] = u32x4{__builtin_bit_cast(u32x2, v[0])[0], __builtin_bit_cast(u32x2, v[0])[1],
+                                  __builtin_bit_cast(u32x2, v[1])[0], __builtin_bit_cast(u32x2, v[1])[1]};
+                }
+#pragma unroll
+                for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+                    for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
             }
         }
+
+        if (S == 1) {
+#pragma unroll
+            for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = m0 + wm * P::TM + a * 32 + mfma32_row(i, lane);
+                    if (r < rows) {
+                        const int yr = rowlist ? rowlist[r] : r;
+#pragma unroll
+                        for (int b = 0; b < P::FB; ++b)
+                            y[(size_t)yr * K + k0 + wn * P::TN + b * 32 + l32] = acc[a][b][i];
+                    }
+                }
+        } else {
+            // partial tile of split sp, summed by split_reduce_kernel
+            float *pt = partial + ((size_t)sp * tiles + tile) * (BM * BN);
+#pragma unroll
+            for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rl = wm * P::TM + a * 32 + mfma32_row(i, lane);
+#pragma unroll
+                    for (int b = 0; b < P::FB; ++b)
+                        pt[rl * BN + wn * P::TN + b * 32 + l32] = acc[a][b][i];
+                }
+        }
+        __syncthreads();  // the next work item refills the ring
+    }
 }
 
+// y[row_r] = sum over splits s = 0, 1, ... of the partial tiles (fixed
+// order), when the down GEMM split its reduction.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void split_reduce_kernel(
+    const float *__restrict__ partial, const int32_t *__restrict__ rowlist,
+    const int32_t *__restrict__ count, int R_cap, int K, int N, int grid_down,
+    float *__restrict__ y) {
+    const int rows = rows_of(count, R_cap);
+    const int nrb = (rows + BM - 1) / BM;
+    const int tiles = nrb * (K / BN);
+    const int S = split_count(tiles, grid_down, N / kPK);
+    if (S == 1) return;
+    const int K4 = K / 4;
+    for (int q = blockIdx.x * 256 + threadIdx.x; q < rows * K4; q += gridDim.x * 256) {
+        const int r = q / K4, col = 4 * (q % K4);
+        const int tile = (col / BN) * nrb + r / BM;
+        const float *src = partial + (size_t)tile * (BM * BN) + (r % BM) * BN + col % BN;
+        float4 sum = *reinterpret_cast<const float4 *>(src);
+        for (int s2 = 1; s2 < S; ++s2) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + (size_t)s2 * tiles * (BM * BN));
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
+        }
+        *reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col) = sum;
+    }
+}
+
+template <typename F>
+hipError_t set_lds(F *kernel, int bytes, bool &done) {
+    if (done) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done = true;
+    return e;
+}
+
+// dense comparator shapes and overflow-path shapes
+using GuDense = GU<256, 128, 4, 2>;
+using GuRows = GU<64, 128, 1, 4>;
+using Dn = DN<128, 128, 2, 2>;
+constexpr int kSplitGrid = 256;  // work items of the split down GEMM
+
 }  // namespace
+
+size_t split_partial_bytes() { return (size_t)kSplitGrid * 128 * 128 * sizeof(float); }
 
 hipError_t launch_gateup(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t, int K,
                          int N, const int32_t *rowlist, const int32_t *count, int R_cap,
                          uint16_t *h, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gateup_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kGuLds);
+    if (rowlist) {
+        static bool attr = false;
+        hipError_t e = set_lds(&gateup_kernel<64, 128, 1, 4>, GuRows::LDS, attr);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        const int tiles = (R_cap + 63) / 64 * (N / 128);
+        const int grid = tiles < 1024 ? tiles : 1024;
+        hipLaunchKernelGGL((gateup_kernel<64, 128, 1, 4>), dim3(grid), dim3(GuRows::NTH),
+                           GuRows::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, h);
+    } else {
+        static bool attr = false;
+        hipError_t e = set_lds(&gateup_kernel<256, 128, 4, 2>, GuDense::LDS, attr);
+        if (e != hipSuccess) return e;
+        const int grid = (R_cap + 255) / 256 * (N / 128);
+        hipLaunchKernelGGL((gateup_kernel<256, 128, 4, 2>), dim3(grid), dim3(GuDense::NTH),
+                           GuDense::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, h);
     }
-    dim3 grid(N / kGuBN, (R_cap + kGuBM - 1) / kGuBM);
-    hipLaunchKernelGGL(gateup_kernel, grid, dim3(kThreads), kGuLds, s, x, wg_t, wu_t, K, N,
-                       rowlist, count, R_cap, h);
     return hipGetLastError();
 }
 
 hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
-                       hipStream_t s) {
+                       float *partial, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&down_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kDnLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    dim3 grid(K / kDnBN, (R_cap + kDnBM - 1) / kDnBM);
-    hipLaunchKernelGGL(down_kernel, grid, dim3(kThreads), kDnLds, s, h, wd, K, N, rowlist,
-                       count, R_cap, y);
+    static bool attr = false;
+    hipError_t e = set_lds(&down_kernel<128, 128, 2, 2>, Dn::LDS, attr);
+    if (e != hipSuccess) return e;
+    const int tiles = (R_cap + 127) / 128 * (K / 128);
+    const int grid = partial ? kSplitGrid : tiles;
+    hipLaunchKernelGGL((down_kernel<128, 128, 2, 2>), dim3(grid), dim3(Dn::NTH), Dn::LDS, s, h,
+                       wd, K, N, rowlist, count, R_cap, y, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
+                               const int32_t *count, int R_cap, int K, int N, float *y,
+                               hipStream_t s) {
+    if (R_cap <= 0) return hipSuccess;
+    // enough workgroups for the largest split case: at most kSplitGrid tiles
+    int grid = (int)(((size_t)R_cap * K / 4 + 255) / 256);
+    grid = grid < 1024 ? grid : 1024;
+    hipLaunchKernelGGL((split_reduce_kernel<128, 128>), dim3(grid), dim3(256), 0, s, partial,
+                       rowlist, count, R_cap, K, N, kSplitGrid, y);
     return hipGetLastError();
 }
 

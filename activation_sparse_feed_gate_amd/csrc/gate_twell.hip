@@ -9,10 +9,14 @@
 // reported for a retry).
 //
 // gfx950 design
-// - Macro tile 256 rows x 256 columns, 4 waves in a 2 x 2 grid, each wave
-//   owning 128 x 128 outputs as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
-//   (256 fp32 accumulators per lane).  K advances 64 at a time through a
-//   double-buffered, XOR-swizzled LDS stage (2 x 64 KB).
+// - Macro tile 256 rows x 256 columns, 8 waves (two per SIMD, so one wave's
+//   loads overlap the other's matrix work) in a 4 x 2 grid, each wave owning
+//   64 x 128 outputs as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32
+//   accumulators per lane).  Operands stream from global memory straight into
+//   LDS (no register staging) through a 4-stage ring, 32 reduction elements
+//   per stage, three stages ahead of the multiplication.  Tiles are visited
+//   in groups of 8 row blocks so that the workgroups resident on an XCD at a
+//   time share operands in its L2.
 // - Epilogue without an LDS round trip: in the 32x32 MFMA result layout one
 //   accumulator register of a block holds 32 consecutive columns of two rows
 //   (lanes 0-31 and 32-63), so one 64-bit wavefront ballot of (z > 0) gives
@@ -20,110 +24,111 @@
 //   and popcount of the mask bits below a lane gives its slot, in ascending
 //   column order.  With T = 128 a tile is exactly one wave's 128 columns;
 //   with T = 256 it spans the two waves of a wave row, which exchange their
-//   half counts through LDS.
+//   half counts through LDS.  The 64 row counts of a wave are gathered into
+//   one register (lane r holds row r) and stored by one instruction.
 // - Each workgroup writes one bit per row (overflowing or not) for its column
 //   block, so no buffer needs clearing beforehand; the compaction kernel ORs
 //   the column blocks and lists the set rows in ascending order.
 #include "tw_device.hpp"
+#include "tw_gemm.hpp"
 #include "tw_internal.hpp"
 
 namespace tw {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kStageBytes = kGateBM * kRowBytes;           // 32 KB per operand
-constexpr int kLdsTiles = 4 * kStageBytes;                  // A, B double-buffered
+constexpr int kThreads = 512;                               // 8 waves, 2 per SIMD
+constexpr int kStageBytes = 2 * kGateBM * kPRow;            // A and B rows of one stage: 32 KB
+constexpr int kLdsTiles = kPStages * kStageBytes;           // 128 KB ring
 constexpr int kLdsBytes = kLdsTiles + 64 + 2 * kGateBM * 4; // + row flags + half counts
+
+// Tile (bm, bn) of workgroup `bid`: grouped ordering.  Consecutive
+// workgroups walk a group of up to 8 row blocks column block by column
+// block, so the ~32 workgroups resident on one XCD at a time share about 8 A
+// row blocks and 4 weight column blocks in that XCD's L2.
+__device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int &bm, int &bn) {
+    constexpr int G = 8;
+    const int group = bid / (G * nbn);
+    const int first = group * G;
+    const int gm = min(G, nbm - first);
+    const int t = bid - group * G * nbn;
+    bm = first + t % gm;
+    bn = t / gm;
+}
 
 template <int T>
 __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t, int M, int K, int N,
-    int C, int NBN, float *__restrict__ tw_val, int32_t *__restrict__ tw_idx,
+    int C, int NBM, int NBN, float *__restrict__ tw_val, int32_t *__restrict__ tw_idx,
     int32_t *__restrict__ tw_cnt, uint32_t *__restrict__ oflag, float *__restrict__ zdbg) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    char *As = smem;
-    char *Bs = smem + 2 * kStageBytes;
     uint32_t *s_flag = reinterpret_cast<uint32_t *>(smem + kLdsTiles);
     int *s_half = reinterpret_cast<int *>(smem + kLdsTiles + 64);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int bn = blockIdx.x % NBN;
-    const int bm = blockIdx.x / NBN;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves, 64 x 128 outputs each
+    int bm, bn;
+    tile_of(blockIdx.x, NBM, NBN, bm, bn);
     const int m0 = bm * kGateBM, n0 = bn * kGateBN;
 
     if (tid < 8) s_flag[tid] = 0u;
 
-    // This thread moves chunk kc = tid % 8 of tile rows tid/8 + 32*i, i < 8.
-    const int r0 = tid >> 3, kc0 = tid & 7;
-    int aoff[8], boff[8];
+    // Each wave streams rows [32 wave, 32 wave + 32) of both operands: two
+    // 16-row direct loads per operand and stage (rows past M or N repeat the
+    // last row; their results are never stored).
+    const uint16_t *asrc[2], *bsrc[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int ra = min(m0 + r0 + 32 * i, M - 1);
-        const int rb = min(n0 + r0 + 32 * i, N - 1);
-        aoff[i] = ra * K + kc0 * 8;
-        boff[i] = rb * K + kc0 * 8;
+    for (int j = 0; j < 2; ++j) {
+        const int r = wave * 32 + j * 16 + (lane >> 2);
+        asrc[j] = x + (size_t)min(m0 + r, M - 1) * K;
+        bsrc[j] = wg_t + (size_t)min(n0 + r, N - 1) * K;
     }
-    u32x4 ra[8], rb[8];
+    auto issue = [&](int kt) {
+        char *st = smem + (kt & (kPStages - 1)) * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        ra[i] = ld16(x + aoff[i]);
-        rb[i] = ld16(wg_t + boff[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        lds_st16(As, lds_off(r0 + 32 * i, kc0), ra[i]);
-        lds_st16(Bs, lds_off(r0 + 32 * i, kc0), rb[i]);
-    }
-    __syncthreads();
+        for (int j = 0; j < 2; ++j) {
+            const int row0 = wave * 32 + j * 16;
+            dma_rows16(asrc[j], kt * kPK, lane, row0, st + row0 * kPRow);
+            dma_rows16(bsrc[j], kt * kPK, lane, row0, st + (kGateBM + row0) * kPRow);
+        }
+    };
 
-    f32x16 acc[4][4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-    const int KT = K / kBK;
-    const int frow = lane & 31;
+    const int KT = K / kPK;
+    issue(0);
+    if (KT > 1) issue(1);
+    if (KT > 2) issue(2);
     for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < KT;
-        if (more) {
-            const int k1 = (kt + 1) * kBK;
+        // stage kt has landed once at most the later stages' 4 loads each
+        // are outstanding; the barrier then publishes it to every wave (and
+        // tells every wave that stage kt-1 is no longer being read)
+        if (kt + 2 < KT) wait_vmcnt<8>();
+        else if (kt + 1 < KT) wait_vmcnt<4>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (kt + 3 < KT) issue(kt + 3);
+        const char *st = smem + (kt & (kPStages - 1)) * kStageBytes;
+        const char *bt = st + kGateBM * kPRow;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                ra[i] = ld16(x + aoff[i] + k1);
-                rb[i] = ld16(wg_t + boff[i] + k1);
-            }
-        }
-        const char *Ac = As + cur * kStageBytes;
-        const char *Bc = Bs + cur * kStageBytes;
+        for (int s = 0; s < 2; ++s) {
+            u32x4 fa[2], fb[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int kc = 2 * s + (lane >> 5);
-            u32x4 fa[4], fb[4];
+            for (int a = 0; a < 2; ++a) fa[a] = frag(st, wm * 64 + a * 32, s, lane);
 #pragma unroll
-            for (int a = 0; a < 4; ++a) fa[a] = lds_ld16(Ac, lds_off(wm * 128 + a * 32 + frow, kc));
+            for (int b = 0; b < 4; ++b) fb[b] = frag(bt, wn * 128 + b * 32, s, lane);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) fb[b] = lds_ld16(Bc, lds_off(wn * 128 + b * 32 + frow, kc));
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 2; ++a)
 #pragma unroll
                 for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
         }
-        if (more) {
-            char *An = As + (cur ^ 1) * kStageBytes;
-            char *Bn = Bs + (cur ^ 1) * kStageBytes;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                lds_st16(An, lds_off(r0 + 32 * i, kc0), ra[i]);
-                lds_st16(Bn, lds_off(r0 + 32 * i, kc0), rb[i]);
-            }
-        }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---------------- epilogue: ReLU + TwELL pack + row overflow bits ----
     const int l32 = lane & 31;
@@ -133,11 +138,12 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     const bool live = ncol0 < N;      // false only in a half-empty last column block
     const int NT = N / T;
     const int t = ncol0 / T;
+    const int wrow0 = m0 + wm * 64;   // first of the 64 rows this wave holds
 
     if (T == 256) {
         // pass 1: this wave's half-tile count of every row it holds
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < 2; ++a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 int tot = 0;
@@ -146,19 +152,23 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
                     const uint64_t bal = __ballot(acc[a][b][i] > 0.0f);
                     tot += __popc(half ? (uint32_t)(bal >> 32) : (uint32_t)bal);
                 }
-                const int rloc = wm * 128 + a * 32 + mfma32_row(i, lane);
+                const int rloc = wm * 64 + a * 32 + mfma32_row(i, lane);
                 if (l32 == 0) s_half[wn * kGateBM + rloc] = tot;
             }
         }
         __syncthreads();
     }
 
+    // lane r collects the count of wave row r; bit r of `over` marks an
+    // overflowing row (wave-uniform)
+    int cnt_lane = 0;
+    uint64_t over = 0;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+    for (int a = 0; a < 2; ++a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int rloc = wm * 128 + a * 32 + mfma32_row(i, lane);
-            const int m = m0 + rloc;
+            const int rw = a * 32 + mfma32_row(i, lane);  // wave row of this lane
+            const int m = wrow0 + rw;
             uint32_t mk[4];
             int pre[4];
             int tot = 0;
@@ -170,12 +180,10 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
                 tot += __popc(mk[b]);
             }
             int off = 0, total = tot;
-            bool owner = true;  // the wave that stores the count of this (row, tile)
             if (T == 256) {
-                const int other = s_half[(wn ^ 1) * kGateBM + rloc];
+                const int other = s_half[(wn ^ 1) * kGateBM + wm * 64 + rw];
                 off = wn ? other : 0;
                 total = tot + other;
-                owner = wn == 0;
             }
             if (m < M && live) {
                 const size_t tb = ((size_t)m * NT + t) * C;
@@ -190,16 +198,29 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
                         }
                     }
                 }
-                if (owner && l32 == 0) {
-                    tw_cnt[(size_t)m * NT + t] = total;
-                    if (total > C) atomicOr(&s_flag[rloc >> 5], 1u << (rloc & 31));
-                }
                 if (zdbg) {
 #pragma unroll
                     for (int b = 0; b < 4; ++b)
                         zdbg[(size_t)m * N + ncol0 + b * 32 + l32] = acc[a][b][i];
                 }
             }
+            // rows of lanes 0 and 32 (the two rows of this register)
+            const int rA = a * 32 + mfma32_row(i, 0), rB = rA + 4;
+            const int tA = __builtin_amdgcn_readlane(total, 0);
+            const int tB = __builtin_amdgcn_readlane(total, 32);
+            cnt_lane = lane == rA ? tA : cnt_lane;
+            cnt_lane = lane == rB ? tB : cnt_lane;
+            // rows past M repeat row M-1 and must not be routed
+            if (tA > C && wrow0 + rA < M) over |= 1ull << rA;
+            if (tB > C && wrow0 + rB < M) over |= 1ull << rB;
+        }
+    }
+    const bool owner = T == 128 || wn == 0;  // the wave that stores this tile's counts
+    if (owner && live) {
+        if (wrow0 + lane < M) tw_cnt[(size_t)(wrow0 + lane) * NT + t] = cnt_lane;
+        if (lane == 0 && over) {
+            if ((uint32_t)over) atomicOr(&s_flag[wm * 2], (uint32_t)over);
+            if ((uint32_t)(over >> 32)) atomicOr(&s_flag[wm * 2 + 1], (uint32_t)(over >> 32));
         }
     }
     __syncthreads();
@@ -265,7 +286,7 @@ hipError_t launch_gate_t(const uint16_t *x, const uint16_t *wg_t, int M, int K, 
     const int NBN = gate_col_blocks(N);
     const int NBM = (M + kGateBM - 1) / kGateBM;
     hipLaunchKernelGGL(gate_twell_kernel<T>, dim3(NBN * NBM), dim3(kThreads), kLdsBytes, s, x,
-                       wg_t, M, K, N, C, NBN, tw_val, tw_idx, tw_cnt, oflag, z_debug);
+                       wg_t, M, K, N, C, NBM, NBN, tw_val, tw_idx, tw_cnt, oflag, z_debug);
     return hipGetLastError();
 }
 

@@ -41,7 +41,11 @@ tw_status check_shape(int M, int K, int N, int T, int C, int R_max) {
 size_t pack_ws(int M, int N) {
     return round_up((size_t)tw::gate_col_blocks(N) * tw::row_words(M) * 4, 256);
 }
-size_t sparse_ws(int R_max, int N) { return round_up((size_t)R_max * N * 2, 256); }
+// overflow path: h rows [R_max][N] bf16, then the split partial tiles
+size_t sparse_ws(int R_max, int N) {
+    if (R_max == 0) return 0;
+    return round_up((size_t)R_max * N * 2, 256) + tw::split_partial_bytes();
+}
 
 tw_status record(void *const *events, int i, hipStream_t s) {
     if (!events) return TW_OK;
@@ -157,7 +161,9 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    uint16_t *h = static_cast<uint16_t *>(ws);
+    char *w = static_cast<char *>(ws);
+    uint16_t *h = reinterpret_cast<uint16_t *>(w);
+    float *partial = reinterpret_cast<float *>(w + round_up((size_t)R_max * N * 2, 256));
     TW_TRY(record(events, 0, s));
     TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx, tw_cnt,
                                              y, s),
@@ -166,9 +172,12 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     TW_TRY(launched(tw::launch_gateup(x, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, s),
                     "fallback gate+up launch"));
     TW_TRY(record(events, 2, s));
-    TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, s),
+    TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, partial, s),
                     "fallback down launch"));
     TW_TRY(record(events, 3, s));
+    TW_TRY(launched(tw::launch_split_reduce(partial, ovf_rows, ovf_count, R_max, K, N, y, s),
+                    "fallback split-reduce launch"));
+    TW_TRY(record(events, 4, s));
     return TW_OK;
 }
 
@@ -193,7 +202,8 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu
     TW_TRY(launched(tw::launch_gateup(x, wg_t, wu_t, K, N, nullptr, nullptr, M, h, s),
                     "dense gate+up launch"));
     TW_TRY(record(events, 1, s));
-    TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, s), "dense down launch"));
+    TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, nullptr, s),
+                    "dense down launch"));
     TW_TRY(record(events, 2, s));
     return TW_OK;
 }

@@ -35,9 +35,15 @@ hipError_t launch_gateup(const uint16_t *x, const uint16_t *wg_t, const uint16_t
                          int R_cap, uint16_t *h, hipStream_t s);
 
 // y[row_r][k] = sum_n h[r][n] * wd[n][k] (fp32) for r < rows, with row_r =
-// rowlist[r] or r as above.
+// rowlist[r] or r as above.  With a `partial` buffer (split_partial_bytes())
+// the reduction is split when there are few rows, and launch_split_reduce
+// must follow on the stream to sum the partial tiles into y.
 hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
-                       hipStream_t s);
+                       float *partial, hipStream_t s);
+hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
+                               const int32_t *count, int R_cap, int K, int N, float *y,
+                               hipStream_t s);
+size_t split_partial_bytes();
 
 }  // namespace tw

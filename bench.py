@@ -180,7 +180,7 @@ def main():
     # ---- timed: the sparse path ----
     Ks = args.steps
     evp = [hev.create(3) for _ in range(Ks)]
-    evs = [hev.create(4) for _ in range(Ks)]
+    evs = [hev.create(5) for _ in range(Ks)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(Ks):
@@ -206,6 +206,7 @@ def main():
         "sparse_updown": avg(evs, 0),
         "fallback_gateup": avg(evs, 1),
         "fallback_down": avg(evs, 2),
+        "fallback_reduce": avg(evs, 3),
     }
     kern_dense = {"dense_gateup": avg(evd, 0), "dense_down": avg(evd, 1)}
     for l in (evp, evs, evd):

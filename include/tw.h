@@ -41,7 +41,8 @@
  *   recorded on `stream` before the first kernel and events[i+1] after
  *   kernel i, so per-kernel durations can be read with
  *   hipEventElapsedTime.  tw_pack_gate launches 2 kernels, tw_sparse_ffn_fwd
- *   3 and tw_ffn_fwd 2.
+ *   4 (sparse up+down, then the overflow rows' gate+up, down and the sum of
+ *   split partial results) and tw_ffn_fwd 2.
  *
  * Weight layout (one layout serves every path): wg_t, wu_t and wd are all
  * [N][K] row-major bf16.  wg_t and wu_t hold W_g and W_u transposed, so the
