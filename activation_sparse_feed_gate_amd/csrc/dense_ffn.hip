@@ -39,7 +39,7 @@ __device__ __forceinline__ int rows_of(const int32_t *count, int R_cap) {
 }
 
 // ------------------------------ gate + up ---------------------------------
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 struct GU {
     static constexpr int NW = WM * WN, NTH = NW * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -47,17 +47,17 @@ struct GU {
     static constexpr int SR = BM + 2 * BN;            // stage rows: A, then W_g, then W_u
     static constexpr int NI = SR / (16 * NW);         // direct loads per wave and stage
     static constexpr int STAGE = SR * kPRow;
-    static constexpr int LDS = kPStages * STAGE;
+    static constexpr int LDS = S * STAGE;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
     static_assert(SR % (16 * NW) == 0 && BM % 16 == 0 && BN % 16 == 0, "stage rows");
 };
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t,
     const uint16_t *__restrict__ wu_t, int K, int N, const int32_t *__restrict__ rowlist,
     const int32_t *__restrict__ count, int R_cap, uint16_t *__restrict__ h) {
-    using P = GU<BM, BN, WM, WN>;
+    using P = GU<BM, BN, WM, WN, S>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int rows = rows_of(count, R_cap);
@@ -85,8 +85,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                 src[j] = wu_t + (size_t)(n0 + sr - BM - BN) * K;
             }
         }
-        auto issue = [&](int kt) {
-            char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
+        auto issue = [&](int kt, char *st) {
 #pragma unroll
             for (int j = 0; j < P::NI; ++j) {
                 const int row0 = (wave * P::NI + j) * 16;
@@ -101,16 +100,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                 ag[a][b] = f32x16{};
                 au[a][b] = f32x16{};
             }
-        issue(0);
-        if (KT > 1) issue(1);
-        if (KT > 2) issue(2);
-        for (int kt = 0; kt < KT; ++kt) {
-            if (kt + 2 < KT) wait_vmcnt<2 * P::NI>();
-            else if (kt + 1 < KT) wait_vmcnt<P::NI>();
-            else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            if (kt + 3 < KT) issue(kt + 3);
-            const char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
+        auto compute = [&](const char *st) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 u32x4 fa[P::FA], fg[P::FB], fu[P::FB];
@@ -129,7 +119,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                         au[a][b] = mfma32(fa[a], fu[b], au[a][b]);
                     }
             }
-        }
+        };
+        kloop<S, P::NI>(0, KT, smem, P::STAGE, issue, compute);
 #pragma unroll
         for (int a = 0; a < P::FA; ++a)
 #pragma unroll
@@ -162,7 +153,7 @@ __device__ __forceinline__ int split_count(int tiles, int grid, int NS) {
 }
 
 // --------------------------------- down -----------------------------------
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S>
 struct DN {
     static constexpr int NW = WM * WN, NTH = NW * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;
@@ -171,7 +162,7 @@ struct DN {
     static constexpr int A_BYTES = BM * kPRow;
     static constexpr int B_BYTES = kPK * BROW;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = kPStages * STAGE;
+    static constexpr int LDS = S * STAGE;
     static constexpr int NIA = BM / (16 * NW);          // A direct loads per wave and stage
     static constexpr int BR_PER = 1024 / BROW;          // W_d rows per 1 KB direct load
     static constexpr int NIB = kPK / BR_PER / NW;       // B direct loads per wave and stage
@@ -186,12 +177,12 @@ struct DN {
 // positions, i.e. all 64 banks once.
 __device__ __forceinline__ int bsw(int row) { return 4 * (row & 3); }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int STG>
 __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ wd, int K, int N,
     const int32_t *__restrict__ rowlist, const int32_t *__restrict__ count, int R_cap,
     float *__restrict__ y, float *__restrict__ partial) {
-    using P = DN<BM, BN, WM, WN>;
+    using P = DN<BM, BN, WM, WN, STG>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int rows = rows_of(count, R_cap);
@@ -221,8 +212,7 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
         }
         // B: this lane's row within a 1 KB load and its swizzled chunk
         const int brl = lane >> 4;  // 0..3
-        auto issue = [&](int kt) {
-            char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
+        auto issue = [&](int kt, char *st) {
 #pragma unroll
             for (int j = 0; j < P::NIA; ++j) {
                 const int row0 = (wave * P::NIA + j) * 16;
@@ -243,17 +233,7 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
         for (int a = 0; a < P::FA; ++a)
 #pragma unroll
             for (int b = 0; b < P::FB; ++b) acc[a][b] = f32x16{};
-        const int n_st = kt1 - kt0;
-        issue(kt0);
-        if (n_st > 1) issue(kt0 + 1);
-        if (n_st > 2) issue(kt0 + 2);
-        for (int kt = kt0; kt < kt1; ++kt) {
-            if (kt + 2 < kt1) wait_vmcnt<2 * P::NI>();
-            else if (kt + 1 < kt1) wait_vmcnt<P::NI>();
-            else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            if (kt + 3 < kt1) issue(kt + 3);
-            const char *st = smem + (kt & (kPStages - 1)) * P::STAGE;
+        auto compute = [&](const char *st) {
             const char *bt = st + P::A_BYTES;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -274,15 +254,17 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
                         v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                             (__attribute__((address_space(3))) i16x4 *)(bt + off));
                     }
-                    fb[b] = u32x4{__builtin_bit_cast(u32x2, v[0])[0], __builtin_bit_cast(u32x2, v[0])[1],
-                                  __builtin_bit_cast(u32x2, v[1])[0], __builtin_bit_cast(u32x2, v[1])[1]};
+                    const u32x2 lo = __builtin_bit_cast(u32x2, v[0]);
+                    const u32x2 hi = __builtin_bit_cast(u32x2, v[1]);
+                    fb[b] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
 #pragma unroll
                 for (int a = 0; a < P::FA; ++a)
 #pragma unroll
                     for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
             }
-        }
+        };
+        kloop<STG, P::NI>(kt0, kt1, smem, P::STAGE, issue, compute);
 
         if (S == 1) {
 #pragma unroll
@@ -352,10 +334,12 @@ hipError_t set_lds(F *kernel, int bytes, bool &done) {
     return e;
 }
 
-// dense comparator shapes and overflow-path shapes
-using GuDense = GU<256, 128, 4, 2>;
-using GuRows = GU<64, 128, 1, 4>;
-using Dn = DN<128, 128, 2, 2>;
+// dense comparator shapes and overflow-path shapes (the thin overflow
+// tiles do little matrix work per stage, so they keep more stages in flight)
+using GuDense = GU<256, 128, 4, 2, 4>;
+using GuRows = GU<64, 128, 1, 4, 6>;
+using DnDense = DN<128, 128, 2, 2, 4>;
+using DnRows = DN<128, 128, 2, 2, 8>;
 constexpr int kSplitGrid = 256;  // work items of the split down GEMM
 
 }  // namespace
@@ -368,18 +352,18 @@ hipError_t launch_gateup(const uint16_t *x, const uint16_t *wg_t, const uint16_t
     if (R_cap <= 0) return hipSuccess;
     if (rowlist) {
         static bool attr = false;
-        hipError_t e = set_lds(&gateup_kernel<64, 128, 1, 4>, GuRows::LDS, attr);
+        hipError_t e = set_lds(&gateup_kernel<64, 128, 1, 4, 6>, GuRows::LDS, attr);
         if (e != hipSuccess) return e;
         const int tiles = (R_cap + 63) / 64 * (N / 128);
         const int grid = tiles < 1024 ? tiles : 1024;
-        hipLaunchKernelGGL((gateup_kernel<64, 128, 1, 4>), dim3(grid), dim3(GuRows::NTH),
+        hipLaunchKernelGGL((gateup_kernel<64, 128, 1, 4, 6>), dim3(grid), dim3(GuRows::NTH),
                            GuRows::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, h);
     } else {
         static bool attr = false;
-        hipError_t e = set_lds(&gateup_kernel<256, 128, 4, 2>, GuDense::LDS, attr);
+        hipError_t e = set_lds(&gateup_kernel<256, 128, 4, 2, 4>, GuDense::LDS, attr);
         if (e != hipSuccess) return e;
         const int grid = (R_cap + 255) / 256 * (N / 128);
-        hipLaunchKernelGGL((gateup_kernel<256, 128, 4, 2>), dim3(grid), dim3(GuDense::NTH),
+        hipLaunchKernelGGL((gateup_kernel<256, 128, 4, 2, 4>), dim3(grid), dim3(GuDense::NTH),
                            GuDense::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, h);
     }
     return hipGetLastError();
@@ -389,13 +373,20 @@ hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
                        float *partial, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    static bool attr = false;
-    hipError_t e = set_lds(&down_kernel<128, 128, 2, 2>, Dn::LDS, attr);
-    if (e != hipSuccess) return e;
     const int tiles = (R_cap + 127) / 128 * (K / 128);
-    const int grid = partial ? kSplitGrid : tiles;
-    hipLaunchKernelGGL((down_kernel<128, 128, 2, 2>), dim3(grid), dim3(Dn::NTH), Dn::LDS, s, h,
-                       wd, K, N, rowlist, count, R_cap, y, partial);
+    if (partial) {
+        static bool attr = false;
+        hipError_t e = set_lds(&down_kernel<128, 128, 2, 2, 8>, DnRows::LDS, attr);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((down_kernel<128, 128, 2, 2, 8>), dim3(kSplitGrid), dim3(DnRows::NTH),
+                           DnRows::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial);
+    } else {
+        static bool attr = false;
+        hipError_t e = set_lds(&down_kernel<128, 128, 2, 2, 4>, DnDense::LDS, attr);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((down_kernel<128, 128, 2, 2, 4>), dim3(tiles), dim3(DnDense::NTH),
+                           DnDense::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial);
+    }
     return hipGetLastError();
 }
 

@@ -37,8 +37,9 @@ namespace tw {
 namespace {
 
 constexpr int kThreads = 512;                               // 8 waves, 2 per SIMD
+constexpr int kStages = 4;
 constexpr int kStageBytes = 2 * kGateBM * kPRow;            // A and B rows of one stage: 32 KB
-constexpr int kLdsTiles = kPStages * kStageBytes;           // 128 KB ring
+constexpr int kLdsTiles = kStages * kStageBytes;            // 128 KB ring
 constexpr int kLdsBytes = kLdsTiles + 64 + 2 * kGateBM * 4; // + row flags + half counts
 
 // Tile (bm, bn) of workgroup `bid`: grouped ordering.  Consecutive
@@ -84,8 +85,7 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
         asrc[j] = x + (size_t)min(m0 + r, M - 1) * K;
         bsrc[j] = wg_t + (size_t)min(n0 + r, N - 1) * K;
     }
-    auto issue = [&](int kt) {
-        char *st = smem + (kt & (kPStages - 1)) * kStageBytes;
+    auto issue = [&](int kt, char *st) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row0 = wave * 32 + j * 16;
@@ -100,20 +100,7 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-    const int KT = K / kPK;
-    issue(0);
-    if (KT > 1) issue(1);
-    if (KT > 2) issue(2);
-    for (int kt = 0; kt < KT; ++kt) {
-        // stage kt has landed once at most the later stages' 4 loads each
-        // are outstanding; the barrier then publishes it to every wave (and
-        // tells every wave that stage kt-1 is no longer being read)
-        if (kt + 2 < KT) wait_vmcnt<8>();
-        else if (kt + 1 < KT) wait_vmcnt<4>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (kt + 3 < KT) issue(kt + 3);
-        const char *st = smem + (kt & (kPStages - 1)) * kStageBytes;
+    auto compute = [&](const char *st) {
         const char *bt = st + kGateBM * kPRow;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -127,7 +114,8 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
 #pragma unroll
                 for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
         }
-    }
+    };
+    kloop<kStages, 4>(0, K / kPK, smem, kStageBytes, issue, compute);
     __syncthreads();
 
     // ---------------- epilogue: ReLU + TwELL pack + row overflow bits ----

@@ -1,7 +1,7 @@
 // tw_gemm.hpp -- the software pipeline shared by the bf16 MFMA GEMMs:
 // operands stream from global memory straight into LDS (global_load_lds,
-// no register staging) through a ring of 4 stages, each 32 reduction
-// elements deep, so three stages are in flight while one is multiplied.
+// no register staging) through a ring of S stages, each 32 reduction
+// elements deep, so S-1 stages are in flight while one is multiplied.
 #pragma once
 
 #include "tw_device.hpp"
@@ -12,7 +12,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kPK = 32;         // reduction depth of one pipeline stage
 constexpr int kPRow = kPK * 2;  // 64 bytes per operand row in a stage
-constexpr int kPStages = 4;
 
 // Stage layout: operand row r occupies 64 bytes (4 chunks of 16 bytes);
 // logical chunk kc lives at physical chunk kc ^ swz(r).  Across the 16 rows
@@ -28,6 +27,43 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `later` stages of NI direct loads each are still in
+// flight (the loads of one wave complete in issue order).
+template <int NI, int S>
+__device__ __forceinline__ void wait_later(int later) {
+    switch (later) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: if constexpr (S > 2) { wait_vmcnt<NI>(); break; } [[fallthrough]];
+    case 2: if constexpr (S > 3) { wait_vmcnt<2 * NI>(); break; } [[fallthrough]];
+    case 3: if constexpr (S > 4) { wait_vmcnt<3 * NI>(); break; } [[fallthrough]];
+    case 4: if constexpr (S > 5) { wait_vmcnt<4 * NI>(); break; } [[fallthrough]];
+    case 5: if constexpr (S > 6) { wait_vmcnt<5 * NI>(); break; } [[fallthrough]];
+    default: if constexpr (S > 7) { wait_vmcnt<6 * NI>(); } else { wait_vmcnt<0>(); } break;
+    }
+}
+
+// The k-loop over stages [kt0, kt1) through a ring of S slots of
+// `stage_bytes` at `ring`.  issue(kt, slot) enqueues this wave's NI direct
+// loads of stage kt into `slot`; compute(slot) multiplies a landed stage.
+// Every wave waits for its own loads of stage kt, then one barrier makes
+// the whole stage visible and also certifies that the slot refilled next
+// (read in the previous iteration) is free.  A bare s_barrier is used: the
+// fence of __syncthreads() would drain the loads still in flight.
+template <int S, int NI, typename Issue, typename Compute>
+__device__ __forceinline__ void kloop(int kt0, int kt1, char *ring, int stage_bytes, Issue issue,
+                                      Compute compute) {
+    static_assert(S >= 2 && S <= 8 && NI * (S - 2) < 64, "ring depth");
+    const int n = kt1 - kt0;
+    for (int j = 0; j < S - 1 && j < n; ++j) issue(kt0 + j, ring + (j % S) * stage_bytes);
+    for (int i = 0; i < n; ++i) {
+        const int later = min(S - 2, n - 1 - i);
+        wait_later<NI, S>(later);
+        __builtin_amdgcn_s_barrier();
+        if (i + S - 1 < n) issue(kt0 + i + S - 1, ring + ((i + S - 1) % S) * stage_bytes);
+        compute(ring + (i % S) * stage_bytes);
+    }
 }
 
 // One wavefront-wide direct load: 16 operand rows x 64 bytes (1 KB) into LDS

@@ -120,6 +120,11 @@ def main():
     ap.add_argument("--density", type=float, default=None, help="override the target density")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="also run a plain elementwise copy of MB megabytes (fp32, read + "
+                         "write) so that a counter profile can scale FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of HIP-graph replays")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -165,6 +170,15 @@ def main():
     def dense(ev=None):
         tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd, stream=stream, events=ev)
 
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)  # reads and writes n * 4 bytes
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
         dense()
@@ -177,25 +191,62 @@ def main():
     R = int(ovf.sum())
     sparse_nnz = int(nnz[~ovf].sum())
 
-    # ---- timed: the sparse path ----
     Ks = args.steps
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(Ks):
+            fn(s_)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / Ks
+
+    # ---- per-kernel durations: eager launches with HIP events between kernels ----
     evp = [hev.create(3) for _ in range(Ks)]
     evs = [hev.create(5) for _ in range(Ks)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(Ks):
-        step(evp[s], evs[s])
-    torch.cuda.synchronize()
-    t_sparse = (time.perf_counter() - t0) / Ks
-
-    # ---- timed: the dense comparator ----
     evd = [hev.create(3) for _ in range(Ks)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(Ks):
-        dense(evd[s])
-    torch.cuda.synchronize()
-    t_dense = (time.perf_counter() - t0) / Ks
+    t_sparse_eager = timed(lambda i: step(evp[i], evs[i]))
+    t_dense_eager = timed(lambda i: dense(evd[i]))
+
+    # ---- whole-step throughput: each path captured once in a HIP graph ----
+    g_sparse, g_dense = None, None
+    if not args.no_graph:
+        g_sparse, g_dense = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step_cap = lambda: (tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
+                                                bufs["tw_cnt"], bufs["ovf_rows"],
+                                                bufs["ovf_count"], R_max, ws),
+                                tw.tw_sparse_ffn_fwd(x, wg, wu, wdn, T, C, bufs["tw_val"],
+                                                     bufs["tw_idx"], bufs["tw_cnt"],
+                                                     bufs["ovf_rows"], bufs["ovf_count"], R_max,
+                                                     y, ws))
+            with torch.cuda.graph(g_sparse, stream=cap):
+                step_cap()
+            with torch.cuda.graph(g_dense, stream=cap):
+                tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd)
+        torch.cuda.current_stream().wait_stream(cap)
+        for _ in range(2):
+            g_sparse.replay()
+            g_dense.replay()
+        t_sparse = timed(lambda i: g_sparse.replay())
+        t_dense = timed(lambda i: g_dense.replay())
+    else:
+        t_sparse, t_dense = t_sparse_eager, t_dense_eager
+
+    # ---- sanity line: the same dense FFN on torch.matmul (hipBLASLt) ----
+    wgu = torch.cat([wg, wu], dim=0)
+    wd_row = wdn  # [N, K]: y = h @ W_d
+
+    def blas_ffn():
+        gu = x @ wgu.t()
+        h = (torch.relu(gu[:, :N]) * gu[:, N:]).to(torch.bfloat16)
+        return h @ wd_row
+
+    for _ in range(3):
+        blas_ffn()
+    t_blas = timed(lambda i: blas_ffn())
 
     def avg(evl, i):
         return sum(hev.ms(e[i], e[i + 1]) for e in evl) / len(evl) * 1e-3  # seconds
@@ -266,6 +317,13 @@ def main():
         "roofline": roof(dominant, kern[dominant]),
         "speedup_vs_dense": t_dense / t_sparse,
         "dense": {"ms_per_step": t_dense * 1e3, "value": M / t_dense},
+        "eager": {"sparse_ms_per_step": t_sparse_eager * 1e3,
+                  "dense_ms_per_step": t_dense_eager * 1e3},
+        "timing": "HIP graph replay of one step" if not args.no_graph else "eager launches",
+        "hipblaslt_dense": {"ms_per_step": t_blas * 1e3,
+                            "speedup_vs": t_blas / t_sparse,
+                            "note": "torch.matmul gate+up GEMM, ReLU*u in torch, bf16 h, "
+                                    "torch.matmul down; sanity reference only"},
         "kernels_us": {k: v * 1e6 for k, v in {**kern, **kern_dense}.items()},
         "stages": stages,
         "realized": {"density": float(nnz.sum()) / (M * N), "overflow_rows": R,
