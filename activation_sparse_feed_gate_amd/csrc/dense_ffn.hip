@@ -69,8 +69,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const int l32 = lane & 31;
     const int KT = K / kPK;
 
+    const int ncb = N / BN;
     for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-        const int rb = t % nrb, cb = t / nrb;  // neighbours in t share weight columns
+        int rb, cb;
+        if (rowlist) {
+            // few rows: all row blocks of a weight column block on one XCD
+            // (workgroup index % 8), so the weights are fetched once per XCD
+            if ((ncb & 7) == 0 && (gridDim.x & 7) == 0) {
+                const int local = t >> 3;
+                cb = (local / nrb) * 8 + (t & 7);
+                rb = local % nrb;
+            } else {
+                rb = t % nrb;
+                cb = t / nrb;
+            }
+        } else {
+            xcd_tile(t, nrb, ncb, rb, cb);
+        }
         const int m0 = rb * BM, n0 = cb * BN;
         const uint16_t *src[P::NI];
 #pragma unroll
@@ -200,7 +215,9 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
 
     for (int wi = blockIdx.x; wi < work; wi += gridDim.x) {
         const int tile = wi % tiles, sp = wi / tiles;
-        const int rb = tile % nrb, cb = tile / nrb;
+        int rb, cb;
+        if (S == 1 && !rowlist) xcd_tile(tile, nrb, ncb, rb, cb);
+        else { rb = tile % nrb; cb = tile / nrb; }
         const int m0 = rb * BM, k0 = cb * BN;
         const int kt0 = sp * (NS / S), kt1 = kt0 + NS / S;
 
@@ -311,7 +328,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
     const int K4 = K / 4;
     for (int q = blockIdx.x * 256 + threadIdx.x; q < rows * K4; q += gridDim.x * 256) {
         const int r = q / K4, col = 4 * (q % K4);
-        const int tile = (col / BN) * nrb + r / BM;
+        const int tile = (col / BN) * nrb + r / BM;  // as the split down GEMM numbers them
         const float *src = partial + (size_t)tile * (BM * BN) + (r % BM) * BN + col % BN;
         float4 sum = *reinterpret_cast<const float4 *>(src);
         for (int s2 = 1; s2 < S; ++s2) {

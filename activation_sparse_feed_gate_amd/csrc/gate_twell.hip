@@ -14,9 +14,9 @@
 //   64 x 128 outputs as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32
 //   accumulators per lane).  Operands stream from global memory straight into
 //   LDS (no register staging) through a 4-stage ring, 32 reduction elements
-//   per stage, three stages ahead of the multiplication.  Tiles are visited
-//   in groups of 8 row blocks so that the workgroups resident on an XCD at a
-//   time share operands in its L2.
+//   per stage, three stages ahead of the multiplication.  Each XCD is given a
+//   compact region of the tile grid so that its L2 serves the workgroups
+//   resident on it (xcd_tile).
 // - Epilogue without an LDS round trip: in the 32x32 MFMA result layout one
 //   accumulator register of a block holds 32 consecutive columns of two rows
 //   (lanes 0-31 and 32-63), so one 64-bit wavefront ballot of (z > 0) gives
@@ -42,20 +42,6 @@ constexpr int kStageBytes = 2 * kGateBM * kPRow;            // A and B rows of o
 constexpr int kLdsTiles = kStages * kStageBytes;            // 128 KB ring
 constexpr int kLdsBytes = kLdsTiles + 64 + 2 * kGateBM * 4; // + row flags + half counts
 
-// Tile (bm, bn) of workgroup `bid`: grouped ordering.  Consecutive
-// workgroups walk a group of up to 8 row blocks column block by column
-// block, so the ~32 workgroups resident on one XCD at a time share about 8 A
-// row blocks and 4 weight column blocks in that XCD's L2.
-__device__ __forceinline__ void tile_of(int bid, int nbm, int nbn, int &bm, int &bn) {
-    constexpr int G = 8;
-    const int group = bid / (G * nbn);
-    const int first = group * G;
-    const int gm = min(G, nbm - first);
-    const int t = bid - group * G * nbn;
-    bm = first + t % gm;
-    bn = t / gm;
-}
-
 template <int T>
 __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t, int M, int K, int N,
@@ -70,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;  // 4 x 2 waves, 64 x 128 outputs each
     int bm, bn;
-    tile_of(blockIdx.x, NBM, NBN, bm, bn);
+    xcd_tile(blockIdx.x, NBM, NBN, bm, bn);
     const int m0 = bm * kGateBM, n0 = bn * kGateBN;
 
     if (tid < 8) s_flag[tid] = 0u;

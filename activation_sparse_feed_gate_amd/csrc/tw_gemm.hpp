@@ -66,6 +66,31 @@ __device__ __forceinline__ void kloop(int kt0, int kt1, char *ring, int stage_by
     }
 }
 
+// Output tile (bm, bn) of tile index t in an nbm x nbn grid, XCD-aware.
+// Workgroups are dealt round-robin to the 8 XCDs (index % 8), and each XCD
+// has its own L2.  When the grid splits evenly, XCD x gets one of 2 x 4
+// regions of the grid, walked in groups of up to 8 row blocks column block
+// by column block, so that the ~32 workgroups resident on one XCD share a
+// few A row blocks and B column blocks in its L2.  Otherwise the whole grid
+// is walked in such groups.
+__device__ __forceinline__ void xcd_tile(int t, int nbm, int nbn, int &bm, int &bn) {
+    int r0m = 0, r0n = 0, rm = nbm, rn = nbn, local = t;
+    if ((nbm & 1) == 0 && (nbn & 3) == 0) {
+        const int x = t & 7;
+        local = t >> 3;
+        rm = nbm >> 1;
+        rn = nbn >> 2;
+        r0m = (x >> 2) * rm;
+        r0n = (x & 3) * rn;
+    }
+    constexpr int G = 8;
+    const int group = local / (G * rn);
+    const int gm = min(G, rm - group * G);
+    const int ti = local - group * G * rn;
+    bm = r0m + group * G + ti % gm;
+    bn = r0n + ti / gm;
+}
+
 // One wavefront-wide direct load: 16 operand rows x 64 bytes (1 KB) into LDS
 // at `dst` (wave-uniform).  Lane l writes physical chunk l % 4 of row l / 4,
 // so it fetches the logical chunk that the swizzle puts there.

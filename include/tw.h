@@ -7,8 +7,9 @@
  *     h_u = x W_u,   h_g = ReLU(x W_g),   h = h_u (elementwise) h_g,   y = h W_d
  *
  * with x [M, K] (M tokens, model dimension K) and an expanded hidden
- * dimension N.  Its inference path (section 2-2, "gate matmul plus TwELL
- * epilogue -> fused sparse up and down") is split over two calls:
+ * dimension N.  Its two-stage inference path (section 2-2: a gate projection
+ * whose epilogue builds the packed form, then the up and down projections
+ * fused over the active neurons) is split over two calls:
  *
  *   tw_pack_gate       gate GEMM whose epilogue applies the ReLU and packs the
  *                      active entries of every (token row, column tile) in the
@@ -37,12 +38,14 @@
  * - Device buffers must be 16-byte aligned.  When M == 0 the buffers whose
  *   size is a multiple of M may be NULL.
  * - Optional `events`: NULL, or an array of hipEvent_t (passed as void*)
- *   with one more entry than the call launches kernels.  events[0] is
- *   recorded on `stream` before the first kernel and events[i+1] after
- *   kernel i, so per-kernel durations can be read with
- *   hipEventElapsedTime.  tw_pack_gate launches 2 kernels, tw_sparse_ffn_fwd
- *   4 (sparse up+down, then the overflow rows' gate+up, down and the sum of
- *   split partial results) and tw_ffn_fwd 2.
+ *   with one more entry than the call launches kernels, for per-kernel
+ *   durations with hipEventElapsedTime.  tw_pack_gate (2 kernels) and
+ *   tw_ffn_fwd (2 kernels) record events[0] on `stream` before the first
+ *   kernel and events[i+1] after kernel i.  tw_sparse_ffn_fwd launches 4:
+ *   events[0] is recorded before any of them, events[1] after the sparse
+ *   up+down kernel, events[2..4] after the overflow rows' gate+up, down and
+ *   split-sum kernels, which run concurrently with the sparse kernel on a
+ *   side stream of the library (see tw_sparse_ffn_fwd).
  *
  * Weight layout (one layout serves every path): wg_t, wu_t and wd are all
  * [N][K] row-major bf16.  wg_t and wu_t hold W_g and W_u transposed, so the
@@ -136,6 +139,13 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t,
  *   tw_val, tw_idx, tw_cnt  the packing written by tw_pack_gate
  *   ovf_rows, ovf_count     the routing written by tw_pack_gate (device)
  *   y        [M][K]         fp32 out
+ *
+ * The overflow rows' dense path runs on a side stream the library creates
+ * for the current device on the first call with R_max > 0 (default
+ * priority), forked from `stream` and joined back into it with events: all
+ * work is still complete when `stream` reaches the end of the call, and the
+ * call can be captured into a HIP graph once that first call has been made
+ * outside capture.
  */
 tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
                             const uint16_t *wu_t, const uint16_t *wd,
