@@ -39,7 +39,13 @@ namespace {
 constexpr int kThreads = 512;                               // 8 waves, 2 per SIMD
 constexpr int kStages = 4;
 constexpr int kStageBytes = 2 * kGateBM * kPRow;            // A and B rows of one stage: 32 KB
-constexpr int kLdsTiles = kStages * kStageBytes;            // 128 KB ring
+constexpr int kRing = kStages * kStageBytes;                 // 128 KB ring
+// Epilogue staging over the ring: per wave 32 rows x 128 fp32 columns, rows
+// padded to 132 floats: 16 lanes reading the same columns of 16 different
+// rows then touch 16 different 16-byte bank groups.
+constexpr int kEpiPitch = 132;
+constexpr int kEpiWave = 32 * kEpiPitch * 4;                 // 17 KB
+constexpr int kLdsTiles = kRing > 8 * kEpiWave ? kRing : 8 * kEpiWave;
 constexpr int kLdsBytes = kLdsTiles + 64 + 2 * kGateBM * 4; // + row flags + half counts
 
 template <int T>
@@ -86,108 +92,99 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
 
-    auto compute = [&](const char *st) {
+    u32x4 fa[2][2], fb[2][4];  // [register set][block]
+    auto load = [&](const char *st, int s, int buf) {
         const char *bt = st + kGateBM * kPRow;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            u32x4 fa[2], fb[4];
+        for (int a = 0; a < 2; ++a) fa[buf][a] = frag(st, wm * 64 + a * 32, s, lane);
 #pragma unroll
-            for (int a = 0; a < 2; ++a) fa[a] = frag(st, wm * 64 + a * 32, s, lane);
-#pragma unroll
-            for (int b = 0; b < 4; ++b) fb[b] = frag(bt, wn * 128 + b * 32, s, lane);
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
-        }
+        for (int b = 0; b < 4; ++b) fb[buf][b] = frag(bt, wn * 128 + b * 32, s, lane);
     };
-    kloop<kStages, 4>(0, K / kPK, smem, kStageBytes, issue, compute);
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
+    };
+    kloop_pipelined<kStages, 4>(0, K / kPK, smem, kStageBytes, issue, load, mma);
     __syncthreads();
 
     // ---------------- epilogue: ReLU + TwELL pack + row overflow bits ----
-    const int l32 = lane & 31;
-    const int half = lane >> 5;
-    const uint32_t below = (1u << l32) - 1u;
+    // The ring is free after the main loop (the barrier above).  Each wave
+    // stages 32 of its 64 rows at a time in LDS.  Lane l then owns half a
+    // row: row l % 32, columns 64 (l / 32) ... +63 of this wave's 128.  It
+    // builds the half-row's activity mask (z > 0) with vector compares, the
+    // two halves' popcounts give the row count and this half's offset, and
+    // the lane stores its entries in ascending column order.
     const int ncol0 = n0 + wn * 128;  // first column of this wave
     const bool live = ncol0 < N;      // false only in a half-empty last column block
     const int NT = N / T;
     const int t = ncol0 / T;
     const int wrow0 = m0 + wm * 64;   // first of the 64 rows this wave holds
+    const int l32 = lane & 31, hc = lane >> 5;
+    float *st = reinterpret_cast<float *>(smem + wave * kEpiWave);
+    const float *rowp = st + l32 * kEpiPitch + hc * 64;
 
-    if (T == 256) {
-        // pass 1: this wave's half-tile count of every row it holds
-#pragma unroll
-        for (int a = 0; a < 2; ++a) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                int tot = 0;
-#pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const uint64_t bal = __ballot(acc[a][b][i] > 0.0f);
-                    tot += __popc(half ? (uint32_t)(bal >> 32) : (uint32_t)bal);
-                }
-                const int rloc = wm * 64 + a * 32 + mfma32_row(i, lane);
-                if (l32 == 0) s_half[wn * kGateBM + rloc] = tot;
-            }
-        }
-        __syncthreads();
-    }
-
-    // lane r collects the count of wave row r; bit r of `over` marks an
-    // overflowing row (wave-uniform)
-    int cnt_lane = 0;
-    uint64_t over = 0;
+    int cnt_lane = 0;   // lane r: count of wave row r (this wave's columns or the whole tile)
+    uint64_t over = 0;  // bit r: wave row r overflows (wave-uniform)
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int rw = a * 32 + mfma32_row(i, lane);  // wave row of this lane
-            const int m = wrow0 + rw;
-            uint32_t mk[4];
-            int pre[4];
-            int tot = 0;
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const uint64_t bal = __ballot(acc[a][b][i] > 0.0f);
-                mk[b] = half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-                pre[b] = tot;
-                tot += __popc(mk[b]);
-            }
-            int off = 0, total = tot;
-            if (T == 256) {
-                const int other = s_half[(wn ^ 1) * kGateBM + wm * 64 + rw];
-                off = wn ? other : 0;
-                total = tot + other;
-            }
-            if (m < M && live) {
-                const size_t tb = ((size_t)m * NT + t) * C;
+            for (int i = 0; i < 16; ++i)
+                st[mfma32_row(i, lane) * kEpiPitch + b * 32 + l32] = acc[a][b][i];
+        if (zdbg && live) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float v = acc[a][b][i];
-                    if (v > 0.0f) {
-                        const int slot = off + pre[b] + __popc(mk[b] & below);
-                        if (slot < C) {
-                            tw_idx[tb + slot] = ncol0 + b * 32 + l32;
-                            tw_val[tb + slot] = v;
-                        }
-                    }
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int m = wrow0 + a * 32 + mfma32_row(i, lane);
+                    if (m < M) zdbg[(size_t)m * N + ncol0 + b * 32 + l32] = acc[a][b][i];
                 }
-                if (zdbg) {
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        zdbg[(size_t)m * N + ncol0 + b * 32 + l32] = acc[a][b][i];
-                }
-            }
-            // rows of lanes 0 and 32 (the two rows of this register)
-            const int rA = a * 32 + mfma32_row(i, 0), rB = rA + 4;
-            const int tA = __builtin_amdgcn_readlane(total, 0);
-            const int tB = __builtin_amdgcn_readlane(total, 32);
-            cnt_lane = lane == rA ? tA : cnt_lane;
-            cnt_lane = lane == rB ? tB : cnt_lane;
-            // rows past M repeat row M-1 and must not be routed
-            if (tA > C && wrow0 + rA < M) over |= 1ull << rA;
-            if (tB > C && wrow0 + rB < M) over |= 1ull << rB;
         }
+        uint32_t mk[2] = {0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const float4 v = *reinterpret_cast<const float4 *>(rowp + 4 * q);
+            const uint32_t bits = (v.x > 0.0f ? 1u : 0u) | (v.y > 0.0f ? 2u : 0u) |
+                                  (v.z > 0.0f ? 4u : 0u) | (v.w > 0.0f ? 8u : 0u);
+            mk[q >> 3] |= bits << (4 * (q & 7));
+        }
+        const int cnt = __popc(mk[0]) + __popc(mk[1]);
+        const int pcnt = __shfl_xor(cnt, 32);           // the other half of the row
+        int total = cnt + pcnt;                          // this wave's 128 columns
+        int off = hc ? pcnt : 0;                         // entries before this half
+        const int rw = a * 32 + l32;                     // wave row of this lane
+        const int m = wrow0 + rw;
+        if (T == 256) {
+            // the two waves of a wave row hold the two halves of each tile
+            if (hc == 0) s_half[wn * kGateBM + wm * 64 + rw] = total;
+            __syncthreads();
+            const int other = s_half[(wn ^ 1) * kGateBM + wm * 64 + rw];
+            if (wn) off += other;
+            total += other;
+        }
+        if (live && m < M && off < C) {
+            const size_t tb = ((size_t)m * NT + t) * C;
+            uint64_t bits = (uint64_t)mk[0] | ((uint64_t)mk[1] << 32);
+            int slot = off;
+            while (bits && slot < C) {
+                const int c = __builtin_ctzll(bits);
+                bits &= bits - 1;
+                tw_idx[tb + slot] = ncol0 + hc * 64 + c;
+                tw_val[tb + slot] = rowp[c];
+                ++slot;
+            }
+        }
+        // every lane joins the shuffle: a permute reading an inactive lane
+        // yields 0, so it must not sit under the select below
+        const int tsh = __shfl(total, lane & 31);
+        cnt_lane = (lane >> 5) == a ? tsh : cnt_lane;
+        // rows past M repeat row M-1 and must not be routed
+        const uint64_t ov = __ballot(hc == 0 && total > C && m < M);
+        over |= (ov & 0xffffffffull) << (32 * a);
+        if (T == 256) __syncthreads();  // s_half is rewritten for the next 32 rows
     }
     const bool owner = T == 128 || wn == 0;  // the wave that stores this tile's counts
     if (owner && live) {
