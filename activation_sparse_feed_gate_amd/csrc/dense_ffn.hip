@@ -32,10 +32,10 @@
 namespace tw {
 namespace {
 
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
+// Rows to process: the device-side count (capped) or R_cap.  Read into a
+// scalar register: buffer descriptors built from it must be wave-uniform.
 __device__ __forceinline__ int rows_of(const int32_t *count, int R_cap) {
-    return count ? min(*count, R_cap) : R_cap;
+    return __builtin_amdgcn_readfirstlane(count ? min(*count, R_cap) : R_cap);
 }
 
 // ------------------------------ gate + up ---------------------------------
@@ -49,14 +49,14 @@ struct GU {
     static constexpr int STAGE = SR * kPRow;
     static constexpr int LDS = S * STAGE;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
-    static_assert(SR % (16 * NW) == 0 && BM % 16 == 0 && BN % 16 == 0, "stage rows");
+    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "each load row group in one operand");
 };
 
 template <int BM, int BN, int WM, int WN, int S>
 __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t,
     const uint16_t *__restrict__ wu_t, int K, int N, const int32_t *__restrict__ rowlist,
-    const int32_t *__restrict__ count, int R_cap, uint16_t *__restrict__ h) {
+    const int32_t *__restrict__ count, int R_cap, int xrows, uint16_t *__restrict__ h) {
     using P = GU<BM, BN, WM, WN, S>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -87,24 +87,41 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
             xcd_tile(t, nrb, ncb, rb, cb);
         }
         const int m0 = rb * BM, n0 = cb * BN;
-        const uint16_t *src[P::NI];
+        // x rows come through the row list (any of the xrows rows) or are
+        // the tile's own; the weight rows are the column block's
+        const uint16_t *xb = rowlist ? x : x + (size_t)m0 * K;
+        const uint64_t xbytes = (uint64_t)(rowlist ? xrows : rows - m0) * K * 2;
+        const uint16_t *gb = wg_t + (size_t)n0 * K, *ub = wu_t + (size_t)n0 * K;
+        // Load j of a wave fetches stage rows [16 (j NW + wave), +16): since
+        // BM and BN are multiples of 16 NW, j alone decides the operand.
+        uint32_t voff[P::NI];
 #pragma unroll
         for (int j = 0; j < P::NI; ++j) {
-            const int sr = (wave * P::NI + j) * 16 + (lane >> 2);
-            if (sr < BM) {
+            const int row0 = (j * P::NW + wave) * 16;
+            const int sr = row0 + (lane >> 2);
+            uint32_t row_off;
+            if (j * P::NW * 16 < BM) {
                 const int r = min(m0 + sr, rows - 1);
-                src[j] = x + (size_t)(rowlist ? rowlist[r] : r) * K;
-            } else if (sr < BM + BN) {
-                src[j] = wg_t + (size_t)(n0 + sr - BM) * K;
+                row_off = rowlist ? (uint32_t)rowlist[r] * K * 2 : (uint32_t)(r - m0) * K * 2;
+            } else if (j * P::NW * 16 < BM + BN) {
+                row_off = (uint32_t)(sr - BM) * K * 2;
             } else {
-                src[j] = wu_t + (size_t)(n0 + sr - BM - BN) * K;
+                row_off = (uint32_t)(sr - BM - BN) * K * 2;
             }
+            voff[j] = rows16_voff(row_off, lane, row0);
         }
+        const rsrc_t rx = make_rsrc(xb, xbytes);
+        const rsrc_t rg = make_rsrc(gb, (uint64_t)BN * K * 2);
+        const rsrc_t ru = make_rsrc(ub, (uint64_t)BN * K * 2);
         auto issue = [&](int kt, char *st) {
+            const uint32_t soff = kt * kPK * 2;
 #pragma unroll
             for (int j = 0; j < P::NI; ++j) {
-                const int row0 = (wave * P::NI + j) * 16;
-                dma_rows16(src[j], kt * kPK, lane, row0, st + row0 * kPRow);
+                const int row0 = (j * P::NW + wave) * 16;
+                char *dst = st + row0 * kPRow;
+                if (j * P::NW * 16 < BM) dma16(rx, voff[j], soff, dst);
+                else if (j * P::NW * 16 < BM + BN) dma16(rg, voff[j], soff, dst);
+                else dma16(ru, voff[j], soff, dst);
             }
         };
         f32x16 ag[P::FA][P::FB], au[P::FA][P::FB];
@@ -115,27 +132,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                 ag[a][b] = f32x16{};
                 au[a][b] = f32x16{};
             }
-        auto compute = [&](const char *st) {
+        u32x4 fa[2][P::FA], fg[2][P::FB], fu[2][P::FB];  // [register set][block]
+        auto load = [&](const char *st, int s, int buf) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 fa[P::FA], fg[P::FB], fu[P::FB];
+            for (int a = 0; a < P::FA; ++a) fa[buf][a] = frag(st, wm * P::TM + a * 32, s, lane);
 #pragma unroll
-                for (int a = 0; a < P::FA; ++a) fa[a] = frag(st, wm * P::TM + a * 32, s, lane);
-#pragma unroll
-                for (int b = 0; b < P::FB; ++b) {
-                    fg[b] = frag(st, BM + wn * P::TN + b * 32, s, lane);
-                    fu[b] = frag(st, BM + BN + wn * P::TN + b * 32, s, lane);
-                }
-#pragma unroll
-                for (int a = 0; a < P::FA; ++a)
-#pragma unroll
-                    for (int b = 0; b < P::FB; ++b) {
-                        ag[a][b] = mfma32(fa[a], fg[b], ag[a][b]);
-                        au[a][b] = mfma32(fa[a], fu[b], au[a][b]);
-                    }
+            for (int b = 0; b < P::FB; ++b) {
+                fg[buf][b] = frag(st, BM + wn * P::TN + b * 32, s, lane);
+                fu[buf][b] = frag(st, BM + BN + wn * P::TN + b * 32, s, lane);
             }
         };
-        kloop<S, P::NI>(0, KT, smem, P::STAGE, issue, compute);
+        auto mma = [&](int buf) {
+#pragma unroll
+            for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b) {
+                    ag[a][b] = mfma32(fa[buf][a], fg[buf][b], ag[a][b]);
+                    au[a][b] = mfma32(fa[buf][a], fu[buf][b], au[a][b]);
+                }
+        };
+        kloop_pipelined<S, P::NI>(0, KT, smem, P::STAGE, issue, load, mma);
 #pragma unroll
         for (int a = 0; a < P::FA; ++a)
 #pragma unroll
@@ -221,28 +237,34 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
         const int m0 = rb * BM, k0 = cb * BN;
         const int kt0 = sp * (NS / S), kt1 = kt0 + NS / S;
 
-        const uint16_t *asrc[P::NIA];
+        const rsrc_t rh = make_rsrc(h + (size_t)m0 * N, (uint64_t)(rows - m0) * N * 2);
+        const rsrc_t rd = make_rsrc(wd + k0, ((uint64_t)N * K - k0) * 2);
+        uint32_t aoff[P::NIA], boff[P::NIB];
 #pragma unroll
         for (int j = 0; j < P::NIA; ++j) {
-            const int sr = (wave * P::NIA + j) * 16 + (lane >> 2);
-            asrc[j] = h + (size_t)min(m0 + sr, rows - 1) * N;
+            const int row0 = (wave * P::NIA + j) * 16;
+            const int r = min(m0 + row0 + (lane >> 2), rows - 1);
+            aoff[j] = rows16_voff((uint32_t)(r - m0) * N * 2, lane, row0);
         }
-        // B: this lane's row within a 1 KB load and its swizzled chunk
+        // B: this lane's W_d row within a 1 KB load and its swizzled chunk
         const int brl = lane >> 4;  // 0..3
+#pragma unroll
+        for (int j = 0; j < P::NIB; ++j) {
+            const int row = (wave * P::NIB + j) * P::BR_PER + brl;
+            boff[j] = (uint32_t)row * K * 2 + (uint32_t)(((lane & 15) ^ bsw(row)) << 4);
+        }
         auto issue = [&](int kt, char *st) {
+            const uint32_t soff_a = kt * kPK * 2;
+            const uint32_t soff_b = (uint32_t)kt * kPK * K * 2;
 #pragma unroll
             for (int j = 0; j < P::NIA; ++j) {
                 const int row0 = (wave * P::NIA + j) * 16;
-                dma_rows16(asrc[j], kt * kPK, lane, row0, st + row0 * kPRow);
+                dma16(rh, aoff[j], soff_a, st + row0 * kPRow);
             }
 #pragma unroll
             for (int j = 0; j < P::NIB; ++j) {
-                const int row = (wave * P::NIB + j) * P::BR_PER + brl;
-                const int c = (lane & 15) ^ bsw(row);
-                const uint16_t *src = wd + (size_t)(kt * kPK + row) * K + k0 + c * 8;
-                __builtin_amdgcn_global_load_lds(
-                    static_cast<const void *>(src),
-                    (lds_void *)(st + P::A_BYTES + (row - brl) * P::BROW), 16, 0, 0);
+                const int row = (wave * P::NIB + j) * P::BR_PER;
+                dma16(rd, boff[j], soff_b, st + P::A_BYTES + row * P::BROW);
             }
         };
         f32x16 acc[P::FA][P::FB];
@@ -250,38 +272,36 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
         for (int a = 0; a < P::FA; ++a)
 #pragma unroll
             for (int b = 0; b < P::FB; ++b) acc[a][b] = f32x16{};
-        auto compute = [&](const char *st) {
+        u32x4 fa[2][P::FA], fb[2][P::FB];  // [register set][block]
+        auto load = [&](const char *st, int s, int buf) {
             const char *bt = st + P::A_BYTES;
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 fa[P::FA], fb[P::FB];
+            for (int a = 0; a < P::FA; ++a) fa[buf][a] = frag(st, wm * P::TM + a * 32, s, lane);
 #pragma unroll
-                for (int a = 0; a < P::FA; ++a) fa[a] = frag(st, wm * P::TM + a * 32, s, lane);
+            for (int b = 0; b < P::FB; ++b) {
+                // lane (g4, i16) supplies row 16 s + 8 (g4 / 2) + 4 hh + i16 / 4,
+                // columns c0 + 4 (i16 % 4) ..+3 and receives column c0 + i16
+                const int c0 = wn * P::TN + b * 32 + 16 * (g4 & 1) + 4 * (i16 & 3);
+                i16x4 v[2];
 #pragma unroll
-                for (int b = 0; b < P::FB; ++b) {
-                    // lane (g4, i16) supplies row 16 s + 8 (g4 / 2) + 4 hh + i16 / 4,
-                    // columns c0 + 4 (i16 % 4) ..+3 and receives column c0 + i16
-                    const int c0 = wn * P::TN + b * 32 + 16 * (g4 & 1) + 4 * (i16 & 3);
-                    i16x4 v[2];
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int row = 16 * s + 8 * (g4 >> 1) + 4 * hh + (i16 >> 2);
-                        const uint32_t off = row * P::BROW + (((c0 >> 3) ^ bsw(row)) << 4) +
-                                             (c0 & 7) * 2;
-                        v[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (__attribute__((address_space(3))) i16x4 *)(bt + off));
-                    }
-                    const u32x2 lo = __builtin_bit_cast(u32x2, v[0]);
-                    const u32x2 hi = __builtin_bit_cast(u32x2, v[1]);
-                    fb[b] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                for (int hh = 0; hh < 2; ++hh) {
+                    const int row = 16 * s + 8 * (g4 >> 1) + 4 * hh + (i16 >> 2);
+                    const uint32_t off = row * P::BROW + (((c0 >> 3) ^ bsw(row)) << 4) +
+                                         (c0 & 7) * 2;
+                    v[hh] = lds_tr16((const lds_i16x4 *)(bt + off));
                 }
-#pragma unroll
-                for (int a = 0; a < P::FA; ++a)
-#pragma unroll
-                    for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[a], fb[b], acc[a][b]);
+                const u32x2 lo = __builtin_bit_cast(u32x2, v[0]);
+                const u32x2 hi = __builtin_bit_cast(u32x2, v[1]);
+                fb[buf][b] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
         };
-        kloop<STG, P::NI>(kt0, kt1, smem, P::STAGE, issue, compute);
+        auto mma = [&](int buf) {
+#pragma unroll
+            for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
+        };
+        kloop_pipelined<STG, P::NI>(kt0, kt1, smem, P::STAGE, issue, load, mma);
 
         if (S == 1) {
 #pragma unroll
@@ -363,8 +383,8 @@ constexpr int kSplitGrid = 256;  // work items of the split down GEMM
 
 size_t split_partial_bytes() { return (size_t)kSplitGrid * 128 * 128 * sizeof(float); }
 
-hipError_t launch_gateup(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t, int K,
-                         int N, const int32_t *rowlist, const int32_t *count, int R_cap,
+hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const uint16_t *wu_t,
+                         int K, int N, const int32_t *rowlist, const int32_t *count, int R_cap,
                          uint16_t *h, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
     if (rowlist) {
@@ -374,14 +394,14 @@ hipError_t launch_gateup(const uint16_t *x, const uint16_t *wg_t, const uint16_t
         const int tiles = (R_cap + 63) / 64 * (N / 128);
         const int grid = tiles < 1024 ? tiles : 1024;
         hipLaunchKernelGGL((gateup_kernel<64, 128, 1, 4, 6>), dim3(grid), dim3(GuRows::NTH),
-                           GuRows::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, h);
+                           GuRows::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h);
     } else {
         static bool attr = false;
         hipError_t e = set_lds(&gateup_kernel<256, 128, 4, 2, 4>, GuDense::LDS, attr);
         if (e != hipSuccess) return e;
         const int grid = (R_cap + 255) / 256 * (N / 128);
         hipLaunchKernelGGL((gateup_kernel<256, 128, 4, 2, 4>), dim3(grid), dim3(GuDense::NTH),
-                           GuDense::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, h);
+                           GuDense::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h);
     }
     return hipGetLastError();
 }

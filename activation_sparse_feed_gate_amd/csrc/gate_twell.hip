@@ -70,19 +70,23 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     // Each wave streams rows [32 wave, 32 wave + 32) of both operands: two
     // 16-row direct loads per operand and stage (rows past M or N repeat the
     // last row; their results are never stored).
-    const uint16_t *asrc[2], *bsrc[2];
+    const rsrc_t ra = make_rsrc(x + (size_t)m0 * K, (uint64_t)(M - m0) * K * 2);
+    const rsrc_t rb = make_rsrc(wg_t + (size_t)n0 * K, (uint64_t)(N - n0) * K * 2);
+    uint32_t aoff[2], boff[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int r = wave * 32 + j * 16 + (lane >> 2);
-        asrc[j] = x + (size_t)min(m0 + r, M - 1) * K;
-        bsrc[j] = wg_t + (size_t)min(n0 + r, N - 1) * K;
+        const int row0 = wave * 32 + j * 16;
+        const int r = row0 + (lane >> 2);
+        aoff[j] = rows16_voff((uint32_t)(min(m0 + r, M - 1) - m0) * K * 2, lane, row0);
+        boff[j] = rows16_voff((uint32_t)(min(n0 + r, N - 1) - n0) * K * 2, lane, row0);
     }
     auto issue = [&](int kt, char *st) {
+        const uint32_t soff = kt * kPK * 2;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row0 = wave * 32 + j * 16;
-            dma_rows16(asrc[j], kt * kPK, lane, row0, st + row0 * kPRow);
-            dma_rows16(bsrc[j], kt * kPK, lane, row0, st + (kGateBM + row0) * kPRow);
+            dma16(ra, aoff[j], soff, st + row0 * kPRow);
+            dma16(rb, boff[j], soff, st + (kGateBM + row0) * kPRow);
         }
     };
 
@@ -106,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
 #pragma unroll
             for (int b = 0; b < 4; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
     };
+    settle_scalars(tw_val, tw_idx, tw_cnt, oflag, zdbg);
     kloop_pipelined<kStages, 4>(0, K / kPK, smem, kStageBytes, issue, load, mma);
     __syncthreads();
 

@@ -36,6 +36,8 @@ tw_status check_shape(int M, int K, int N, int T, int C, int R_max) {
     if (K % 128) return fail(TW_EUNSUPPORTED, "K=%d: must be a multiple of 128", K);
     if (K > 4096) return fail(TW_EUNSUPPORTED, "K=%d: at most 4096", K);
     if (R_max < 0 || R_max > M) return fail(TW_EINVAL, "R_max=%d outside [0, M=%d]", R_max, M);
+    if ((int64_t)M * K >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "M*K=%lld: x must stay under 4 GiB", (long long)M * K);
     return TW_OK;
 }
 
@@ -212,7 +214,7 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     TW_TRY(record(events, 0, s));
     TW_TRY(launched(hipEventRecord(sd->fork, s), "fork record"));
     TW_TRY(launched(hipStreamWaitEvent(f, sd->fork, 0), "fork wait"));
-    TW_TRY(launched(tw::launch_gateup(x, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, f),
+    TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, f),
                     "fallback gate+up launch"));
     TW_TRY(record(events, 2, f));
     TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, partial, f),
@@ -236,6 +238,8 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu
     if (M < 0 || K <= 0 || N <= 0) return fail(TW_EINVAL, "M=%d K=%d N=%d: need M >= 0, K, N > 0", M, K, N);
     if (N % 128) return fail(TW_EUNSUPPORTED, "N=%d: must be a multiple of 128", N);
     if (K % 128) return fail(TW_EUNSUPPORTED, "K=%d: must be a multiple of 128", K);
+    if ((int64_t)N * K >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "N*K=%lld: weights must stay under 4 GiB", (long long)N * K);
     TW_NEED_M(x);
     TW_NEED(wg_t);
     TW_NEED(wu_t);
@@ -248,7 +252,7 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint16_t *h = static_cast<uint16_t *>(ws);
     TW_TRY(record(events, 0, s));
-    TW_TRY(launched(tw::launch_gateup(x, wg_t, wu_t, K, N, nullptr, nullptr, M, h, s),
+    TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, nullptr, nullptr, M, h, s),
                     "dense gate+up launch"));
     TW_TRY(record(events, 1, s));
     TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, nullptr, s),

@@ -68,6 +68,22 @@ __device__ __forceinline__ void kloop(int kt0, int kt1, char *ring, int stage_by
     }
 }
 
+// Scalar values the epilogue needs (kernel arguments) must be in registers
+// before the k-loop.  Scalar loads and LDS reads share one completion
+// counter and scalar loads may return out of order, so a scalar load still
+// in flight inside the loop forces every LDS wait there to drain all reads
+// (instead of only the older sub-step's), exposing the LDS latency before
+// each batch of matrix instructions.  An empty asm that consumes the values
+// makes their loads complete here.
+template <typename P>
+__device__ __forceinline__ void settle_scalar(P p) {
+    asm volatile("" ::"s"(p));
+}
+template <typename... P>
+__device__ __forceinline__ void settle_scalars(P... p) {
+    (settle_scalar(p), ...);
+}
+
 // Output tile (bm, bn) of tile index t in an nbm x nbn grid, XCD-aware.
 // Workgroups are dealt round-robin to the 8 XCDs (index % 8), and each XCD
 // has its own L2.  When the grid splits evenly, XCD x gets one of 2 x 4
@@ -103,6 +119,10 @@ __device__ __forceinline__ void xcd_tile(int t, int nbm, int nbn, int &bm, int &
 // second half multiplies.  The barrier of iteration i certifies that every
 // wave has finished reading stage i, so stage i + S - 1 may refill the slot
 // of stage i - 1 at the start of iteration i.
+// The steady state (a stage still to issue) has no branches, so the
+// compiler can wait for exactly the fragments each matrix instruction
+// needs; a branch around the next stage's reads would make it wait for
+// those too.  The last S - 1 stages drain in a second loop.
 template <int S, int NI, typename Issue, typename Load, typename Mma>
 __device__ __forceinline__ void kloop_pipelined(int kt0, int kt1, char *ring, int stage_bytes,
                                                 Issue issue, Load load, Mma mma) {
@@ -113,14 +133,28 @@ __device__ __forceinline__ void kloop_pipelined(int kt0, int kt1, char *ring, in
     wait_later<NI, S>(min(S - 2, n - 1));
     __builtin_amdgcn_s_barrier();
     load(ring, 0, 0);
-    for (int i = 0; i < n; ++i) {
-        char *cur = ring + (i % S) * stage_bytes;
-        load(cur, 1, 1);
-        if (i + S - 1 < n) issue(kt0 + i + S - 1, ring + ((i + S - 1) % S) * stage_bytes);
+    int i = 0;
+    // sched_barrier(0) keeps the instruction scheduler from moving the
+    // fragment reads behind the matrix instructions (which would fold the
+    // two register sets into one and serialise reads and multiplies)
+    for (; i + S - 1 < n; ++i) {
+        load(ring + (i % S) * stage_bytes, 1, 1);
+        issue(kt0 + i + S - 1, ring + ((i + S - 1) % S) * stage_bytes);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(S - 2) * NI>();  // stage i + 1 landed
+        __builtin_amdgcn_s_barrier();
+        load(ring + ((i + 1) % S) * stage_bytes, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (; i < n; ++i) {
+        load(ring + (i % S) * stage_bytes, 1, 1);
         mma(0);
         if (i + 1 < n) {
-            // stage i+1 landed (only later stages may still be in flight)
-            wait_later<NI, S>(min(S - 2, n - 2 - i));
+            wait_later<NI, S>(n - 2 - i);
             __builtin_amdgcn_s_barrier();
             load(ring + ((i + 1) % S) * stage_bytes, 0, 0);
         }
@@ -128,17 +162,51 @@ __device__ __forceinline__ void kloop_pipelined(int kt0, int kt1, char *ring, in
     }
 }
 
-// One wavefront-wide direct load: 16 operand rows x 64 bytes (1 KB) into LDS
-// at `dst` (wave-uniform).  Lane l writes physical chunk l % 4 of row l / 4,
-// so it fetches the logical chunk that the swizzle puts there.
-// `src_row` points at the lane's operand row, `k` is the stage's first
-// reduction element.
-__device__ __forceinline__ void dma_rows16(const uint16_t *src_row, int k, int lane, int row0,
-                                           char *dst) {
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer descriptor over `bytes` bytes at `base` (capped at 4 GiB - 1;
+// a lane whose offset falls outside reads zeros).  Word 3 selects data
+// format 32, which untyped buffer accesses need to be nonzero on gfx9-family
+// parts.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint64_t bytes) {
+    const uint32_t n = bytes < 0xffffffffull ? (uint32_t)bytes : 0xffffffffu;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n,
+                                             0x00020000);
+}
+
+// One wavefront-wide direct load: lane l copies the 16 bytes at byte
+// voff + soff of the buffer to LDS dst + 16 l (dst wave-uniform, soff
+// scalar).  The buffer form is used rather than the global one: the
+// compiler books a global load-to-LDS as an access to both memories, and
+// while one is in flight it turns every LDS wait into a wait for all
+// outstanding LDS reads, so the fragments of the next sub-step could not be
+// in flight across the current sub-step's matrix instructions.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, char *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, voff, soff, 0, 0);
+}
+
+// Lane offset for a 16-row x 64-byte stage load (1 KB): lane l writes
+// physical chunk l % 4 of stage row row0 + l / 4, so it fetches the logical
+// chunk that the swizzle puts there.  `row_off` is the byte offset of the
+// lane's operand row in the buffer; the stage's reduction offset goes into
+// the scalar offset of dma16.
+__device__ __forceinline__ uint32_t rows16_voff(uint32_t row_off, int lane, int row0) {
     const int r = row0 + (lane >> 2);
-    const int kc = (lane & 3) ^ swz(r);
-    __builtin_amdgcn_global_load_lds(static_cast<const void *>(src_row + k + kc * 8),
-                                     (lds_void *)(dst), 16, 0, 0);
+    return row_off + (uint32_t)(((lane & 3) ^ swz(r)) << 4);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// ds_read_b64_tr_b16: in each 16-lane group, lane i receives element i % 4
+// of the 8-byte rows addressed by lanes 4 e + i / 4 (e = 0..3), a 4 x 4
+// transpose of 16-bit elements.  The stages of the ring are ordered by
+// explicit vector-memory waits and barriers.  Reads that carry no alias
+// information are additionally made to wait for every direct load in flight
+// (all later stages too); inlining this wrapper through a restrict-qualified
+// pointer gives the read alias information like ordinary LDS loads have.
+__device__ __forceinline__ i16x4 lds_tr16(const lds_i16x4 *__restrict__ p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_i16x4 *>(p));
 }
 
 // Fragment of v_mfma_f32_32x32x16_bf16 for sub-step s (0 or 1) of a stage:

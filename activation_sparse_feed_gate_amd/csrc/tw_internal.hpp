@@ -29,8 +29,9 @@ hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const u
 
 // h[r][n] = bf16(ReLU(x_r . wg_t[n]) * (x_r . wu_t[n])) for r < rows, where
 // x_r is x[rowlist[r]] (rowlist != nullptr, rows = min(*count, R_cap)) or
-// x[r] (rowlist == nullptr, rows = R_cap).
-hipError_t launch_gateup(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t,
+// x[r] (rowlist == nullptr, rows = R_cap).  x has M rows; with a row list
+// M * K * 2 must stay below 4 GiB (32-bit buffer offsets).
+hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const uint16_t *wu_t,
                          int K, int N, const int32_t *rowlist, const int32_t *count,
                          int R_cap, uint16_t *h, hipStream_t s);
 

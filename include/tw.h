@@ -26,9 +26,11 @@
  * ---------------------------------------
  * - bf16 values travel as raw uint16_t bit patterns.
  * - Every pointer argument except `stream` is a device pointer to memory the
- *   caller owns; the library allocates and frees nothing and keeps no state
- *   between calls, so calls on different streams may run concurrently as
- *   long as their output and workspace buffers are distinct.
+ *   caller owns.  The library allocates no device memory and keeps no data
+ *   between calls (its only state is the per-device side stream and two
+ *   events of tw_sparse_ffn_fwd), so calls on different streams may run
+ *   concurrently as long as their output and workspace buffers are
+ *   distinct.
  * - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *   void*; NULL is the default stream).  Nothing synchronises the host.
  * - Argument and shape errors are detected on the host before any work is
@@ -54,7 +56,9 @@
  *
  * Supported shapes: M >= 0, K a positive multiple of 128 and at most 4096,
  * N a positive multiple of T, T in {128, 256}, N / T <= 256, 1 <= C <= T,
- * 0 <= R_max <= M.
+ * 0 <= R_max <= M, and M * K < 2^31 (x under 4 GiB: the dense backup
+ * gathers its rows with 32-bit buffer offsets).  tw_ffn_fwd has its own
+ * limits, stated at its declaration.
  */
 #ifndef TW_H
 #define TW_H
@@ -161,6 +165,8 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
  * projections in one MFMA GEMM whose epilogue forms h = ReLU(g) * u rounded
  * to bf16, then the down projection into fp32 y [M][K].
  * The workspace holds h [M][N] bf16: ws_bytes >= tw_ffn_workspace_bytes.
+ * Shapes: M >= 0, K and N positive multiples of 128, N * K < 2^31 (each
+ * weight matrix under 4 GiB: 32-bit buffer offsets).
  */
 size_t tw_ffn_workspace_bytes(int M, int K, int N);
 tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
