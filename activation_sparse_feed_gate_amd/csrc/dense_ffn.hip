@@ -334,30 +334,39 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
 }
 
 // y[row_r] = sum over splits s = 0, 1, ... of the partial tiles (fixed
-// order), when the down GEMM split its reduction.
+// order), when the down GEMM split its reduction.  Each thread owns four
+// consecutive outputs; the loads of all its partials are issued before the
+// first add, so the kernel pays one memory latency instead of S.
 template <int BM, int BN>
 __global__ __launch_bounds__(256) void split_reduce_kernel(
     const float *__restrict__ partial, const int32_t *__restrict__ rowlist,
     const int32_t *__restrict__ count, int R_cap, int K, int N, int grid_down,
     float *__restrict__ y) {
+    constexpr int kMaxSplit = 16;
     const int rows = rows_of(count, R_cap);
     const int nrb = (rows + BM - 1) / BM;
     const int tiles = nrb * (K / BN);
     const int S = split_count(tiles, grid_down, N / kPK);
     if (S == 1) return;
     const int K4 = K / 4;
+    const size_t split_stride = (size_t)tiles * (BM * BN);
     for (int q = blockIdx.x * 256 + threadIdx.x; q < rows * K4; q += gridDim.x * 256) {
         const int r = q / K4, col = 4 * (q % K4);
         const int tile = (col / BN) * nrb + r / BM;  // as the split down GEMM numbers them
         const float *src = partial + (size_t)tile * (BM * BN) + (r % BM) * BN + col % BN;
-        float4 sum = *reinterpret_cast<const float4 *>(src);
-        for (int s2 = 1; s2 < S; ++s2) {
-            const float4 v = *reinterpret_cast<const float4 *>(src + (size_t)s2 * tiles * (BM * BN));
-            sum.x += v.x;
-            sum.y += v.y;
-            sum.z += v.z;
-            sum.w += v.w;
-        }
+        float4 v[kMaxSplit];
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxSplit; ++s2)
+            if (s2 < S) v[s2] = *reinterpret_cast<const float4 *>(src + s2 * split_stride);
+        float4 sum = v[0];
+#pragma unroll
+        for (int s2 = 1; s2 < kMaxSplit; ++s2)
+            if (s2 < S) {
+                sum.x += v[s2].x;
+                sum.y += v[s2].y;
+                sum.z += v[s2].z;
+                sum.w += v[s2].w;
+            }
         *reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col) = sum;
     }
 }
@@ -391,8 +400,10 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
         static bool attr = false;
         hipError_t e = set_lds(&gateup_kernel<64, 128, 1, 4, 6>, GuRows::LDS, attr);
         if (e != hipSuccess) return e;
+        // one workgroup per CU at most: the grid is sized for the capacity
+        // and most of it would find no rows
         const int tiles = (R_cap + 63) / 64 * (N / 128);
-        const int grid = tiles < 1024 ? tiles : 1024;
+        const int grid = tiles < 256 ? tiles : 256;
         hipLaunchKernelGGL((gateup_kernel<64, 128, 1, 4, 6>), dim3(grid), dim3(GuRows::NTH),
                            GuRows::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h);
     } else {

@@ -205,21 +205,41 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
 }
 
 // Ascending list of the rows whose bit is set in any column block.  One
-// workgroup: each thread ORs one 32-row word over the column blocks, a
-// block-wide scan of the popcounts gives every set bit its list position.
+// workgroup, 1024 words (32768 rows) at a time: the (word, column block)
+// pairs of a chunk are spread over all threads, each issuing its loads
+// before ORing them into LDS, so the kernel waits for memory about once per
+// chunk; then a block-wide scan of the words' popcounts gives every set bit
+// its list position.
 __global__ __launch_bounds__(1024) void ovf_compact_kernel(const uint32_t *__restrict__ oflag,
                                                            int NB, int MW, int R_max,
                                                            int32_t *__restrict__ ovf_rows,
                                                            int32_t *__restrict__ ovf_count) {
+    __shared__ uint32_t s_or[1024];
     __shared__ int s_wsum[16];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     int running = 0;
     for (int base = 0; base < MW; base += 1024) {
+        const int cw = min(1024, MW - base);  // words in this chunk
+        const int pairs = cw * NB;
+        s_or[tid] = 0u;
+        __syncthreads();
+        for (int i0 = tid; i0 < pairs; i0 += 4 * 1024) {
+            uint32_t v[4];
+            int wl[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * 1024;
+                wl[u] = i % cw;
+                v[u] = i < pairs ? oflag[(size_t)(i / cw) * MW + base + wl[u]] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (v[u]) atomicOr(&s_or[wl[u]], v[u]);
+        }
+        __syncthreads();
         const int w = base + tid;
-        uint32_t word = 0;
-        if (w < MW)
-            for (int nb = 0; nb < NB; ++nb) word |= oflag[(size_t)nb * MW + w];
+        uint32_t word = tid < cw ? s_or[tid] : 0u;
         const int c = __popc(word);
         int incl = c;
 #pragma unroll

@@ -6,7 +6,6 @@
 
 #include <cstdarg>
 #include <cstdio>
-#include <mutex>
 
 #include "tw_internal.hpp"
 
@@ -59,38 +58,6 @@ tw_status record(void *const *events, int i, hipStream_t s) {
 
 tw_status launched(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(TW_EHIP, "%s: %s", what, hipGetErrorString(e));
-    return TW_OK;
-}
-
-// The overflow rows' dense path writes rows of y that the sparse kernel
-// leaves alone, so it runs concurrently on a side stream of the library
-// (one per device, default priority), forked from and joined back into the
-// caller's stream with events; the pattern is also valid under graph
-// capture.  The first call on a device creates the stream and its events
-// (it must not itself be captured).  The mutex keeps the fork/join
-// sequences of calls from different host threads from interleaving.
-struct Side {
-    bool ready = false;
-    hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-Side g_side[64];
-
-tw_status side_for_current_device(Side **out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(TW_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
-    if (dev < 0 || dev >= 64) return fail(TW_EUNSUPPORTED, "device index %d", dev);
-    Side &sd = g_side[dev];
-    if (!sd.ready) {
-        if ((e = hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming)) != hipSuccess ||
-            (e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming)) != hipSuccess)
-            return fail(TW_EHIP, "side stream set-up: %s", hipGetErrorString(e));
-        sd.ready = true;
-    }
-    *out = &sd;
     return TW_OK;
 }
 
@@ -199,36 +166,30 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     char *w = static_cast<char *>(ws);
     uint16_t *h = reinterpret_cast<uint16_t *>(w);
     float *partial = reinterpret_cast<float *>(w + round_up((size_t)R_max * N * 2, 256));
-    if (R_max == 0) {
-        TW_TRY(record(events, 0, s));
-        TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx,
-                                                 tw_cnt, y, s),
-                        "sparse_updown launch"));
-        for (int i = 1; i <= 4; ++i) TW_TRY(record(events, i, s));
-        return TW_OK;
-    }
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    Side *sd = nullptr;
-    TW_TRY(side_for_current_device(&sd));
-    hipStream_t f = sd->stream;
+    // All on the caller's stream: the sparse kernel, then the overflow
+    // rows' dense path (which writes the rows the sparse kernel skips).
+    // Running the two concurrently on a second stream was measured slower
+    // at the smaller shapes: the dense kernels' large LDS tiles cannot sit
+    // beside the sparse kernel's workgroups, and the cross-stream edges
+    // cost several microseconds each.
     TW_TRY(record(events, 0, s));
-    TW_TRY(launched(hipEventRecord(sd->fork, s), "fork record"));
-    TW_TRY(launched(hipStreamWaitEvent(f, sd->fork, 0), "fork wait"));
-    TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, f),
-                    "fallback gate+up launch"));
-    TW_TRY(record(events, 2, f));
-    TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, partial, f),
-                    "fallback down launch"));
-    TW_TRY(record(events, 3, f));
-    TW_TRY(launched(tw::launch_split_reduce(partial, ovf_rows, ovf_count, R_max, K, N, y, f),
-                    "fallback split-reduce launch"));
-    TW_TRY(record(events, 4, f));
-    TW_TRY(launched(hipEventRecord(sd->join, f), "join record"));
     TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx, tw_cnt,
                                              y, s),
                     "sparse_updown launch"));
     TW_TRY(record(events, 1, s));
-    TW_TRY(launched(hipStreamWaitEvent(s, sd->join, 0), "join wait"));
+    if (R_max > 0) {
+        TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, s),
+                        "fallback gate+up launch"));
+        TW_TRY(record(events, 2, s));
+        TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, partial, s),
+                        "fallback down launch"));
+        TW_TRY(record(events, 3, s));
+        TW_TRY(launched(tw::launch_split_reduce(partial, ovf_rows, ovf_count, R_max, K, N, y, s),
+                        "fallback split-reduce launch"));
+        TW_TRY(record(events, 4, s));
+    } else {
+        for (int i = 2; i <= 4; ++i) TW_TRY(record(events, i, s));
+    }
     return TW_OK;
 }
 

@@ -1,7 +1,7 @@
 // tw_gemm.hpp -- the software pipeline shared by the bf16 MFMA GEMMs:
-// operands stream from global memory straight into LDS (global_load_lds,
-// no register staging) through a ring of S stages, each 32 reduction
-// elements deep, so S-1 stages are in flight while one is multiplied.
+// operands stream from global memory straight into LDS (buffer loads with
+// the LDS bit, no register staging) through a ring of S stages, each 32
+// reduction elements deep, several stages ahead of the multiplication.
 #pragma once
 
 #include "tw_device.hpp"
@@ -24,6 +24,11 @@ __device__ __forceinline__ uint32_t poff(int r, int kc) {
     return (uint32_t)(r * kPRow + ((kc ^ swz(r)) << 4));
 }
 
+// s_waitcnt lgkmcnt(0) with the other counters left alone.
+__device__ __forceinline__ void wait_lgkm0() {
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
+}
+
 // s_waitcnt vmcnt(N) with the other counters left alone.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -43,28 +48,6 @@ __device__ __forceinline__ void wait_later(int later) {
     case 4: if constexpr (S > 5) { wait_vmcnt<4 * NI>(); break; } [[fallthrough]];
     case 5: if constexpr (S > 6) { wait_vmcnt<5 * NI>(); break; } [[fallthrough]];
     default: if constexpr (S > 7) { wait_vmcnt<6 * NI>(); } else { wait_vmcnt<0>(); } break;
-    }
-}
-
-// The k-loop over stages [kt0, kt1) through a ring of S slots of
-// `stage_bytes` at `ring`.  issue(kt, slot) enqueues this wave's NI direct
-// loads of stage kt into `slot`; compute(slot) multiplies a landed stage.
-// Every wave waits for its own loads of stage kt, then one barrier makes
-// the whole stage visible and also certifies that the slot refilled next
-// (read in the previous iteration) is free.  A bare s_barrier is used: the
-// fence of __syncthreads() would drain the loads still in flight.
-template <int S, int NI, typename Issue, typename Compute>
-__device__ __forceinline__ void kloop(int kt0, int kt1, char *ring, int stage_bytes, Issue issue,
-                                      Compute compute) {
-    static_assert(S >= 2 && S <= 8 && NI * (S - 2) < 64, "ring depth");
-    const int n = kt1 - kt0;
-    for (int j = 0; j < S - 1 && j < n; ++j) issue(kt0 + j, ring + (j % S) * stage_bytes);
-    for (int i = 0; i < n; ++i) {
-        const int later = min(S - 2, n - 1 - i);
-        wait_later<NI, S>(later);
-        __builtin_amdgcn_s_barrier();
-        if (i + S - 1 < n) issue(kt0 + i + S - 1, ring + ((i + S - 1) % S) * stage_bytes);
-        compute(ring + (i % S) * stage_bytes);
     }
 }
 
@@ -109,20 +92,27 @@ __device__ __forceinline__ void xcd_tile(int t, int nbm, int nbn, int &bm, int &
     bn = r0n + ti / gm;
 }
 
-// The same k-loop with the LDS reads software-pipelined against the matrix
-// instructions.  Each stage has two sub-steps of 16 reduction elements;
-// load(slot, sub, buf) reads one sub-step's fragments into register set
-// buf (0 or 1) and mma(buf) issues its matrix instructions.  The fragments
-// of the next sub-step are always read before the current one's matrix
-// instructions are issued, and the barrier sits in the middle of a stage:
-// after it the next stage's first fragments load while the current stage's
-// second half multiplies.  The barrier of iteration i certifies that every
-// wave has finished reading stage i, so stage i + S - 1 may refill the slot
-// of stage i - 1 at the start of iteration i.
-// The steady state (a stage still to issue) has no branches, so the
-// compiler can wait for exactly the fragments each matrix instruction
-// needs; a branch around the next stage's reads would make it wait for
-// those too.  The last S - 1 stages drain in a second loop.
+// The k-loop over stages [kt0, kt1) through a ring of S slots of
+// `stage_bytes` at `ring`, with the LDS reads software-pipelined against the
+// matrix instructions.  issue(kt, slot) enqueues this wave's NI direct loads
+// of stage kt into `slot`.  Each stage has two sub-steps of 16 reduction
+// elements; load(slot, sub, buf) reads one sub-step's fragments into
+// register set buf (0 or 1) and mma(buf) issues its matrix instructions.
+// The fragments of the next sub-step are always read before the current
+// one's matrix instructions are issued, and the barrier of iteration i sits
+// in the middle of stage i, after the first sub-step's matrix instructions.
+// Before it every wave waits for its own loads of stage i + 1 (vector
+// memory) and for its reads of stage i's second sub-step (LDS; they were
+// issued a whole batch of matrix instructions earlier, so this wait is
+// normally free).  The barrier therefore certifies that stage i + 1 is in
+// LDS and that no wave reads stage i any more: after it the next stage's
+// fragments may be read, and from iteration i + 1 on, stage i's slot may be
+// refilled.
+// A bare s_barrier is used: the fence of __syncthreads() would drain the
+// loads still in flight.  The steady state (a stage still to issue) has no
+// branches, so the compiler can wait for exactly the fragments each matrix
+// instruction needs; a branch around the next stage's reads would make it
+// wait for those too.  The last stages drain in a second loop.
 template <int S, int NI, typename Issue, typename Load, typename Mma>
 __device__ __forceinline__ void kloop_pipelined(int kt0, int kt1, char *ring, int stage_bytes,
                                                 Issue issue, Load load, Mma mma) {
@@ -130,7 +120,7 @@ __device__ __forceinline__ void kloop_pipelined(int kt0, int kt1, char *ring, in
     const int n = kt1 - kt0;
     for (int j = 0; j < S - 1 && j < n; ++j) issue(kt0 + j, ring + (j % S) * stage_bytes);
     if (n <= 0) return;
-    wait_later<NI, S>(min(S - 2, n - 1));
+    wait_later<NI, S>(min(S - 2, n - 1));  // stage 0 landed
     __builtin_amdgcn_s_barrier();
     load(ring, 0, 0);
     int i = 0;
@@ -139,11 +129,12 @@ __device__ __forceinline__ void kloop_pipelined(int kt0, int kt1, char *ring, in
     // two register sets into one and serialise reads and multiplies)
     for (; i + S - 1 < n; ++i) {
         load(ring + (i % S) * stage_bytes, 1, 1);
-        issue(kt0 + i + S - 1, ring + ((i + S - 1) % S) * stage_bytes);
+        issue(kt0 + i + S - 1, ring + ((i + S - 1) % S) * stage_bytes);  // slot of stage i - 1
         __builtin_amdgcn_sched_barrier(0);
         mma(0);
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<(S - 2) * NI>();  // stage i + 1 landed
+        wait_lgkm0();                // stage i fully read
         __builtin_amdgcn_s_barrier();
         load(ring + ((i + 1) % S) * stage_bytes, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -155,6 +146,7 @@ __device__ __forceinline__ void kloop_pipelined(int kt0, int kt1, char *ring, in
         mma(0);
         if (i + 1 < n) {
             wait_later<NI, S>(n - 2 - i);
+            wait_lgkm0();
             __builtin_amdgcn_s_barrier();
             load(ring + ((i + 1) % S) * stage_bytes, 0, 0);
         }

@@ -125,6 +125,9 @@ def main():
                          "write) so that a counter profile can scale FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays")
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="consecutive steps captured in one HIP graph (1: a graph launch "
+                         "per step)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -208,30 +211,50 @@ def main():
     t_sparse_eager = timed(lambda i: step(evp[i], evs[i]))
     t_dense_eager = timed(lambda i: dense(evd[i]))
 
-    # ---- whole-step throughput: each path captured once in a HIP graph ----
+    # ---- whole-step throughput: G consecutive steps of each path captured in
+    # one HIP graph (as a model forward would chain its layers), replayed so
+    # that exactly Ks steps run in the timed region ----
     g_sparse, g_dense = None, None
     if not args.no_graph:
-        g_sparse, g_dense = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        G = max(1, min(args.graph_steps, Ks))
+        sizes = [G] * (Ks // G) + ([Ks % G] if Ks % G else [])
+        step_cap = lambda: (tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
+                                            bufs["tw_cnt"], bufs["ovf_rows"],
+                                            bufs["ovf_count"], R_max, ws),
+                            tw.tw_sparse_ffn_fwd(x, wg, wu, wdn, T, C, bufs["tw_val"],
+                                                 bufs["tw_idx"], bufs["tw_cnt"],
+                                                 bufs["ovf_rows"], bufs["ovf_count"], R_max,
+                                                 y, ws))
+        dense_cap = lambda: tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd)
+        graphs = {}
         cap = torch.cuda.Stream()
         cap.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(cap):
-            step_cap = lambda: (tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
-                                                bufs["tw_cnt"], bufs["ovf_rows"],
-                                                bufs["ovf_count"], R_max, ws),
-                                tw.tw_sparse_ffn_fwd(x, wg, wu, wdn, T, C, bufs["tw_val"],
-                                                     bufs["tw_idx"], bufs["tw_cnt"],
-                                                     bufs["ovf_rows"], bufs["ovf_count"], R_max,
-                                                     y, ws))
-            with torch.cuda.graph(g_sparse, stream=cap):
-                step_cap()
-            with torch.cuda.graph(g_dense, stream=cap):
-                tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd)
+            for n in set(sizes):
+                gs, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gs, stream=cap):
+                    for _ in range(n):
+                        step_cap()
+                with torch.cuda.graph(gd, stream=cap):
+                    for _ in range(n):
+                        dense_cap()
+                graphs[n] = (gs, gd)
         torch.cuda.current_stream().wait_stream(cap)
-        for _ in range(2):
-            g_sparse.replay()
-            g_dense.replay()
-        t_sparse = timed(lambda i: g_sparse.replay())
-        t_dense = timed(lambda i: g_dense.replay())
+        for n in graphs:
+            graphs[n][0].replay()
+            graphs[n][1].replay()
+
+        def timed_graphs(which):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for n in sizes:
+                graphs[n][which].replay()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / Ks
+
+        t_sparse = timed_graphs(0)
+        t_dense = timed_graphs(1)
+        g_sparse = graphs
     else:
         t_sparse, t_dense = t_sparse_eager, t_dense_eager
 
@@ -254,12 +277,12 @@ def main():
     def span(evl, i, j):
         return sum(hev.ms(e[i], e[j]) for e in evl) / len(evl) * 1e-3
 
-    # the overflow path runs beside the sparse kernel (both start at event 0)
+    # the overflow path follows the sparse kernel on the same stream
     kern = {
         "gate_twell": avg(evp, 0),
         "ovf_compact": avg(evp, 1),
         "sparse_updown": span(evs, 0, 1),
-        "fallback_gateup": span(evs, 0, 2),
+        "fallback_gateup": span(evs, 1, 2),
         "fallback_down": span(evs, 2, 3),
         "fallback_reduce": span(evs, 3, 4),
     }
@@ -323,7 +346,8 @@ def main():
         "dense": {"ms_per_step": t_dense * 1e3, "value": M / t_dense},
         "eager": {"sparse_ms_per_step": t_sparse_eager * 1e3,
                   "dense_ms_per_step": t_dense_eager * 1e3},
-        "timing": "HIP graph replay of one step" if not args.no_graph else "eager launches",
+        "timing": (f"HIP graphs of {min(args.graph_steps, Ks)} consecutive steps, "
+                   f"replayed to run {Ks} steps") if not args.no_graph else "eager launches",
         "hipblaslt_dense": {"ms_per_step": t_blas * 1e3,
                             "speedup_vs": t_blas / t_sparse,
                             "note": "torch.matmul gate+up GEMM, ReLU*u in torch, bf16 h, "

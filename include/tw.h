@@ -26,9 +26,8 @@
  * ---------------------------------------
  * - bf16 values travel as raw uint16_t bit patterns.
  * - Every pointer argument except `stream` is a device pointer to memory the
- *   caller owns.  The library allocates no device memory and keeps no data
- *   between calls (its only state is the per-device side stream and two
- *   events of tw_sparse_ffn_fwd), so calls on different streams may run
+ *   caller owns.  The library allocates no device memory and keeps no
+ *   state between calls, so calls on different streams may run
  *   concurrently as long as their output and workspace buffers are
  *   distinct.
  * - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
@@ -46,8 +45,8 @@
  *   kernel and events[i+1] after kernel i.  tw_sparse_ffn_fwd launches 4:
  *   events[0] is recorded before any of them, events[1] after the sparse
  *   up+down kernel, events[2..4] after the overflow rows' gate+up, down and
- *   split-sum kernels, which run concurrently with the sparse kernel on a
- *   side stream of the library (see tw_sparse_ffn_fwd).
+ *   split-sum kernels, which follow it on the same stream (with R_max == 0
+ *   only the sparse kernel runs and events[1..4] are recorded together).
  *
  * Weight layout (one layout serves every path): wg_t, wu_t and wd are all
  * [N][K] row-major bf16.  wg_t and wu_t hold W_g and W_u transposed, so the
@@ -144,12 +143,8 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t,
  *   ovf_rows, ovf_count     the routing written by tw_pack_gate (device)
  *   y        [M][K]         fp32 out
  *
- * The overflow rows' dense path runs on a side stream the library creates
- * for the current device on the first call with R_max > 0 (default
- * priority), forked from `stream` and joined back into it with events: all
- * work is still complete when `stream` reaches the end of the call, and the
- * call can be captured into a HIP graph once that first call has been made
- * outside capture.
+ * The overflow rows' dense path follows the sparse kernel on `stream`; it
+ * writes exactly the listed rows of y, which the sparse kernel leaves alone.
  */
 tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
                             const uint16_t *wu_t, const uint16_t *wd,
