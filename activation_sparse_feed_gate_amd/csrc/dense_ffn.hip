@@ -380,17 +380,31 @@ hipError_t set_lds(F *kernel, int bytes, bool &done) {
     return e;
 }
 
+// A kernel instantiation with its shape constants.
+template <int BM, int BN, int WM, int WN, int S>
+struct GuCfg : GU<BM, BN, WM, WN, S> {
+    static constexpr int BM_ = BM, BN_ = BN;
+    static constexpr auto kernel = &gateup_kernel<BM, BN, WM, WN, S>;
+};
+template <int BM, int BN, int WM, int WN, int S>
+struct DnCfg : DN<BM, BN, WM, WN, S> {
+    static constexpr int BM_ = BM, BN_ = BN;
+    static constexpr auto kernel = &down_kernel<BM, BN, WM, WN, S>;
+};
+
 // dense comparator shapes and overflow-path shapes (the thin overflow
 // tiles do little matrix work per stage, so they keep more stages in flight)
-using GuDense = GU<256, 128, 4, 2, 4>;
-using GuRows = GU<64, 128, 1, 4, 6>;
-using DnDense = DN<128, 128, 2, 2, 4>;
-using DnRows = DN<128, 128, 2, 2, 8>;
+using GuDense = GuCfg<256, 128, 4, 2, 4>;
+using GuRows = GuCfg<128, 128, 2, 4, 4>;
+using DnDense = DnCfg<128, 128, 2, 2, 4>;
+using DnRows = DnCfg<128, 128, 2, 4, 6>;
 constexpr int kSplitGrid = 256;  // work items of the split down GEMM
 
 }  // namespace
 
-size_t split_partial_bytes() { return (size_t)kSplitGrid * 128 * 128 * sizeof(float); }
+size_t split_partial_bytes() {
+    return (size_t)kSplitGrid * DnRows::BM_ * DnRows::BN_ * sizeof(float);
+}
 
 hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const uint16_t *wu_t,
                          int K, int N, const int32_t *rowlist, const int32_t *count, int R_cap,
@@ -398,21 +412,21 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
     if (R_cap <= 0) return hipSuccess;
     if (rowlist) {
         static bool attr = false;
-        hipError_t e = set_lds(&gateup_kernel<64, 128, 1, 4, 6>, GuRows::LDS, attr);
+        hipError_t e = set_lds(GuRows::kernel, GuRows::LDS, attr);
         if (e != hipSuccess) return e;
         // one workgroup per CU at most: the grid is sized for the capacity
         // and most of it would find no rows
-        const int tiles = (R_cap + 63) / 64 * (N / 128);
+        const int tiles = (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_);
         const int grid = tiles < 256 ? tiles : 256;
-        hipLaunchKernelGGL((gateup_kernel<64, 128, 1, 4, 6>), dim3(grid), dim3(GuRows::NTH),
-                           GuRows::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h);
+        hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
+                           wu_t, K, N, rowlist, count, R_cap, M, h);
     } else {
         static bool attr = false;
-        hipError_t e = set_lds(&gateup_kernel<256, 128, 4, 2, 4>, GuDense::LDS, attr);
+        hipError_t e = set_lds(GuDense::kernel, GuDense::LDS, attr);
         if (e != hipSuccess) return e;
-        const int grid = (R_cap + 255) / 256 * (N / 128);
-        hipLaunchKernelGGL((gateup_kernel<256, 128, 4, 2, 4>), dim3(grid), dim3(GuDense::NTH),
-                           GuDense::LDS, s, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h);
+        const int grid = (R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_);
+        hipLaunchKernelGGL(GuDense::kernel, dim3(grid), dim3(GuDense::NTH), GuDense::LDS, s, x,
+                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h);
     }
     return hipGetLastError();
 }
@@ -421,19 +435,19 @@ hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
                        float *partial, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    const int tiles = (R_cap + 127) / 128 * (K / 128);
     if (partial) {
         static bool attr = false;
-        hipError_t e = set_lds(&down_kernel<128, 128, 2, 2, 8>, DnRows::LDS, attr);
+        hipError_t e = set_lds(DnRows::kernel, DnRows::LDS, attr);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((down_kernel<128, 128, 2, 2, 8>), dim3(kSplitGrid), dim3(DnRows::NTH),
-                           DnRows::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial);
+        hipLaunchKernelGGL(DnRows::kernel, dim3(kSplitGrid), dim3(DnRows::NTH), DnRows::LDS, s, h,
+                           wd, K, N, rowlist, count, R_cap, y, partial);
     } else {
         static bool attr = false;
-        hipError_t e = set_lds(&down_kernel<128, 128, 2, 2, 4>, DnDense::LDS, attr);
+        hipError_t e = set_lds(DnDense::kernel, DnDense::LDS, attr);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((down_kernel<128, 128, 2, 2, 4>), dim3(tiles), dim3(DnDense::NTH),
-                           DnDense::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial);
+        const int tiles = (R_cap + DnDense::BM_ - 1) / DnDense::BM_ * (K / DnDense::BN_);
+        hipLaunchKernelGGL(DnDense::kernel, dim3(tiles), dim3(DnDense::NTH), DnDense::LDS, s, h,
+                           wd, K, N, rowlist, count, R_cap, y, partial);
     }
     return hipGetLastError();
 }
@@ -445,7 +459,7 @@ hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
     // enough workgroups for the largest split case: at most kSplitGrid tiles
     int grid = (int)(((size_t)R_cap * K / 4 + 255) / 256);
     grid = grid < 1024 ? grid : 1024;
-    hipLaunchKernelGGL((split_reduce_kernel<128, 128>), dim3(grid), dim3(256), 0, s, partial,
+    hipLaunchKernelGGL((split_reduce_kernel<DnRows::BM_, DnRows::BN_>), dim3(grid), dim3(256), 0, s, partial,
                        rowlist, count, R_cap, K, N, kSplitGrid, y);
     return hipGetLastError();
 }
