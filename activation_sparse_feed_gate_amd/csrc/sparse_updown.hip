@@ -16,8 +16,10 @@
 // - Within a wave, lane l owns the 16-byte chunks l, l+64, ... of a K-row:
 //   the gathers of W_u^T[j] and W_d[j] are fully coalesced 1 KB wave loads,
 //   x_m stays in registers for the whole row, and y_m accumulates in fp32
-//   registers.  Entries are taken four at a time so that eight row loads are
-//   in flight before the first dot product needs its data.
+//   registers.  Entries are taken two at a time (four row loads in flight
+//   per wave): larger batches hold more registers and leave fewer waves
+//   resident, which measured slower at every shape (at K = 1024, 78 VGPRs
+//   and six waves per SIMD against 112 and four).
 // - The dot product is reduced across the wave with DPP (no LDS), its
 //   product with g is the scalar h_j, and h_j * W_d[j] is added lane-wise.
 // - The four partial y rows are summed in LDS in a fixed order (the result
@@ -30,6 +32,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+constexpr int kBatch = 2;  // active neurons gathered together per wave
 
 template <int KCH>
 __global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
@@ -108,20 +111,20 @@ __global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
             gl = tw_val[q];
         }
         const int nb = min(64, ne - e0);
-        for (int b = 0; b < nb; b += 4) {
-            int j[4];
-            float g[4];
+        for (int b = 0; b < nb; b += kBatch) {
+            int j[kBatch];
+            float g[kBatch];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kBatch; ++u) {
                 const bool ok = b + u < nb;
                 const int src = ok ? b + u : b;
                 j[u] = __builtin_amdgcn_readlane(jl, src);
                 g[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), src))
                           : 0.0f;
             }
-            u32x4 wu[4][KCH], wv[4][KCH];
+            u32x4 wu[kBatch][KCH], wv[kBatch][KCH];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kBatch; ++u) {
                 const uint16_t *pu = wu_t + (size_t)j[u] * K;
                 const uint16_t *pd = wd + (size_t)j[u] * K;
 #pragma unroll
@@ -132,9 +135,9 @@ __global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
                     wv[u][ch] = in ? ld16(pd + 8 * q) : u32x4{0u, 0u, 0u, 0u};
                 }
             }
-            float p[4];
+            float p[kBatch];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < kBatch; ++u) {
                 float s = 0.0f;
 #pragma unroll
                 for (int ch = 0; ch < KCH; ++ch)
@@ -146,9 +149,9 @@ __global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
                 p[u] = s;
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) p[u] = wave_sum(p[u]) * g[u];
+            for (int u = 0; u < kBatch; ++u) p[u] = wave_sum(p[u]) * g[u];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < kBatch; ++u)
 #pragma unroll
                 for (int ch = 0; ch < KCH; ++ch)
 #pragma unroll
