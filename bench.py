@@ -117,11 +117,21 @@ def cpu_baseline(d, w, budget_s: float):
     while passes == 0 or secs < 0.5 * budget_s:
         secs += run(rows)
         passes += 1
+    # the oracle's plain dense FFN on the same rows, for the CPU's own
+    # sparse-over-dense ratio (one pass, a quarter of the budget at most)
+    xs = oracle.widen_bf16(d["x"][rows])
+    nd = max(1, min(len(rows), int(0.25 * budget_s / max(secs / passes / len(rows) * 4, 1e-9))))
+    t = time.perf_counter()
+    orc.dense_ffn(xs[:nd], wg, wu, wd)
+    dsecs = time.perf_counter() - t
     return {"value": passes * len(rows) / secs, "unit": "tokens/s", "cores": orc.threads(),
             "kind": "oracle",
             "sample": f"{len(rows)} of {w.M} token rows, evenly strided, {passes} pass(es); "
                       f"float64 gate, TwELL packing, sparse up+down with dense recompute of "
-                      f"overflow rows; {secs:.1f} s"}
+                      f"overflow rows; {secs:.1f} s",
+            "dense_value": nd / dsecs,
+            "dense_sample": f"oracle dense gated FFN (float64) on {nd} of those rows; "
+                            f"{dsecs:.1f} s"}
 
 
 def main():
@@ -138,7 +148,9 @@ def main():
                          "write) so that a counter profile can scale FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays")
-    ap.add_argument("--graph-steps", type=int, default=10,
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="replays for the Infinity-Cache-cold line (0: skip it)")
+    ap.add_argument("--graph-steps", type=int, default=5,
                     help="consecutive steps captured in one HIP graph (1: a graph launch "
                          "per step)")
     args = ap.parse_args()
@@ -258,18 +270,70 @@ def main():
             graphs[n][1].replay()
 
         def timed_graphs(which):
+            """Mean step time over the Ks steps (host clock around the whole
+            loop), and per-replay step times from events between replays."""
+            evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in sizes]
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            for n in sizes:
+            for (a, b), n in zip(evs_, sizes):
+                a.record()
                 graphs[n][which].replay()
+                b.record()
             torch.cuda.synchronize()
-            return (time.perf_counter() - t0) / Ks
+            mean = (time.perf_counter() - t0) / Ks
+            per = [a.elapsed_time(b) * 1e-3 / n for (a, b), n in zip(evs_, sizes)]
+            return mean, per
 
-        t_sparse = timed_graphs(0)
-        t_dense = timed_graphs(1)
+        t_sparse, per_sparse = timed_graphs(0)
+        t_dense, per_dense = timed_graphs(1)
         g_sparse = graphs
+
+        # ---- Infinity-Cache-cold steps: an in-place pass over 512 MB (twice
+        # the 256 MB cache) before each step evicts the weights, as in a deep
+        # model where the other layers' weights pass through the cache between
+        # two uses of this one.  Step time = (flush + step) - flush, each the
+        # median of Kc graph replays. ----
+        cold = None
+        if args.cold_steps > 0:
+            flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+            gf, gfs, gfd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(gf, stream=cap):
+                    flush.add_(1)
+                with torch.cuda.graph(gfs, stream=cap):
+                    flush.add_(1)
+                    step_cap()
+                with torch.cuda.graph(gfd, stream=cap):
+                    flush.add_(1)
+                    dense_cap()
+            torch.cuda.current_stream().wait_stream(cap)
+
+            def med_replay(g):
+                ts = []
+                for _ in range(args.cold_steps):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    g.replay()
+                    b.record()
+                    b.synchronize()
+                    ts.append(a.elapsed_time(b) * 1e-3)
+                return float(np.median(ts))
+
+            for g in (gf, gfs, gfd):
+                g.replay()
+            t_f = med_replay(gf)
+            t_cs = med_replay(gfs) - t_f
+            t_cd = med_replay(gfd) - t_f
+            cold = {"ms_per_step": t_cs * 1e3, "value": M / t_cs, "dense_ms_per_step": t_cd * 1e3,
+                    "speedup_vs_dense": t_cd / t_cs, "flush_ms": t_f * 1e3,
+                    "note": f"median of {args.cold_steps} replays of (512 MB in-place pass + step) "
+                            f"minus the pass alone"}
+            del flush
     else:
         t_sparse, t_dense = t_sparse_eager, t_dense_eager
+        per_sparse, per_dense, cold = [t_sparse_eager], [t_dense_eager], None
 
     # ---- sanity line: the same dense FFN on torch.matmul (hipBLASLt) ----
     wgu = torch.cat([wg, wu], dim=0)
@@ -356,7 +420,11 @@ def main():
                    "density": w.density, "sigma_s": w.sigma_s, "seed": w.seed, "R_max": R_max},
         "roofline": roof(dominant, kern[dominant]),
         "speedup_vs_dense": t_dense / t_sparse,
-        "dense": {"ms_per_step": t_dense * 1e3, "value": M / t_dense},
+        "ms_per_step_p10_p50_p90": [float(np.percentile(per_sparse, q)) * 1e3 for q in (10, 50, 90)],
+        "dense": {"ms_per_step": t_dense * 1e3, "value": M / t_dense,
+                  "ms_per_step_p10_p50_p90": [float(np.percentile(per_dense, q)) * 1e3
+                                              for q in (10, 50, 90)]},
+        "cold": cold,
         "eager": {"sparse_ms_per_step": t_sparse_eager * 1e3,
                   "dense_ms_per_step": t_dense_eager * 1e3},
         "timing": (f"HIP graphs of {min(args.graph_steps, Ks)} consecutive steps, "
