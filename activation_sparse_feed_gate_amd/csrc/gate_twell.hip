@@ -10,22 +10,24 @@
 //
 // gfx950 design
 // - Macro tile 256 rows x 256 columns, 8 waves (two per SIMD, so one wave's
-//   loads overlap the other's matrix work) in a 4 x 2 grid, each wave owning
-//   64 x 128 outputs as 2 x 4 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32
-//   accumulators per lane).  Operands stream from global memory straight into
-//   LDS (no register staging) through a 4-stage ring, 32 reduction elements
-//   per stage, three stages ahead of the multiplication.  Each XCD is given a
-//   compact region of the tile grid so that its L2 serves the workgroups
-//   resident on it (xcd_tile).
-// - Epilogue without an LDS round trip: in the 32x32 MFMA result layout one
-//   accumulator register of a block holds 32 consecutive columns of two rows
-//   (lanes 0-31 and 32-63), so one 64-bit wavefront ballot of (z > 0) gives
-//   the activity masks of both rows.  Popcounts of the masks give the counts,
-//   and popcount of the mask bits below a lane gives its slot, in ascending
-//   column order.  With T = 128 a tile is exactly one wave's 128 columns;
-//   with T = 256 it spans the two waves of a wave row, which exchange their
-//   half counts through LDS.  The 64 row counts of a wave are gathered into
-//   one register (lane r holds row r) and stored by one instruction.
+//   loads and LDS reads overlap the other's matrix work) in a 4 x 2 grid,
+//   each wave owning 64 x 128 outputs as 2 x 4 blocks of
+//   v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane).  Operands
+//   stream from global memory straight into LDS (buffer loads with the LDS
+//   bit, no register staging) through a 4-stage ring, 32 reduction elements
+//   per stage, with the fragment reads software-pipelined against the matrix
+//   instructions (tw_gemm.hpp).  Each XCD is given a compact region of the
+//   tile grid so that its L2 serves the workgroups resident on it.
+// - Epilogue: the ring is free after the k-loop.  Each wave stages 32 of its
+//   64 rows of accumulators in LDS at a time; lane l then owns half a row
+//   (row l % 32, 64 of the wave's 128 columns), builds its activity mask
+//   (z > 0) with vector compares, and the two halves' popcounts give the
+//   row count and this half's first slot, so the lane stores its entries in
+//   ascending column order straight into TwELL.  No dense gate is written.
+//   With T = 128 a tile is exactly one wave's 128 columns; with T = 256 it
+//   spans the two waves of a wave row, which exchange their half counts
+//   through LDS.  The 64 row counts of a wave are gathered into one register
+//   (lane r holds row r) and stored by one instruction.
 // - Each workgroup writes one bit per row (overflowing or not) for its column
 //   block, so no buffer needs clearing beforehand; the compaction kernel ORs
 //   the column blocks and lists the set rows in ascending order.

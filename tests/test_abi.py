@@ -78,7 +78,7 @@ def _pack(tw, M=64, K=256, N=1024, T=128, C=16, R=64, ws=1 << 20, **ptrs):
     (dict(C=129), 1), (dict(K=192), 2), (dict(K=8192), 2), (dict(R=65), 1), (dict(R=-1), 1),
     (dict(M=-1), 1), (dict(K=0), 1), (dict(x=None), 1), (dict(wg=None), 1), (dict(val=None), 1),
     (dict(n=None), 1), (dict(w=None), 1), (dict(x=P + 8), 1), (dict(z=P + 4), 1), (dict(ws=16), 1),
-    (dict(N=128 * 300), 2),
+    (dict(N=128 * 300), 2), (dict(M=1 << 20, K=4096, R=0), 2), (dict(M=1 << 19, K=4096, R=0), 2),
 ])
 def test_pack_rejects(tw, kw, code):
     assert _pack(tw, **kw) == code
@@ -96,3 +96,5 @@ def test_sparse_and_dense_reject(tw):
     assert L.tw_ffn_fwd(P, P, P, P, 64, 256, 1000, P, P, 1 << 24, None, None) == 2
     assert L.tw_ffn_fwd(P, P, P, None, 64, 256, 1024, P, P, 1 << 24, None, None) == 1
     assert L.tw_ffn_fwd(P, P, P, P, 64, 256, 1024, P, P, 16, None, None) == 1
+    # weights of 4 GiB or more are outside the 32-bit buffer offsets
+    assert L.tw_ffn_fwd(P, P, P, P, 64, 4096, 1 << 19, P, P, 1 << 40, None, None) == 2
