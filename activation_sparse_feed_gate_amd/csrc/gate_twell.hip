@@ -50,7 +50,10 @@ constexpr int kEpiWave = 32 * kEpiPitch * 4;                 // 17 KB
 constexpr int kLdsTiles = kRing > 8 * kEpiWave ? kRing : 8 * kEpiWave;
 constexpr int kLdsBytes = kLdsTiles + 64 + 2 * kGateBM * 4; // + row flags + half counts
 
-template <int T>
+// PACK: the fused gate of the review (ReLU + TwELL packing in the epilogue,
+// zdbg an optional debug copy of the gate).  !PACK: the unfused baseline's
+// first half, the dense gate z written to zdbg and nothing packed (T unused).
+template <int T, bool PACK>
 __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t, int M, int K, int N,
     int C, int NBM, int NBN, float *__restrict__ tw_val, int32_t *__restrict__ tw_idx,
@@ -114,6 +117,22 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     };
     settle_scalars(tw_val, tw_idx, tw_cnt, oflag, zdbg);
     kloop_pipelined<kStages, 4>(0, K / kPK, smem, kStageBytes, issue, load, mma);
+    if constexpr (!PACK) {
+        // each store instruction writes 32 consecutive columns of two rows
+        const int ncol0 = n0 + wn * 128;
+        if (ncol0 < N) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int m = m0 + wm * 64 + a * 32 + mfma32_row(i, lane);
+                        if (m < M) zdbg[(size_t)m * N + ncol0 + b * 32 + (lane & 31)] = acc[a][b][i];
+                    }
+        }
+        return;
+    }
     __syncthreads();
 
     // ---------------- epilogue: ReLU + TwELL pack + row overflow bits ----
@@ -270,21 +289,22 @@ __global__ __launch_bounds__(1024) void ovf_compact_kernel(const uint32_t *__res
     if (tid == 0) *ovf_count = running;
 }
 
-template <int T>
+template <int T, bool PACK>
 hipError_t launch_gate_t(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int C,
                          float *tw_val, int32_t *tw_idx, int32_t *tw_cnt, uint32_t *oflag,
                          float *z_debug, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gate_twell_kernel<T>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+        hipError_t e =
+            hipFuncSetAttribute(reinterpret_cast<const void *>(&gate_twell_kernel<T, PACK>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int NBN = gate_col_blocks(N);
     const int NBM = (M + kGateBM - 1) / kGateBM;
-    hipLaunchKernelGGL(gate_twell_kernel<T>, dim3(NBN * NBM), dim3(kThreads), kLdsBytes, s, x,
-                       wg_t, M, K, N, C, NBM, NBN, tw_val, tw_idx, tw_cnt, oflag, z_debug);
+    hipLaunchKernelGGL((gate_twell_kernel<T, PACK>), dim3(NBN * NBM), dim3(kThreads), kLdsBytes,
+                       s, x, wg_t, M, K, N, C, NBM, NBN, tw_val, tw_idx, tw_cnt, oflag, z_debug);
     return hipGetLastError();
 }
 
@@ -295,8 +315,17 @@ hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int
                              uint32_t *oflag, float *z_debug, hipStream_t s) {
     if (M == 0) return hipSuccess;
     if (T == 128)
-        return launch_gate_t<128>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug, s);
-    return launch_gate_t<256>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug, s);
+        return launch_gate_t<128, true>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
+                                        z_debug, s);
+    return launch_gate_t<256, true>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug,
+                                    s);
+}
+
+hipError_t launch_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
+                             float *z, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+    return launch_gate_t<128, false>(x, wg_t, M, K, N, 1, nullptr, nullptr, nullptr, nullptr, z,
+                                     s);
 }
 
 hipError_t launch_ovf_compact(const uint32_t *oflag, int NB, int MW, int R_max,

@@ -141,6 +141,59 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t, int M, int K, in
     return TW_OK;
 }
 
+tw_status tw_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, float *z,
+                        void *stream, void *const *events) {
+    if (M < 0 || K <= 0 || N <= 0) return fail(TW_EINVAL, "M=%d K=%d N=%d: need M >= 0, K, N > 0", M, K, N);
+    if (K % 128) return fail(TW_EUNSUPPORTED, "K=%d: must be a multiple of 128", K);
+    if (N % 128) return fail(TW_EUNSUPPORTED, "N=%d: must be a multiple of 128", N);
+    TW_NEED_M(x);
+    TW_NEED(wg_t);
+    TW_NEED_M(z);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_gate_dense(x, wg_t, M, K, N, z, s), "dense gate launch"));
+    TW_TRY(record(events, 1, s));
+    return TW_OK;
+}
+
+size_t tw_pack_dense_workspace_bytes(int M, int N) {
+    if (M < 0 || N <= 0) return 0;
+    return pack_ws(M, N) + 256;
+}
+
+tw_status tw_pack_dense(const float *z, int M, int N, int T, int C, float *tw_val,
+                        int32_t *tw_idx, int32_t *tw_cnt, int32_t *ovf_rows, int32_t *ovf_count,
+                        int R_max, void *ws, size_t ws_bytes, void *stream,
+                        void *const *events) {
+    if (M < 0 || N <= 0) return fail(TW_EINVAL, "M=%d N=%d: need M >= 0, N > 0", M, N);
+    if (T != 128 && T != 256) return fail(TW_EUNSUPPORTED, "tile width T=%d: supported 128, 256", T);
+    if (N % T) return fail(TW_EINVAL, "N=%d is not a multiple of T=%d", N, T);
+    if (N / T > 256) return fail(TW_EUNSUPPORTED, "N/T=%d tiles per row: at most 256", N / T);
+    if (C < 1 || C > T) return fail(TW_EINVAL, "capacity C=%d outside [1, T=%d]", C, T);
+    if (R_max < 0 || R_max > M) return fail(TW_EINVAL, "R_max=%d outside [0, M=%d]", R_max, M);
+    TW_NEED_M(z);
+    TW_NEED_M(tw_val);
+    TW_NEED_M(tw_idx);
+    TW_NEED_M(tw_cnt);
+    TW_NEED(ovf_rows);
+    TW_NEED(ovf_count);
+    TW_NEED(ws);
+    const size_t need = tw_pack_dense_workspace_bytes(M, N);
+    if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *oflag = static_cast<uint32_t *>(ws);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_pack_dense(z, M, N, T, C, tw_val, tw_idx, tw_cnt, oflag, s),
+                    "dense pack launch"));
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_col_blocks(N), tw::row_words(M), R_max,
+                                           ovf_rows, ovf_count, s),
+                    "ovf_compact launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
 tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t,
                             const uint16_t *wd, int M, int K, int N, int T, int C,
                             const float *tw_val, const int32_t *tw_idx, const int32_t *tw_cnt,

@@ -19,6 +19,16 @@ hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int
                              int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
                              uint32_t *oflag, float *z_debug, hipStream_t s);
 
+// The dense gate z = x W_g as fp32 [M][N] (the gate kernel without its
+// packing epilogue).
+hipError_t launch_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
+                             float *z, hipStream_t s);
+
+// TwELL packing and row-overflow bits of a dense gate [M][N], in the same
+// layouts the fused gate kernel writes (the compaction follows).
+hipError_t launch_pack_dense(const float *z, int M, int N, int T, int C, float *tw_val,
+                             int32_t *tw_idx, int32_t *tw_cnt, uint32_t *oflag, hipStream_t s);
+
 hipError_t launch_ovf_compact(const uint32_t *oflag, int NB, int MW, int R_max,
                               int32_t *ovf_rows, int32_t *ovf_count, hipStream_t s);
 

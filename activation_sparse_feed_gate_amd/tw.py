@@ -46,6 +46,13 @@ _lib.tw_sparse_ffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, 
                                    _vp, _i, _vp, _vp, _sz, _vp, _vp]
 _lib.tw_ffn_fwd.restype = _i
 _lib.tw_ffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _vp, _vp, _sz, _vp, _vp]
+_lib.tw_gate_dense.restype = _i
+_lib.tw_gate_dense.argtypes = [_vp, _vp, _i, _i, _i, _vp, _vp, _vp]
+_lib.tw_pack_dense_workspace_bytes.restype = _sz
+_lib.tw_pack_dense_workspace_bytes.argtypes = [_i, _i]
+_lib.tw_pack_dense.restype = _i
+_lib.tw_pack_dense.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp,
+                               _vp]
 
 TW_OK, TW_EINVAL, TW_EUNSUPPORTED, TW_EHIP = 0, 1, 2, 3
 
@@ -140,6 +147,34 @@ def tw_ffn_fwd(x, wg_t, wu_t, wd, y, ws, stream=None, events=None) -> None:
     _check(st, "tw_ffn_fwd")
 
 
+def tw_gate_dense(x, wg_t, z, stream=None, events=None) -> None:
+    M, K = x.shape
+    N = wg_t.shape[0]
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(wg_t, torch.bfloat16, "wg_t")
+    _dtype(z, torch.float32, "z")
+    ev = _events(events)
+    st = _lib.tw_gate_dense(_ptr(x), _ptr(wg_t), M, K, N, _ptr(z), _stream(stream),
+                            ev[0] if ev else None)
+    _check(st, "tw_gate_dense")
+
+
+def tw_pack_dense_workspace_bytes(M, N) -> int:
+    return int(_lib.tw_pack_dense_workspace_bytes(M, N))
+
+
+def tw_pack_dense(z, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_max, ws, stream=None,
+                  events=None) -> None:
+    M, N = z.shape
+    _dtype(z, torch.float32, "z")
+    ev = _events(events)
+    st = _lib.tw_pack_dense(_ptr(z), M, N, T, C, _ptr(tw_val), _ptr(tw_idx), _ptr(tw_cnt),
+                            _ptr(ovf_rows), _ptr(ovf_count), R_max, _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream(stream),
+                            ev[0] if ev else None)
+    _check(st, "tw_pack_dense")
+
+
 # ------------------------------------------------------------- allocating --
 def alloc_pack(M, N, T, C, R_max, device="cuda"):
     """Output buffers of tw_pack_gate."""
@@ -173,6 +208,21 @@ def pack_gate(x, wg_t, T, C, R_max=None, z_debug=False, ws=None):
     if z_debug:
         out["z"] = z
     out.update(T=T, C=C, R_max=R_max)
+    return out
+
+
+def pack_unfused(x, wg_t, T, C, R_max=None):
+    """The unfused equivalent of pack_gate: dense gate in memory, then packed."""
+    M, K = x.shape
+    N = wg_t.shape[0]
+    R_max = M if R_max is None else R_max
+    out = alloc_pack(M, N, T, C, R_max, x.device)
+    z = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    ws = torch.empty((tw_pack_dense_workspace_bytes(M, N),), dtype=torch.uint8, device=x.device)
+    tw_gate_dense(x, wg_t, z)
+    tw_pack_dense(z, T, C, out["tw_val"], out["tw_idx"], out["tw_cnt"], out["ovf_rows"],
+                  out["ovf_count"], R_max, ws)
+    out.update(T=T, C=C, R_max=R_max, z=z)
     return out
 
 

@@ -148,6 +148,8 @@ def main():
                          "write) so that a counter profile can scale FETCH_SIZE/WRITE_SIZE")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of HIP-graph replays")
+    ap.add_argument("--no-fusion-ablation", dest="fusion_ablation", action="store_false",
+                    help="skip timing the unfused gate + pack path")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="replays for the Infinity-Cache-cold line (0: skip it)")
     ap.add_argument("--graph-steps", type=int, default=5,
@@ -289,6 +291,49 @@ def main():
         t_dense, per_dense = timed_graphs(1)
         g_sparse = graphs
 
+        # ---- the fusion the method turns on: packing in the gate's epilogue
+        # (tw_pack_gate) against the unfused path that writes the dense gate
+        # and packs it in a separate pass (tw_gate_dense + tw_pack_dense) ----
+        fusion = None
+        if args.fusion_ablation:
+            zbuf = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            wsp = torch.empty((tw.tw_pack_dense_workspace_bytes(M, N),), dtype=torch.uint8,
+                              device="cuda")
+            bu = tw.alloc_pack(M, N, T, C, R_max)
+            fused_cap = lambda: tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
+                                                bufs["tw_cnt"], bufs["ovf_rows"],
+                                                bufs["ovf_count"], R_max, ws)
+            unfused_cap = lambda: (tw.tw_gate_dense(x, wg, zbuf),
+                                   tw.tw_pack_dense(zbuf, T, C, bu["tw_val"], bu["tw_idx"],
+                                                    bu["tw_cnt"], bu["ovf_rows"],
+                                                    bu["ovf_count"], R_max, wsp))
+            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(ga, stream=cap):
+                    for _ in range(G):
+                        fused_cap()
+                with torch.cuda.graph(gb, stream=cap):
+                    for _ in range(G):
+                        unfused_cap()
+            torch.cuda.current_stream().wait_stream(cap)
+
+            def per_call(g):
+                g.replay()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(max(1, Ks // G)):
+                    g.replay()
+                torch.cuda.synchronize()
+                return (time.perf_counter() - t0) / (max(1, Ks // G) * G)
+
+            t_fu, t_un = per_call(ga), per_call(gb)
+            fusion = {"fused_pack_us": t_fu * 1e6, "unfused_pack_us": t_un * 1e6,
+                      "unfused_over_fused": t_un / t_fu,
+                      "dense_gate_bytes": M * N * 4,
+                      "note": "tw_pack_gate vs tw_gate_dense + tw_pack_dense (dense fp32 gate "
+                              "written, read back and packed), HIP graphs, same outputs"}
+            del zbuf
+
         # ---- Infinity-Cache-cold steps: an in-place pass over 512 MB (twice
         # the 256 MB cache) before each step evicts the weights, as in a deep
         # model where the other layers' weights pass through the cache between
@@ -333,7 +378,7 @@ def main():
             del flush
     else:
         t_sparse, t_dense = t_sparse_eager, t_dense_eager
-        per_sparse, per_dense, cold = [t_sparse_eager], [t_dense_eager], None
+        per_sparse, per_dense, cold, fusion = [t_sparse_eager], [t_dense_eager], None, None
 
     # ---- sanity line: the same dense FFN on torch.matmul (hipBLASLt) ----
     wgu = torch.cat([wg, wu], dim=0)
@@ -425,6 +470,7 @@ def main():
                   "ms_per_step_p10_p50_p90": [float(np.percentile(per_dense, q)) * 1e3
                                               for q in (10, 50, 90)]},
         "cold": cold,
+        "fusion": fusion,
         "eager": {"sparse_ms_per_step": t_sparse_eager * 1e3,
                   "dense_ms_per_step": t_dense_eager * 1e3},
         "timing": (f"HIP graphs of {min(args.graph_steps, Ks)} consecutive steps, "

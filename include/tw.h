@@ -20,7 +20,8 @@
  *                      rows that fit, and the dense path for the listed rows.
  *
  * tw_ffn_fwd is the dense gated FFN over all rows, the comparator the sparse
- * path is measured against.
+ * path is measured against.  tw_gate_dense + tw_pack_dense are the unfused
+ * equivalent of tw_pack_gate (dense gate written to memory, then packed).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -125,6 +126,33 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t,
                        int32_t *ovf_rows, int32_t *ovf_count, int R_max,
                        float *z_debug, void *ws, size_t ws_bytes,
                        void *stream, void *const *events);
+
+/*
+ * The unfused alternative to tw_pack_gate, in two calls: section 3-4
+ * contrasts packing in the gate's epilogue with computing the dense gate,
+ * writing it to memory and packing it in a separate pass (an extra write,
+ * read and write of the whole gate).  These calls are that separate path,
+ * kept for measuring what the fusion saves and for packing gates computed
+ * elsewhere; their outputs are identical to tw_pack_gate's.
+ *
+ * tw_gate_dense: z = x W_g as fp32 [M][N] (the same kernel and arithmetic
+ * as tw_pack_gate, so z is bitwise tw_pack_gate's z_debug).  K and N
+ * multiples of 128.  events: [0] before, [1] after the kernel.
+ *
+ * tw_pack_dense: TwELL packing and overflow routing of any fp32 gate z
+ * [M][N] (active means z > 0), with exactly the outputs and conventions of
+ * tw_pack_gate above (same shape limits on N, T, C, R_max).  The workspace
+ * holds the row-overflow bits: ws_bytes >= tw_pack_dense_workspace_bytes
+ * (tw_workspace_bytes of the same shape is always enough).  events: [0]
+ * before, [1] after the packing kernel, [2] after the compaction.
+ */
+tw_status tw_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, float *z,
+                        void *stream, void *const *events);
+size_t tw_pack_dense_workspace_bytes(int M, int N);
+tw_status tw_pack_dense(const float *z, int M, int N, int T, int C,
+                        float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                        int32_t *ovf_rows, int32_t *ovf_count, int R_max,
+                        void *ws, size_t ws_bytes, void *stream, void *const *events);
 
 /*
  * Sparse up+down for the rows that fit, dense path for the overflow list.

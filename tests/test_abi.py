@@ -98,3 +98,21 @@ def test_sparse_and_dense_reject(tw):
     assert L.tw_ffn_fwd(P, P, P, P, 64, 256, 1024, P, P, 16, None, None) == 1
     # weights of 4 GiB or more are outside the 32-bit buffer offsets
     assert L.tw_ffn_fwd(P, P, P, P, 64, 4096, 1 << 19, P, P, 1 << 40, None, None) == 2
+
+
+def test_unfused_entry_points_reject(tw):
+    L = tw._lib
+    assert L.tw_gate_dense(P, P, 64, 100, 1024, P, None, None) == 2   # K not a multiple of 128
+    assert L.tw_gate_dense(P, P, 64, 256, 1000, P, None, None) == 2   # N not a multiple of 128
+    assert L.tw_gate_dense(None, P, 64, 256, 1024, P, None, None) == 1
+    assert L.tw_gate_dense(P, P, 64, 256, 1024, P + 4, None, None) == 1
+    assert L.tw_pack_dense_workspace_bytes(64, 1024) >= 4 * 4
+    ws = L.tw_pack_dense_workspace_bytes(64, 1024)
+    # z, M, N, T, C, val, idx, cnt, ovf_rows, ovf_count, R_max, ws, ws_bytes, stream, events
+    assert L.tw_pack_dense(P, 64, 1024, 64, 8, P, P, P, P, P, 64, P, ws, None, None) == 2
+    assert L.tw_pack_dense(P, 64, 1024, 128, 0, P, P, P, P, P, 64, P, ws, None, None) == 1
+    assert L.tw_pack_dense(P, 64, 1000, 128, 8, P, P, P, P, P, 64, P, ws, None, None) == 1
+    assert L.tw_pack_dense(P, 64, 1024, 128, 8, P, P, P, P, P, 65, P, ws, None, None) == 1
+    assert L.tw_pack_dense(P, 64, 1024, 128, 8, P, P, P, P, P, 64, P, 8, None, None) == 1
+    assert L.tw_pack_dense(None, 64, 1024, 128, 8, P, P, P, P, P, 64, P, ws, None, None) == 1
+    assert tw._lib.tw_last_error()
