@@ -73,15 +73,19 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of the hot path: a tiny CPU-checkable block, three
-# blocks at 0.5B / 1B / 2B scale with 1% / 0.5% / 0.3% active gate entries,
-# and an overflow-stress block with a heavier per-token tail.
+# The workloads of the hot path: a tiny CPU-checkable block, three blocks at
+# 0.5B / 1B / 2B scale with 1% / 0.5% / 0.3% active gate entries, an
+# overflow-stress block with a heavier per-token tail, and the pages' own
+# block width for the break-even sweeps.
 WORKLOADS = {
     "tiny": Workload("tiny", 64, 256, 1024, 128, 16, 0.05, 0.0),
     "ffn-0.5b": Workload("ffn-0.5b", 4096, 1024, 4096, 128, 8, 0.01, 0.5),
     "ffn-1b": Workload("ffn-1b", 8192, 1536, 6144, 128, 8, 0.005, 0.5),
     "ffn-2b": Workload("ffn-2b", 16384, 2048, 8192, 256, 16, 0.003, 0.5),
     "ffn-ovf": Workload("ffn-ovf", 16384, 2048, 8192, 128, 4, 0.005, 1.0),
+    # the pages' own FFN block width (hidden 5632 over model width 2048) at
+    # about 28 active neurons per token, the middle of their observed range
+    "ffn-paper": Workload("ffn-paper", 4096, 2048, 5632, 128, 8, 0.005, 0.5),
 }
 
 

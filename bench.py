@@ -141,6 +141,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ffn-0.5b")
     ap.add_argument("--density", type=float, default=None, help="override the target density")
+    ap.add_argument("--M", type=int, default=None,
+                    help="override the token count (decode-like batches)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -172,6 +174,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.density is not None:
         w = w.with_(density=args.density)
+    if args.M is not None:
+        w = w.with_(M=args.M)
     M, K, N, T, C = w.M, w.K, w.N, w.T, w.C
     R_max = M  # room for every row: timing never needs the retry
     d = synth.make_inputs(w)

@@ -129,7 +129,8 @@ def _sample_rows(g, M, C, n_even=32, n_ovf=16, n_heavy=16):
 
 
 @pytest.mark.parametrize("name,dens", [("ffn-0.5b", None), ("ffn-1b", None), ("ffn-2b", None),
-                                       ("ffn-ovf", None), ("ffn-2b", 0.0), ("ffn-2b", 0.05)])
+                                       ("ffn-ovf", None), ("ffn-2b", 0.0), ("ffn-2b", 0.05),
+                                       ("ffn-paper", None)])
 def test_full_size(tw, name, dens):
     w = W[name] if dens is None else W[name].with_(density=dens)
     print(f"case {w}", flush=True)

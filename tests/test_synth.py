@@ -29,7 +29,7 @@ def test_deterministic_and_bias_column():
     assert not np.array_equal(a["x"], c["x"])
 
 
-@pytest.mark.parametrize("name", ["tiny", "ffn-0.5b", "ffn-1b", "ffn-2b", "ffn-ovf"])
+@pytest.mark.parametrize("name", ["tiny", "ffn-0.5b", "ffn-1b", "ffn-2b", "ffn-ovf", "ffn-paper"])
 def test_realized_density(name):
     """Mean active fraction within 5% of the target over all rows (float32
     products are enough for a count); heavy-tailed workloads have rows more
