@@ -23,7 +23,8 @@
 // - The dot product is reduced across the wave with DPP (no LDS), its
 //   product with g is the scalar h_j, and h_j * W_d[j] is added lane-wise.
 // - The four partial y rows are summed in LDS in a fixed order (the result
-//   does not depend on timing) and written once, coalesced.
+//   does not depend on timing) and written once; the staging is laid out so
+//   that neither its stores nor its loads have bank conflicts.
 #include "tw_device.hpp"
 #include "tw_internal.hpp"
 
@@ -41,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
     const float *__restrict__ tw_val,
     const int32_t *__restrict__ tw_idx, const int32_t *__restrict__ tw_cnt,
     float *__restrict__ y) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];  // [kWaves][K] fp32
+    extern __shared__ __attribute__((aligned(16))) char smem[];  // y staging, fp32
     __shared__ int s_off[kThreads + 1];
     __shared__ int s_wtot[kWaves];
 
@@ -162,28 +163,33 @@ __global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
         }
     }
 
+    // y staging, transposed: element (ch, e) of lane l of wave w at float
+    // ((w KCH + ch) 8 + e) 64 + l, so the 64 lanes of a store hit 64
+    // consecutive banks (a lane-contiguous layout, 8 floats per lane, would
+    // put 8 lanes on each bank)
     float *s_y = reinterpret_cast<float *>(smem);
 #pragma unroll
-    for (int ch = 0; ch < KCH; ++ch) {
-        const int q = lane + 64 * ch;
-        if (q < KC) {
-            float *d = s_y + (size_t)wave * K + 8 * q;
+    for (int ch = 0; ch < KCH; ++ch)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) d[e] = yacc[ch][e];
-        }
-    }
+        for (int e = 0; e < 8; ++e) s_y[((wave * KCH + ch) * 8 + e) * 64 + lane] = yacc[ch][e];
     __syncthreads();
-    for (int q = tid; q < 2 * KC; q += kThreads) {
+    // thread i forms the 4 outputs of half (i / 64) % 2 of lane i % 64's
+    // chunk i / 128: consecutive threads read consecutive banks
+    for (int i = tid; i < 128 * KCH; i += kThreads) {
+        const int l = i & 63, half = (i >> 6) & 1, ch = i >> 7;
+        const int q = l + 64 * ch;  // 16-byte chunk of the K-row
+        if (q >= KC) continue;
         float r[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float v = s_y[4 * q + e];
+            const int o = (ch * 8 + 4 * half + e) * 64 + l;
+            float v = s_y[o];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) v += s_y[(size_t)w * K + 4 * q + e];
+            for (int w = 1; w < kWaves; ++w) v += s_y[(size_t)w * KCH * 512 + o];
             r[e] = v;
         }
-        st16(yrow + 4 * q, u32x4{__float_as_uint(r[0]), __float_as_uint(r[1]),
-                                 __float_as_uint(r[2]), __float_as_uint(r[3])});
+        st16(yrow + 8 * q + 4 * half, u32x4{__float_as_uint(r[0]), __float_as_uint(r[1]),
+                                            __float_as_uint(r[2]), __float_as_uint(r[3])});
     }
 }
 
@@ -191,12 +197,12 @@ template <int KCH>
 hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
                     int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
                     const int32_t *tw_cnt, float *y, hipStream_t s) {
-    const size_t lds = (size_t)kWaves * K * sizeof(float);
+    const size_t lds = (size_t)kWaves * KCH * 512 * sizeof(float);  // y staging
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e =
             hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_updown_kernel<KCH>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kWaves * 4096 * 4);
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
