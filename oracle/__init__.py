@@ -16,7 +16,12 @@ integers on small integer matrices, one-hot token rows, the row-wide ELL and
 lossless special cases, exact density 0 and 1, the invariants (each active
 entry appears exactly once, counts sum to the number of non-zeros, the
 sparse evaluation equals the dense one bit for bit), and planted mistakes
-that each of these must catch.
+that each of these must catch.  The hybrid storage of the training forward
+(``hybrid_pack``, ``hybrid_up``, ``hybrid_down``) is pinned the same way: a
+hand-worked fixture (``tests/golden/handworked_hybrid_4x4x8.txt``), integer
+brute force, scipy's CSR rows and numpy products in the lossless case,
+density 0 and 1, and the composed hybrid forward equalling the dense block
+output bit for bit.
 """
 from __future__ import annotations
 
@@ -78,8 +83,15 @@ class Oracle:
         L.tw_oracle_dense_ffn.argtypes = [_D, _D, _D, _D, _int, _int, _int, _D]
         L.tw_oracle_sparse_ffn.argtypes = [_D, _D, _D, _D, _int, _int, _int, _int, _int,
                                            _I, _I, _D, _D]
+        L.tw_oracle_hybrid_pack.argtypes = [_int, _int, _int, _I, _I, _D, _int, _int,
+                                            _I, _I, _D, _U8, _I, _I]
+        L.tw_oracle_hybrid_up.argtypes = [_D, _D, _D, _int, _int, _int, _int, _I, _I, _D,
+                                          _U8, _I, _int, _D, _D, _D, _D, _D]
+        L.tw_oracle_hybrid_down.argtypes = [_D, _int, _int, _int, _int, _I, _I, _D, _U8, _I,
+                                            _int, _D, _D]
         for f in ("tw_oracle_gate", "tw_oracle_pack", "tw_oracle_dense_ffn",
-                  "tw_oracle_sparse_ffn"):
+                  "tw_oracle_sparse_ffn", "tw_oracle_hybrid_pack", "tw_oracle_hybrid_up",
+                  "tw_oracle_hybrid_down"):
             getattr(L, f).restype = None
 
     def threads(self) -> int:
@@ -142,6 +154,82 @@ class Oracle:
         self.lib.tw_oracle_sparse_ffn(_p(x, _D), _p(wg, _D), _p(wu, _D), _p(w_d, _D),
                                       M, K, N, T, C, _p(cnt, _I), _p(idx, _I), _p(val, _D),
                                       _p(y, _D))
+        return y
+
+    # ---------------- hybrid storage of the training forward ----------------
+    def hybrid_pack(self, packed: dict, C: int, P: int, R_max: int) -> dict:
+        """Hybrid storage (sparse rows of capacity P, dense backup) from a
+        TwELL packing ``packed`` (``pack``'s output, or the GPU's arrays with
+        ``cnt``, ``idx`` and ``val``) of capacity C."""
+        cnt = np.ascontiguousarray(packed["cnt"], dtype=np.int32)
+        M, NT = cnt.shape
+        idx = np.ascontiguousarray(packed["idx"], dtype=np.int32)
+        val = np.ascontiguousarray(packed["val"], dtype=np.float64)
+        assert idx.shape == val.shape == (M, NT, C)
+        if P < 1 or R_max < 0:
+            raise ValueError("bad P / R_max")
+        hy_cnt = np.empty(M, dtype=np.int32)
+        hy_idx = np.empty((M, P), dtype=np.int32)
+        hy_val = np.empty((M, P), dtype=np.float64)
+        route = np.empty(M, dtype=np.uint8)
+        bk = np.full(max(R_max, 1), -1, dtype=np.int32)
+        count = np.zeros(1, dtype=np.int32)
+        self.lib.tw_oracle_hybrid_pack(M, NT, C, _p(cnt, _I), _p(idx, _I), _p(val, _D), P, R_max,
+                                       _p(hy_cnt, _I), _p(hy_idx, _I), _p(hy_val, _D),
+                                       _p(route, _U8), _p(bk, _I), _p(count, _I))
+        c = int(count[0])
+        return {"hy_cnt": hy_cnt, "hy_idx": hy_idx, "hy_val": hy_val, "route": route,
+                "bk_rows": bk[: min(c, R_max)].copy(), "bk_count": c, "P": P}
+
+    @staticmethod
+    def _hy_arrays(hy: dict):
+        hy_cnt = np.ascontiguousarray(hy["hy_cnt"], dtype=np.int32)
+        hy_idx = np.ascontiguousarray(hy["hy_idx"], dtype=np.int32)
+        route = np.ascontiguousarray(hy["route"], dtype=np.uint8)
+        bk = np.ascontiguousarray(hy["bk_rows"], dtype=np.int32)
+        if bk.size == 0:
+            bk = np.zeros(1, dtype=np.int32)
+        nbk = min(int(hy["bk_count"]), len(hy["bk_rows"]))
+        return hy_cnt, hy_idx, route, bk, nbk
+
+    def hybrid_up(self, x, wg_t, wu_t, hy: dict) -> dict:
+        """Up projection at the hybrid pattern and the product with the gate:
+        hy_u, hy_h [M][P] for sparse rows (NaN elsewhere); bk_g, bk_u, bk_h
+        [nbk][N] for the backup rows."""
+        x, wg, wu = (widen_bf16(a) for a in (x, wg_t, wu_t))
+        M, K = x.shape
+        N = wg.shape[0]
+        P = hy["hy_idx"].shape[1]
+        hy_cnt, hy_idx, route, bk, nbk = self._hy_arrays(hy)
+        hy_g = np.ascontiguousarray(hy["hy_val"], dtype=np.float64)
+        hy_u = np.full((M, P), np.nan)
+        hy_h = np.full((M, P), np.nan)
+        shp = (max(nbk, 1), N)
+        bk_g, bk_u, bk_h = (np.full(shp, np.nan) for _ in range(3))
+        self.lib.tw_oracle_hybrid_up(_p(x, _D), _p(wg, _D), _p(wu, _D), M, K, N, P,
+                                     _p(hy_cnt, _I), _p(hy_idx, _I), _p(hy_g, _D), _p(route, _U8),
+                                     _p(bk, _I), nbk, _p(hy_u, _D), _p(hy_h, _D), _p(bk_g, _D),
+                                     _p(bk_u, _D), _p(bk_h, _D))
+        return {"hy_u": hy_u, "hy_h": hy_h, "bk_g": bk_g[:nbk], "bk_u": bk_u[:nbk],
+                "bk_h": bk_h[:nbk]}
+
+    def hybrid_down(self, wd, hy: dict, hy_h, bk_h) -> np.ndarray:
+        """y = h W_d from hybrid h: stored entries ``hy_h`` [M][P] of sparse
+        rows, dense rows ``bk_h`` [nbk][N] of the backup.  Rows that are
+        routed to the backup but not on its list stay NaN."""
+        w_d = widen_bf16(wd)
+        N, K = w_d.shape
+        hy_cnt, hy_idx, route, bk, nbk = self._hy_arrays(hy)
+        M, P = hy_idx.shape
+        h = np.ascontiguousarray(hy_h, dtype=np.float64)
+        b = np.ascontiguousarray(bk_h, dtype=np.float64).reshape(-1, N)
+        assert h.shape == (M, P) and b.shape[0] >= nbk
+        if b.shape[0] == 0:
+            b = np.zeros((1, N))
+        y = np.full((M, K), np.nan)
+        self.lib.tw_oracle_hybrid_down(_p(w_d, _D), M, K, N, P, _p(hy_cnt, _I), _p(hy_idx, _I),
+                                       _p(h, _D), _p(route, _U8), _p(bk, _I), nbk, _p(b, _D),
+                                       _p(y, _D))
         return y
 
 

@@ -23,6 +23,13 @@
  *   idx   [M][N/T][C]   TwELL original hidden index (global column j)
  *   val   [M][N/T][C]   TwELL packed value
  *   y     [M][K]        block output
+ * Hybrid storage (training forward), sparse capacity P, backup room R_max:
+ *   hy_cnt [M]          non-zeros of each row (the true count)
+ *   hy_idx [M][P]       original hidden index of each stored entry
+ *   hy_val [M][P]       stored gate value (hy_u, hy_h: up and product values)
+ *   route  [M]          1 if the row lives in the dense backup, else 0
+ *   bk_rows [R_max]     backup rows in ascending order
+ *   bk_g, bk_u, bk_h [R_max][N]  dense gate, up and product rows of the backup
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -190,6 +197,143 @@ void tw_oracle_sparse_ffn(const double *x, const double *wg_t, const double *wu_
                 for (int k = 0; k < K; ++k)
                     ym[k] += h * wdj[k];
             }
+        }
+    }
+}
+
+/* Hybrid storage of the gate activation, section 3-6 (compact ELL-like rows
+ * for most tokens, a dense backup for the few heavy ones, a binary routing
+ * vector saying which holds each row) with the static capacities of section
+ * 4-3 (at most P stored non-zeros per sparse row, at most R_max backup rows,
+ * overflow reported for a retry with more room).  It is built from a TwELL
+ * packing, the order of the training pipeline in section 2-2 (TwELL gate,
+ * then hybrid storage).
+ *
+ * Readings where the page is silent: the row's non-zero count is the sum of
+ * its TwELL tile counts; a row goes to the backup when that count exceeds P
+ * or when one of its tiles exceeded the TwELL capacity C (its packing then
+ * lacks entries); a sparse row stores its entries in ascending column order
+ * (tiles ascending, slots ascending), the row-wide ELL of section 3-3 with
+ * capacity P; unused slots get idx -1, val 0.  hy_cnt is the row's true
+ * count for every row.  bk_rows lists the backup rows in ascending order, at
+ * most R_max of them, and *bk_count receives their true number. */
+void tw_oracle_hybrid_pack(int M, int NT, int C, const int32_t *cnt, const int32_t *idx,
+                           const double *val, int P, int R_max,
+                           int32_t *hy_cnt, int32_t *hy_idx, double *hy_val,
+                           uint8_t *route, int32_t *bk_rows, int32_t *bk_count)
+{
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int m = 0; m < M; ++m) {
+        int nnz = 0, over = 0;
+        for (int t = 0; t < NT; ++t) {
+            const int c = cnt[(size_t)m * NT + t];
+            nnz += c;
+            if (c > C)
+                over = 1;
+        }
+        hy_cnt[m] = nnz;
+        route[m] = (uint8_t)(over || nnz > P);
+        for (int s = 0; s < P; ++s) {
+            hy_idx[(size_t)m * P + s] = -1;
+            hy_val[(size_t)m * P + s] = 0.0;
+        }
+        if (route[m])
+            continue;
+        int n = 0;
+        for (int t = 0; t < NT; ++t) {
+            const size_t tile = (size_t)m * NT + t;
+            for (int s = 0; s < cnt[tile]; ++s) {
+                hy_idx[(size_t)m * P + n] = idx[tile * C + s];
+                hy_val[(size_t)m * P + n] = val[tile * C + s];
+                ++n;
+            }
+        }
+    }
+    int r = 0;
+    for (int m = 0; m < M; ++m) {
+        if (route[m]) {
+            if (r < R_max)
+                bk_rows[r] = m;
+            ++r;
+        }
+    }
+    *bk_count = r;
+}
+
+/* Up projection of the training forward in hybrid form: the dense-to-hybrid
+ * product of section 3-7 (dense x times dense W_u, evaluated only where the
+ * stored gate is non-zero), multiplied elementwise by the gate (section 1-1,
+ * h = h_u h_g).  Sparse rows: for each stored entry s (column j, gate g),
+ * hy_u = x_m . W_u[:, j] and hy_h = hy_u g.  The first nbk backup rows
+ * (m = bk_rows[r]) are recomputed densely from x (section 3-6: heavy rows are
+ * kept whole, not clipped): bk_g[r][j] = ReLU(x_m . W_g[:, j]),
+ * bk_u[r][j] = x_m . W_u[:, j], bk_h = bk_u bk_g, for every j. */
+void tw_oracle_hybrid_up(const double *x, const double *wg_t, const double *wu_t,
+                         int M, int K, int N, int P,
+                         const int32_t *hy_cnt, const int32_t *hy_idx, const double *hy_g,
+                         const uint8_t *route, const int32_t *bk_rows, int nbk,
+                         double *hy_u, double *hy_h, double *bk_g, double *bk_u, double *bk_h)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; ++m) {
+        if (route[m])
+            continue;
+        const double *xm = x + (size_t)m * K;
+        for (int s = 0; s < hy_cnt[m]; ++s) {
+            const size_t e = (size_t)m * P + s;
+            const double u = dot(xm, wu_t + (size_t)hy_idx[e] * K, K);
+            hy_u[e] = u;
+            hy_h[e] = u * hy_g[e];
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nbk; ++r) {
+        const double *xm = x + (size_t)bk_rows[r] * K;
+        for (int j = 0; j < N; ++j) {
+            const size_t e = (size_t)r * N + j;
+            const double g = relu(dot(xm, wg_t + (size_t)j * K, K));
+            const double u = dot(xm, wu_t + (size_t)j * K, K);
+            bk_g[e] = g;
+            bk_u[e] = u;
+            bk_h[e] = u * g;
+        }
+    }
+}
+
+/* Down projection of the training forward: the hybrid-to-dense product of
+ * section 3-7, y = h W_d with h in hybrid form.  A sparse row sums its
+ * stored entries, y_m = sum over s of hy_h[s] W_d[hy_idx[s], :] (s
+ * ascending); backup row r sums its dense row, y_m = sum over j ascending of
+ * bk_h[r][j] W_d[j, :], for m = bk_rows[r], r < nbk.  Rows routed to the
+ * backup but past nbk are not written. */
+void tw_oracle_hybrid_down(const double *wd, int M, int K, int N, int P,
+                           const int32_t *hy_cnt, const int32_t *hy_idx, const double *hy_h,
+                           const uint8_t *route, const int32_t *bk_rows, int nbk,
+                           const double *bk_h, double *y)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; ++m) {
+        if (route[m])
+            continue;
+        double *ym = y + (size_t)m * K;
+        for (int k = 0; k < K; ++k)
+            ym[k] = 0.0;
+        for (int s = 0; s < hy_cnt[m]; ++s) {
+            const size_t e = (size_t)m * P + s;
+            const double *wdj = wd + (size_t)hy_idx[e] * K;
+            for (int k = 0; k < K; ++k)
+                ym[k] += hy_h[e] * wdj[k];
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nbk; ++r) {
+        double *ym = y + (size_t)bk_rows[r] * K;
+        for (int k = 0; k < K; ++k)
+            ym[k] = 0.0;
+        for (int j = 0; j < N; ++j) {
+            const double *wdj = wd + (size_t)j * K;
+            for (int k = 0; k < K; ++k)
+                ym[k] += bk_h[(size_t)r * N + j] * wdj[k];
         }
     }
 }

@@ -317,5 +317,236 @@ def pin_density_extremes(orc) -> None:
         "overflow beyond R_max is reported for retry"
 
 
+# --------------------------------------------------------------------------
+# hybrid storage of the training forward (sections 3-6, 3-7, 4-3)
+# --------------------------------------------------------------------------
+HYBRID_GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                             "handworked_hybrid_4x4x8.txt")
+
+
+def load_hybrid_golden(path: str = HYBRID_GOLDEN) -> dict:
+    """Parse the hand-worked hybrid fixture into its cases and value tables."""
+    out = {"cases": [], "up": {}, "backup_g": {}, "backup_u": {}, "backup_h": {}}
+    case = None
+    with open(path) as f:
+        for raw in f:
+            s = raw.split("#", 1)[0].strip()
+            if not s:
+                continue
+            head = s.split()
+            key = head[0]
+            if key == "hy_cnt":
+                out["hy_cnt"] = [int(v) for v in head[1:]]
+            elif key == "case":
+                case = {"P": int(head[2]), "R_max": int(head[4]), "sparse": {}}
+                out["cases"].append(case)
+            elif key in ("route", "bk_rows"):
+                case[key] = [int(v) for v in head[1:]]
+            elif key == "bk_count":
+                case[key] = int(head[1])
+            else:
+                row = int(head[1])
+                body = s.split(":", 1)[1].strip()
+                items = [[int(v) for v in e.split()] for e in body.split(",")] if body else []
+                if key == "sparse":
+                    case["sparse"][row] = items
+                elif key == "up":
+                    out["up"][row] = items
+                else:
+                    out[key][row] = items[0]
+    return out
+
+
+def pin_hybrid_golden(orc) -> None:
+    """Hand-worked hybrid storage, up values and output of the 4x4x8 example."""
+    g = load_golden()
+    hg = load_hybrid_golden()
+    T, C, M = g["T"], g["C"], g["M"]
+    x, wg, wu, wd = (_bits(g[k]) for k in ("x", "wg_t", "wu_t", "wd"))
+    p = orc.pack(orc.gate(x, wg), T, C, R_max=M)
+    for case in hg["cases"]:
+        P, R_max = case["P"], case["R_max"]
+        hy = orc.hybrid_pack(p, C, P, R_max)
+        tag = f"P={P} R_max={R_max}"
+        assert list(hy["hy_cnt"]) == hg["hy_cnt"], "hy_cnt " + tag
+        assert list(hy["route"]) == case["route"], "route " + tag
+        assert list(hy["bk_rows"]) == case["bk_rows"], "bk_rows " + tag
+        assert hy["bk_count"] == case["bk_count"], "bk_count " + tag
+        for m, items in case["sparse"].items():
+            n = len(items)
+            assert hy["hy_cnt"][m] == n, "sparse count " + tag
+            assert [int(v) for v in hy["hy_idx"][m, :n]] == [e[0] for e in items], "idx " + tag
+            assert [float(v) for v in hy["hy_val"][m, :n]] == [e[1] for e in items], "val " + tag
+        if R_max < case["bk_count"]:
+            continue
+        up = orc.hybrid_up(x, wg, wu, hy)
+        for m, items in hg["up"].items():
+            if hy["route"][m]:
+                continue
+            n = len(items)
+            assert [int(v) for v in hy["hy_idx"][m, :n]] == [e[0] for e in items], "up idx " + tag
+            assert list(up["hy_u"][m, :n]) == [e[1] for e in items], "hy_u " + tag
+            assert list(up["hy_h"][m, :n]) == [e[2] for e in items], "hy_h " + tag
+        for r, m in enumerate(hy["bk_rows"]):
+            for key in ("bk_g", "bk_u", "bk_h"):
+                want = hg["backup_" + key[3:]][int(m)]
+                assert list(up[key][r]) == want, f"{key} row {m} " + tag
+        y = orc.hybrid_down(wd, hy, up["hy_h"], up["bk_h"])
+        assert np.array_equal(y, g["y"].astype(np.float64)), "hybrid y " + tag
+
+
+def _brute_hybrid(cnt, slots, C, P, R_max):
+    """Hybrid storage from a TwELL packing given as Python lists."""
+    M = len(cnt)
+    hy_cnt, route, ell = [], [], []
+    for m in range(M):
+        n = sum(cnt[m])
+        heavy = n > P or any(c > C for c in cnt[m])
+        hy_cnt.append(n)
+        route.append(1 if heavy else 0)
+        ell.append([] if heavy else [e for t in range(len(cnt[m])) for e in slots[m][t]])
+    bk = [m for m in range(M) if route[m]]
+    return hy_cnt, route, ell, bk[:R_max], len(bk)
+
+
+def pin_hybrid_bruteforce(orc, cases: int = 40, seed: int = 4321) -> None:
+    """Random small integer problems: hybrid storage, up values at the stored
+    entries, dense backup rows and y, exact against Python integers."""
+    rnd = random.Random(seed)
+    for _ in range(cases):
+        T = rnd.choice([1, 2, 3, 4])
+        NT = rnd.randint(1, 3)
+        N = T * NT
+        K = rnd.randint(1, max(1, N))
+        M = rnd.randint(1, 6)
+        C = rnd.randint(1, T)
+        P = rnd.randint(1, N)
+        draw = lambda r, c: [[rnd.randint(-3, 3) for _ in range(c)] for _ in range(r)]
+        x, wg, wu, wd = draw(M, K), draw(N, K), draw(N, K), draw(N, K)
+        z, cnt, slots, _, _, y = _brute(x, wg, wu, wd, T, C, M)
+        hy_cnt, route, ell, _, n_bk = _brute_hybrid(cnt, slots, C, P, M)
+        R_max = rnd.randint(n_bk, M) if rnd.random() < 0.7 else rnd.randint(0, M)
+        bk = [m for m in range(M) if route[m]][:R_max]
+        bx, bg, bu, bd = (_bits(a) for a in (x, wg, wu, wd))
+        p = orc.pack(orc.gate(bx, bg), T, C, M)
+        hy = orc.hybrid_pack(p, C, P, R_max)
+        assert list(hy["hy_cnt"]) == hy_cnt and list(hy["route"]) == route, "routing"
+        assert list(hy["bk_rows"]) == bk and hy["bk_count"] == n_bk, "backup list"
+        for m in range(M):
+            if route[m]:
+                continue
+            n = len(ell[m])
+            assert [int(v) for v in hy["hy_idx"][m, :n]] == [j for j, _ in ell[m]], "idx"
+            assert [float(v) for v in hy["hy_val"][m, :n]] == [v for _, v in ell[m]], "val"
+        up = orc.hybrid_up(bx, bg, bu, hy)
+        u = [[sum(x[m][k] * wu[j][k] for k in range(K)) for j in range(N)] for m in range(M)]
+        for m in range(M):
+            if route[m]:
+                continue
+            for s, (j, gv) in enumerate(ell[m]):
+                assert up["hy_u"][m, s] == u[m][j] and up["hy_h"][m, s] == u[m][j] * gv, "up"
+        for r, m in enumerate(bk):
+            gr = [v if v > 0 else 0 for v in z[m]]
+            assert list(up["bk_g"][r]) == gr and list(up["bk_u"][r]) == u[m], "backup g/u"
+            assert list(up["bk_h"][r]) == [a * b for a, b in zip(gr, u[m])], "backup h"
+        yh = orc.hybrid_down(bd, hy, up["hy_h"], up["bk_h"])
+        for m in range(M):
+            if route[m] and m not in bk:
+                assert np.all(np.isnan(yh[m])), "rows past the backup room stay unwritten"
+            else:
+                assert list(yh[m]) == y[m], "hybrid y"
+
+
+def pin_hybrid_library(orc) -> None:
+    """With room for every entry (P = N, lossless TwELL C = T) no row is
+    heavy and the sparse store is the row-wide ELL of section 3-3, which holds
+    exactly scipy's CSR rows of ReLU(z); the up values at the stored entries
+    and the output agree with numpy's float64 products to rounding."""
+    import scipy.sparse as sp
+
+    w, d = _tiny(M=24)
+    x, wu, wd = (orc_widen(a) for a in (d["x"], d["wu_t"], d["wd"]))
+    z = orc.gate(d["x"], d["wg_t"])
+    g = np.where(z > 0.0, z, 0.0)
+    p = orc.pack(z, w.T, w.T, w.M)
+    hy = orc.hybrid_pack(p, w.T, w.N, w.M)
+    assert not hy["route"].any() and hy["bk_count"] == 0, "nothing is heavy"
+    csr = sp.csr_matrix(g)
+    csr.sort_indices()
+    assert np.array_equal(hy["hy_cnt"], np.diff(csr.indptr)), "counts vs CSR"
+    up = orc.hybrid_up(d["x"], d["wg_t"], d["wu_t"], hy)
+    u_np = x @ wu.T
+    bound_u = 4 * w.K * 2.0 ** -53 * (np.abs(x) @ np.abs(wu).T) + 1e-300
+    h_dense = np.zeros((w.M, w.N))
+    for m in range(w.M):
+        a, b = csr.indptr[m], csr.indptr[m + 1]
+        ids = csr.indices[a:b]
+        assert np.array_equal(hy["hy_idx"][m, :b - a], ids), "idx vs CSR"
+        assert np.array_equal(hy["hy_val"][m, :b - a], csr.data[a:b]), "val vs CSR"
+        assert np.all(np.abs(up["hy_u"][m, :b - a] - u_np[m, ids]) <= bound_u[m, ids]), "u"
+        h_dense[m, ids] = up["hy_h"][m, :b - a]
+    y = orc.hybrid_down(d["wd"], hy, up["hy_h"], up["bk_h"])
+    y_np = h_dense @ wd
+    scale = np.abs(h_dense) @ np.abs(wd) + 1e-300
+    assert np.all(np.abs(y - y_np) <= 1e-12 * scale), "y vs numpy"
+
+
+def pin_hybrid_invariants(orc) -> None:
+    """Generator inputs at several capacities: each active entry is stored
+    exactly once (a sparse slot, or its row in the backup); the routing is the
+    stated rule; stored indices ascend; the composed hybrid forward equals the
+    oracle's dense block output bit for bit (same dot products, same
+    ascending order, inactive terms only add signed zeros)."""
+    for C, P, R_max in ((16, 128, 64), (12, 64, 64), (4, 40, 64), (16, 48, 64), (16, 48, 3)):
+        w, d = _tiny(C=C)
+        z = orc.gate(d["x"], d["wg_t"])
+        p = orc.pack(z, w.T, C, w.M)
+        hy = orc.hybrid_pack(p, C, P, R_max)
+        act = z > 0.0
+        nnz = act.sum(axis=1)
+        heavy = (nnz > P) | (p["cnt"] > C).any(axis=1)
+        assert np.array_equal(hy["hy_cnt"], nnz), "true counts"
+        assert np.array_equal(hy["route"].astype(bool), heavy), "routing rule"
+        rows = np.nonzero(heavy)[0]
+        assert hy["bk_count"] == len(rows) and np.array_equal(hy["bk_rows"], rows[:R_max])
+        for m in np.nonzero(~heavy)[0]:
+            n = nnz[m]
+            ids = hy["hy_idx"][m, :n]
+            assert np.array_equal(ids, np.nonzero(act[m])[0]), "stored entries"
+            assert np.array_equal(hy["hy_val"][m, :n], z[m, ids]), "stored values"
+            assert np.all(hy["hy_idx"][m, n:] == -1), "unused slots"
+        up = orc.hybrid_up(d["x"], d["wg_t"], d["wu_t"], hy)
+        y = orc.hybrid_down(d["wd"], hy, up["hy_h"], up["bk_h"])
+        yd = orc.dense_ffn(d["x"], d["wg_t"], d["wu_t"], d["wd"])
+        done = ~heavy
+        done[hy["bk_rows"]] = True
+        assert np.array_equal(y[done].view(np.uint64), yd[done].view(np.uint64)), \
+            "hybrid forward == dense bitwise"
+        assert np.all(np.isnan(y[~done])), "rows past the backup room are not written"
+
+
+def pin_hybrid_extremes(orc) -> None:
+    """Density 0: every row sparse and empty, y = 0.  Density 1 with P < N:
+    every row heavy; with a small backup room the true count is reported."""
+    w, d = _tiny(density=0.0)
+    p = orc.pack(orc.gate(d["x"], d["wg_t"]), w.T, w.C, w.M)
+    hy = orc.hybrid_pack(p, w.C, 128, w.M // 8)
+    assert not hy["hy_cnt"].any() and not hy["route"].any() and hy["bk_count"] == 0
+    up = orc.hybrid_up(d["x"], d["wg_t"], d["wu_t"], hy)
+    y = orc.hybrid_down(d["wd"], hy, up["hy_h"], up["bk_h"])
+    assert not y.any(), "density 0 output"
+
+    w, d = _tiny(density=1.0, C=128)
+    p = orc.pack(orc.gate(d["x"], d["wg_t"]), w.T, w.C, w.M)
+    hy = orc.hybrid_pack(p, w.C, 128, w.M // 8)
+    assert np.all(hy["hy_cnt"] == w.N) and hy["route"].all(), "density 1: every row heavy"
+    assert hy["bk_count"] == w.M and np.array_equal(hy["bk_rows"], np.arange(w.M // 8)), \
+        "backup room exceeded: retry signalled"
+    hy = orc.hybrid_pack(p, w.C, w.N, w.M)
+    assert not hy["route"].any() and np.all(hy["hy_idx"] == np.arange(w.N)[None]), \
+        "density 1, P = N: every row sparse and full"
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_csr_library, pin_numpy_dense, pin_onehot,
-            pin_invariants, pin_density_extremes]
+            pin_invariants, pin_density_extremes, pin_hybrid_golden, pin_hybrid_bruteforce,
+            pin_hybrid_library, pin_hybrid_invariants, pin_hybrid_extremes]

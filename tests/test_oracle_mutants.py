@@ -42,16 +42,46 @@ MUTANTS = [
      "for (int k = 0; k < K; ++k)\n            ym[k] += h * wd[(size_t)k * N + j];\n    }\n}"),
     ("gate row stride", "z[(size_t)m * N + j] = dot(x + (size_t)m * K, wg_t + (size_t)j * K, K);",
      "z[(size_t)m * N + j] = dot(x + (size_t)m, wg_t + (size_t)j * K, K);"),
-    ("sparse drops last slot", "for (int s = 0; s < cnt[tile]; ++s) {",
-     "for (int s = 0; s + 1 < cnt[tile]; ++s) {"),
+    ("sparse drops last slot", "for (int s = 0; s < cnt[tile]; ++s) {\n                const int j",
+     "for (int s = 0; s + 1 < cnt[tile]; ++s) {\n                const int j"),
     ("sparse ignores gate value", "const double g = val[tile * C + s];",
      "const double g = 1.0;"),
     # overflow rows evaluated from their truncated packing instead of the
     # dense backup (the slot loop is clamped so the mutant stays in bounds)
     ("no dense backup", ["if (over) {\n            dense_row", "if (0) {\n            dense_row"],
-     ["for (int s = 0; s < cnt[tile]; ++s) {", "for (int s = 0; s < cnt[tile] && s < C; ++s) {"]),
+     ["for (int s = 0; s < cnt[tile]; ++s) {\n                const int j",
+      "for (int s = 0; s < cnt[tile] && s < C; ++s) {\n                const int j"]),
     ("sparse sign flip", "const double h = u * g;\n                const double *wdj",
      "const double h = -u * g;\n                const double *wdj"),
+    # hybrid storage (the copy loop is clamped where a mutant could read past
+    # a tile's slots)
+    ("hybrid ignores tile overflow",
+     ["route[m] = (uint8_t)(over || nnz > P);", "route[m] = (uint8_t)(nnz > P);"],
+     ["for (int s = 0; s < cnt[tile]; ++s) {\n                hy_idx",
+      "for (int s = 0; s < cnt[tile] && s < C; ++s) {\n                hy_idx"]),
+    ("hybrid heavy at capacity", "route[m] = (uint8_t)(over || nnz > P);",
+     "route[m] = (uint8_t)(over || nnz >= P);"),
+    ("hybrid count clipped", "hy_cnt[m] = nnz;", "hy_cnt[m] = nnz < P ? nnz : P;"),
+    ("hybrid slots restart per tile",
+     "hy_idx[(size_t)m * P + n] = idx[tile * C + s];\n                hy_val[(size_t)m * P + n]",
+     "hy_idx[(size_t)m * P + s] = idx[tile * C + s];\n                hy_val[(size_t)m * P + s]"),
+    ("backup list descending", "for (int m = 0; m < M; ++m) {\n        if (route[m]) {",
+     "for (int m = M - 1; m >= 0; --m) {\n        if (route[m]) {"),
+    ("backup count clipped", "*bk_count = r;", "*bk_count = r < R_max ? r : R_max;"),
+    ("hybrid up uses gate weights", "const double u = dot(xm, wu_t + (size_t)hy_idx[e] * K, K);",
+     "const double u = dot(xm, wg_t + (size_t)hy_idx[e] * K, K);"),
+    ("hybrid product ignores gate", "hy_h[e] = u * hy_g[e];", "hy_h[e] = u;"),
+    ("backup gate without ReLU",
+     "const double g = relu(dot(xm, wg_t + (size_t)j * K, K));\n            const double u = dot(xm, wu_t + (size_t)j * K, K);\n            bk_g[e] = g;",
+     "const double g = dot(xm, wg_t + (size_t)j * K, K);\n            const double u = dot(xm, wu_t + (size_t)j * K, K);\n            bk_g[e] = g;"),
+    ("backup reads x by slot", "const double *xm = x + (size_t)bk_rows[r] * K;",
+     "const double *xm = x + (size_t)r * K;"),
+    ("hybrid down drops last entry",
+     "for (int s = 0; s < hy_cnt[m]; ++s) {\n            const size_t e = (size_t)m * P + s;\n            const double *wdj",
+     "for (int s = 0; s + 1 < hy_cnt[m]; ++s) {\n            const size_t e = (size_t)m * P + s;\n            const double *wdj"),
+    ("hybrid down ignores h", "ym[k] += hy_h[e] * wdj[k];", "ym[k] += wdj[k];"),
+    ("backup output to slot row", "double *ym = y + (size_t)bk_rows[r] * K;",
+     "double *ym = y + (size_t)r * K;"),
 ]
 
 
