@@ -17,7 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libtw.so")
 
-SOURCES = ["gate_twell.hip", "pack_dense.hip", "sparse_updown.hip", "dense_ffn.hip", "tw_api.cpp"]
+SOURCES = ["gate_twell.hip", "pack_dense.hip", "sparse_updown.hip", "dense_ffn.hip", "hybrid.hip",
+           "tw_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -52,11 +52,14 @@ struct GU {
     static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "each load row group in one operand");
 };
 
-template <int BM, int BN, int WM, int WN, int S>
+// KEEP: also store bf16(ReLU(g)) and bf16(u) where g_out / u_out are given
+// (the dense backup rows of the hybrid training storage keep both).
+template <int BM, int BN, int WM, int WN, int S, bool KEEP>
 __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t,
     const uint16_t *__restrict__ wu_t, int K, int N, const int32_t *__restrict__ rowlist,
-    const int32_t *__restrict__ count, int R_cap, int xrows, uint16_t *__restrict__ h) {
+    const int32_t *__restrict__ count, int R_cap, int xrows, uint16_t *__restrict__ h,
+    uint16_t *__restrict__ g_out, uint16_t *__restrict__ u_out) {
     using P = GU<BM, BN, WM, WN, S>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -160,10 +163,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                 if (r < rows) {
 #pragma unroll
                     for (int b = 0; b < P::FB; ++b) {
-                        const float g = ag[a][b][i];
-                        const float hv = (g > 0.0f ? g : 0.0f) * au[a][b][i];
-                        h[(size_t)r * N + n0 + wn * P::TN + b * 32 + l32] =
-                            (uint16_t)f32_to_bf16(hv);
+                        const float g = ag[a][b][i] > 0.0f ? ag[a][b][i] : 0.0f;
+                        const float u = au[a][b][i];
+                        const size_t o = (size_t)r * N + n0 + wn * P::TN + b * 32 + l32;
+                        h[o] = (uint16_t)f32_to_bf16(g * u);
+                        if constexpr (KEEP) {
+                            if (g_out) g_out[o] = (uint16_t)f32_to_bf16(g);
+                            if (u_out) u_out[o] = (uint16_t)f32_to_bf16(u);
+                        }
                     }
                 }
             }
@@ -381,10 +388,10 @@ hipError_t set_lds(F *kernel, int bytes, bool &done) {
 }
 
 // A kernel instantiation with its shape constants.
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, bool KEEP = false>
 struct GuCfg : GU<BM, BN, WM, WN, S> {
     static constexpr int BM_ = BM, BN_ = BN;
-    static constexpr auto kernel = &gateup_kernel<BM, BN, WM, WN, S>;
+    static constexpr auto kernel = &gateup_kernel<BM, BN, WM, WN, S, KEEP>;
 };
 template <int BM, int BN, int WM, int WN, int S>
 struct DnCfg : DN<BM, BN, WM, WN, S> {
@@ -396,6 +403,7 @@ struct DnCfg : DN<BM, BN, WM, WN, S> {
 // tiles do little matrix work per stage, so they keep more stages in flight)
 using GuDense = GuCfg<256, 128, 4, 2, 4>;
 using GuRows = GuCfg<128, 128, 2, 4, 4>;
+using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, true>;
 using DnDense = DnCfg<128, 128, 2, 2, 4>;
 using DnRows = DnCfg<128, 128, 2, 4, 6>;
 constexpr int kSplitGrid = 256;  // work items of the split down GEMM
@@ -419,15 +427,31 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
         const int tiles = (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_);
         const int grid = tiles < 256 ? tiles : 256;
         hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
-                           wu_t, K, N, rowlist, count, R_cap, M, h);
+                           wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr);
     } else {
         static bool attr = false;
         hipError_t e = set_lds(GuDense::kernel, GuDense::LDS, attr);
         if (e != hipSuccess) return e;
         const int grid = (R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_);
         hipLaunchKernelGGL(GuDense::kernel, dim3(grid), dim3(GuDense::NTH), GuDense::LDS, s, x,
-                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h);
+                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,
+                              const uint16_t *wu_t, int K, int N, const int32_t *rowlist,
+                              const int32_t *count, int R_cap, uint16_t *h, uint16_t *g_out,
+                              uint16_t *u_out, hipStream_t s) {
+    if (!g_out && !u_out) return launch_gateup(x, M, wg_t, wu_t, K, N, rowlist, count, R_cap, h, s);
+    if (R_cap <= 0) return hipSuccess;
+    static bool attr = false;
+    hipError_t e = set_lds(GuRowsKeep::kernel, GuRowsKeep::LDS, attr);
+    if (e != hipSuccess) return e;
+    const int tiles = (R_cap + GuRowsKeep::BM_ - 1) / GuRowsKeep::BM_ * (N / GuRowsKeep::BN_);
+    const int grid = tiles < 256 ? tiles : 256;
+    hipLaunchKernelGGL(GuRowsKeep::kernel, dim3(grid), dim3(GuRowsKeep::NTH), GuRowsKeep::LDS, s,
+                       x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, g_out, u_out);
     return hipGetLastError();
 }
 

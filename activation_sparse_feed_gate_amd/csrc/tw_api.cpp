@@ -26,6 +26,12 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Shape checks shared by the TwELL entry points.
+#define TW_TRY_SHAPE(expr)                \
+    do {                                  \
+        tw_status st_ = (expr);           \
+        if (st_ != TW_OK) return st_;     \
+    } while (0)
+
 tw_status check_shape(int M, int K, int N, int T, int C, int R_max) {
     if (M < 0 || K <= 0 || N <= 0) return fail(TW_EINVAL, "M=%d K=%d N=%d: need M >= 0, K, N > 0", M, K, N);
     if (T != 128 && T != 256) return fail(TW_EUNSUPPORTED, "tile width T=%d: supported 128, 256", T);
@@ -37,6 +43,21 @@ tw_status check_shape(int M, int K, int N, int T, int C, int R_max) {
     if (R_max < 0 || R_max > M) return fail(TW_EINVAL, "R_max=%d outside [0, M=%d]", R_max, M);
     if ((int64_t)M * K >= (int64_t(1) << 31))
         return fail(TW_EUNSUPPORTED, "M*K=%lld: x must stay under 4 GiB", (long long)M * K);
+    return TW_OK;
+}
+
+// Shape checks of the hybrid entry points: the TwELL limits, the dense
+// kernels' (N a multiple of 128, each weight matrix and the backup rows
+// under 4 GiB) and the sparse row capacity.
+tw_status check_hybrid(int M, int K, int N, int T, int C, int P, int R_max) {
+    TW_TRY_SHAPE(check_shape(M, K, N, T, C, R_max));
+    if (N % 128) return fail(TW_EUNSUPPORTED, "N=%d: must be a multiple of 128", N);
+    if ((int64_t)N * K >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "N*K=%lld: weights must stay under 4 GiB", (long long)N * K);
+    if ((int64_t)R_max * N >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "R_max*N=%lld: backup rows must stay under 4 GiB",
+                    (long long)R_max * N);
+    if (P < 1 || P > N) return fail(TW_EINVAL, "sparse row capacity P=%d outside [1, N=%d]", P, N);
     return TW_OK;
 }
 
@@ -272,6 +293,115 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu
     TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, nullptr, s),
                     "dense down launch"));
     TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+size_t tw_hybrid_down_workspace_bytes(int R_max) {
+    if (R_max <= 0) return 0;
+    return tw::split_partial_bytes() + 256;
+}
+
+tw_status tw_hybrid_pack(int M, int N, int T, int C, const float *tw_val, const int32_t *tw_idx,
+                         const int32_t *tw_cnt, int P, float *hy_val, int32_t *hy_idx,
+                         int32_t *hy_cnt, uint8_t *route, int32_t *bk_rows, int32_t *bk_count,
+                         int R_max, void *stream, void *const *events) {
+    TW_TRY(check_hybrid(M, 128, N, T, C, P, R_max));
+    TW_NEED_M(tw_val);
+    TW_NEED_M(tw_idx);
+    TW_NEED_M(tw_cnt);
+    TW_NEED_M(hy_val);
+    TW_NEED_M(hy_idx);
+    TW_NEED_M(hy_cnt);
+    TW_NEED_M(route);
+    TW_NEED(bk_rows);
+    TW_NEED(bk_count);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_hybrid_pack(tw_val, tw_idx, tw_cnt, M, N, T, C, P, hy_val, hy_idx,
+                                           hy_cnt, route, s),
+                    "hybrid pack launch"));
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_route_compact(route, M, R_max, bk_rows, bk_count, s),
+                    "route compaction launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+tw_status tw_hybrid_up(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t, int M,
+                       int K, int N, int P, const float *hy_g, const int32_t *hy_idx,
+                       const int32_t *hy_cnt, const uint8_t *route, const int32_t *bk_rows,
+                       const int32_t *bk_count, int R_max, float *hy_u, float *hy_h,
+                       uint16_t *bk_g, uint16_t *bk_u, uint16_t *bk_h, void *stream,
+                       void *const *events) {
+    TW_TRY(check_hybrid(M, K, N, 128, 1, P, R_max));
+    TW_NEED_M(x);
+    TW_NEED(wg_t);
+    TW_NEED(wu_t);
+    TW_NEED_M(hy_g);
+    TW_NEED_M(hy_idx);
+    TW_NEED_M(hy_cnt);
+    TW_NEED_M(route);
+    TW_NEED(bk_rows);
+    TW_NEED(bk_count);
+    TW_NEED_M(hy_h);
+    if (hy_u && !aligned16(hy_u)) return fail(TW_EINVAL, "hy_u is not 16-byte aligned");
+    if (R_max > 0) TW_NEED(bk_h);
+    if (bk_g && !aligned16(bk_g)) return fail(TW_EINVAL, "bk_g is not 16-byte aligned");
+    if (bk_u && !aligned16(bk_u)) return fail(TW_EINVAL, "bk_u is not 16-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_hybrid_up(x, wu_t, M, K, N, P, hy_g, hy_idx, hy_cnt, route, hy_u,
+                                         hy_h, s),
+                    "hybrid up launch"));
+    TW_TRY(record(events, 1, s));
+    if (R_max > 0)
+        TW_TRY(launched(tw::launch_gateup_keep(x, M, wg_t, wu_t, K, N, bk_rows, bk_count, R_max,
+                                               bk_h, bk_g, bk_u, s),
+                        "backup gate+up launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+tw_status tw_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const float *hy_h,
+                         const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                         const int32_t *bk_rows, const int32_t *bk_count, int R_max,
+                         const uint16_t *bk_h, float *y, void *ws, size_t ws_bytes, void *stream,
+                         void *const *events) {
+    TW_TRY(check_hybrid(M, K, N, 128, 1, P, R_max));
+    TW_NEED(wd);
+    TW_NEED_M(hy_h);
+    TW_NEED_M(hy_idx);
+    TW_NEED_M(hy_cnt);
+    TW_NEED_M(route);
+    TW_NEED(bk_rows);
+    TW_NEED(bk_count);
+    TW_NEED_M(y);
+    const size_t need = tw_hybrid_down_workspace_bytes(R_max);
+    if (R_max > 0) {
+        TW_NEED(bk_h);
+        TW_NEED(ws);
+    }
+    if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_hybrid_down(wd, M, K, N, P, hy_h, hy_idx, hy_cnt, route, y, s),
+                    "hybrid down launch"));
+    TW_TRY(record(events, 1, s));
+    if (R_max > 0) {
+        float *partial = static_cast<float *>(ws);
+        TW_TRY(launched(tw::launch_down(bk_h, wd, K, N, bk_rows, bk_count, R_max, y, partial, s),
+                        "backup down launch"));
+        TW_TRY(record(events, 2, s));
+        TW_TRY(launched(tw::launch_split_reduce(partial, bk_rows, bk_count, R_max, K, N, y, s),
+                        "backup split-reduce launch"));
+        TW_TRY(record(events, 3, s));
+    } else {
+        TW_TRY(record(events, 2, s));
+        TW_TRY(record(events, 3, s));
+    }
     return TW_OK;
 }
 

@@ -45,6 +45,14 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
                          int K, int N, const int32_t *rowlist, const int32_t *count,
                          int R_cap, uint16_t *h, hipStream_t s);
 
+// launch_gateup over a row list that also stores g_out[r][n] =
+// bf16(ReLU(x_r . wg_t[n])) and u_out[r][n] = bf16(x_r . wu_t[n]) where
+// those are non-null.
+hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,
+                              const uint16_t *wu_t, int K, int N, const int32_t *rowlist,
+                              const int32_t *count, int R_cap, uint16_t *h, uint16_t *g_out,
+                              uint16_t *u_out, hipStream_t s);
+
 // y[row_r][k] = sum_n h[r][n] * wd[n][k] (fp32) for r < rows, with row_r =
 // rowlist[r] or r as above.  With a `partial` buffer (split_partial_bytes())
 // the reduction is split when there are few rows, and launch_split_reduce
@@ -56,5 +64,18 @@ hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
                                const int32_t *count, int R_cap, int K, int N, float *y,
                                hipStream_t s);
 size_t split_partial_bytes();
+
+// Hybrid storage of the training forward (hybrid.hip).
+hipError_t launch_hybrid_pack(const float *tw_val, const int32_t *tw_idx, const int32_t *tw_cnt,
+                              int M, int N, int T, int C, int P, float *hy_val, int32_t *hy_idx,
+                              int32_t *hy_cnt, uint8_t *route, hipStream_t s);
+hipError_t launch_route_compact(const uint8_t *route, int M, int R_max, int32_t *bk_rows,
+                                int32_t *bk_count, hipStream_t s);
+hipError_t launch_hybrid_up(const uint16_t *x, const uint16_t *wu_t, int M, int K, int N, int P,
+                            const float *hy_g, const int32_t *hy_idx, const int32_t *hy_cnt,
+                            const uint8_t *route, float *hy_u, float *hy_h, hipStream_t s);
+hipError_t launch_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const float *hy_h,
+                              const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                              float *y, hipStream_t s);
 
 }  // namespace tw

@@ -7,8 +7,10 @@ Importing this module fails loudly when the library has not been built
 
 Low-level functions carry the C names and take preallocated tensors:
 ``tw_pack_gate``, ``tw_sparse_ffn_fwd``, ``tw_ffn_fwd``, ``tw_workspace_bytes``,
-``tw_ffn_workspace_bytes``.  ``pack_gate``, ``sparse_ffn`` and ``ffn``
-allocate their outputs and return them.
+``tw_ffn_workspace_bytes``, ``tw_gate_dense``, ``tw_pack_dense`` and the
+hybrid training storage ``tw_hybrid_pack``, ``tw_hybrid_up``,
+``tw_hybrid_down``.  ``pack_gate``, ``pack_unfused``, ``sparse_ffn``, ``ffn``
+and ``hybrid_forward`` allocate their outputs and return them.
 """
 from __future__ import annotations
 
@@ -53,6 +55,17 @@ _lib.tw_pack_dense_workspace_bytes.argtypes = [_i, _i]
 _lib.tw_pack_dense.restype = _i
 _lib.tw_pack_dense.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _sz, _vp,
                                _vp]
+_lib.tw_hybrid_pack.restype = _i
+_lib.tw_hybrid_pack.argtypes = [_i, _i, _i, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                _i, _vp, _vp]
+_lib.tw_hybrid_up.restype = _i
+_lib.tw_hybrid_up.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                              _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.tw_hybrid_down_workspace_bytes.restype = _sz
+_lib.tw_hybrid_down_workspace_bytes.argtypes = [_i]
+_lib.tw_hybrid_down.restype = _i
+_lib.tw_hybrid_down.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp,
+                                _vp, _sz, _vp, _vp]
 
 TW_OK, TW_EINVAL, TW_EUNSUPPORTED, TW_EHIP = 0, 1, 2, 3
 
@@ -175,6 +188,47 @@ def tw_pack_dense(z, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_max, w
     _check(st, "tw_pack_dense")
 
 
+def tw_hybrid_pack(T, C, tw_val, tw_idx, tw_cnt, P, hy_val, hy_idx, hy_cnt, route, bk_rows,
+                   bk_count, R_max, stream=None, events=None) -> None:
+    M, NT = tw_cnt.shape
+    ev = _events(events)
+    st = _lib.tw_hybrid_pack(M, NT * T, T, C, _ptr(tw_val), _ptr(tw_idx), _ptr(tw_cnt), P,
+                             _ptr(hy_val), _ptr(hy_idx), _ptr(hy_cnt), _ptr(route), _ptr(bk_rows),
+                             _ptr(bk_count), R_max, _stream(stream), ev[0] if ev else None)
+    _check(st, "tw_hybrid_pack")
+
+
+def tw_hybrid_up(x, wg_t, wu_t, P, hy_g, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max,
+                 hy_u, hy_h, bk_g, bk_u, bk_h, stream=None, events=None) -> None:
+    M, K = x.shape
+    N = wg_t.shape[0]
+    for t, n in ((x, "x"), (wg_t, "wg_t"), (wu_t, "wu_t")):
+        _dtype(t, torch.bfloat16, n)
+    ev = _events(events)
+    st = _lib.tw_hybrid_up(_ptr(x), _ptr(wg_t), _ptr(wu_t), M, K, N, P, _ptr(hy_g), _ptr(hy_idx),
+                           _ptr(hy_cnt), _ptr(route), _ptr(bk_rows), _ptr(bk_count), R_max,
+                           _ptr(hy_u), _ptr(hy_h), _ptr(bk_g), _ptr(bk_u), _ptr(bk_h),
+                           _stream(stream), ev[0] if ev else None)
+    _check(st, "tw_hybrid_up")
+
+
+def tw_hybrid_down_workspace_bytes(R_max) -> int:
+    return int(_lib.tw_hybrid_down_workspace_bytes(R_max))
+
+
+def tw_hybrid_down(wd, M, P, hy_h, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max, bk_h, y,
+                   ws, stream=None, events=None) -> None:
+    N, K = wd.shape
+    _dtype(wd, torch.bfloat16, "wd")
+    _dtype(y, torch.float32, "y")
+    ev = _events(events)
+    nws = 0 if ws is None else ws.numel() * ws.element_size()
+    st = _lib.tw_hybrid_down(_ptr(wd), M, K, N, P, _ptr(hy_h), _ptr(hy_idx), _ptr(hy_cnt),
+                             _ptr(route), _ptr(bk_rows), _ptr(bk_count), R_max, _ptr(bk_h),
+                             _ptr(y), _ptr(ws), nws, _stream(stream), ev[0] if ev else None)
+    _check(st, "tw_hybrid_down")
+
+
 # ------------------------------------------------------------- allocating --
 def alloc_pack(M, N, T, C, R_max, device="cuda"):
     """Output buffers of tw_pack_gate."""
@@ -247,6 +301,55 @@ def ffn(x, wg_t, wu_t, wd, ws=None):
         ws = torch.empty((tw_ffn_workspace_bytes(M, K, N),), dtype=torch.uint8, device=x.device)
     tw_ffn_fwd(x, wg_t, wu_t, wd, y, ws)
     return y
+
+
+def alloc_hybrid(M, N, P, R_max, keep=True, device="cuda"):
+    """Buffers of the hybrid storage (sparse rows, routing, backup rows).
+    ``keep`` also allocates the up values and the backup gate and up rows
+    (what the backward reads); without it only the product h is stored."""
+    R1 = max(R_max, 1)
+    f32, i32, b16 = torch.float32, torch.int32, torch.bfloat16
+    out = {
+        "hy_cnt": torch.empty((M,), dtype=i32, device=device),
+        "hy_idx": torch.empty((M, P), dtype=i32, device=device),
+        "hy_g": torch.empty((M, P), dtype=f32, device=device),
+        "hy_h": torch.empty((M, P), dtype=f32, device=device),
+        "route": torch.empty((M,), dtype=torch.uint8, device=device),
+        "bk_rows": torch.empty((R1,), dtype=i32, device=device),
+        "bk_count": torch.empty((1,), dtype=i32, device=device),
+        "bk_h": torch.empty((R1, N), dtype=b16, device=device),
+        "hy_u": None, "bk_g": None, "bk_u": None,
+    }
+    if keep:
+        out["hy_u"] = torch.empty((M, P), dtype=f32, device=device)
+        out["bk_g"] = torch.empty((R1, N), dtype=b16, device=device)
+        out["bk_u"] = torch.empty((R1, N), dtype=b16, device=device)
+    out.update(P=P, R_max=R_max)
+    return out
+
+
+def hybrid_forward(x, wg_t, wu_t, wd, packed, P=128, R_max=None, keep=True, hy=None, ws=None):
+    """Training forward over hybrid storage, from a TwELL packing of the gate
+    (``pack_gate``'s output): TwELL -> hybrid, up at the stored entries, down
+    to dense.  Returns (y fp32 [M][K], the hybrid storage dict)."""
+    M, K = x.shape
+    N = wg_t.shape[0]
+    R_max = max(M // 8, 1) if R_max is None else R_max
+    R_max = min(R_max, M)
+    hy = alloc_hybrid(M, N, P, R_max, keep, x.device) if hy is None else hy
+    tw_hybrid_pack(packed["T"], packed["C"], packed["tw_val"], packed["tw_idx"],
+                   packed["tw_cnt"], P, hy["hy_g"], hy["hy_idx"], hy["hy_cnt"], hy["route"],
+                   hy["bk_rows"], hy["bk_count"], R_max)
+    tw_hybrid_up(x, wg_t, wu_t, P, hy["hy_g"], hy["hy_idx"], hy["hy_cnt"], hy["route"],
+                 hy["bk_rows"], hy["bk_count"], R_max, hy["hy_u"], hy["hy_h"], hy["bk_g"],
+                 hy["bk_u"], hy["bk_h"])
+    y = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    nws = tw_hybrid_down_workspace_bytes(R_max)
+    if ws is None and nws:
+        ws = torch.empty((nws,), dtype=torch.uint8, device=x.device)
+    tw_hybrid_down(wd, M, P, hy["hy_h"], hy["hy_idx"], hy["hy_cnt"], hy["route"], hy["bk_rows"],
+                   hy["bk_count"], R_max, hy["bk_h"], y, ws)
+    return y, hy
 
 
 def library_path() -> str:

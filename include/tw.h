@@ -22,6 +22,8 @@
  * tw_ffn_fwd is the dense gated FFN over all rows, the comparator the sparse
  * path is measured against.  tw_gate_dense + tw_pack_dense are the unfused
  * equivalent of tw_pack_gate (dense gate written to memory, then packed).
+ * tw_hybrid_pack, tw_hybrid_up and tw_hybrid_down are the training forward
+ * over the hybrid storage of sections 3-6 and 3-7 (declared at the end).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -196,6 +198,93 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
                      const uint16_t *wu_t, const uint16_t *wd,
                      int M, int K, int N, float *y, void *ws, size_t ws_bytes,
                      void *stream, void *const *events);
+
+/*
+ * Hybrid storage for the training forward (sections 3-6, 3-7 and 4-3).
+ *
+ * Training keeps the gate activation in a hybrid form built from the TwELL
+ * gate (section 2-2: TwELL gate, then hybrid storage): most token rows as a
+ * row-wide ELL of at most P entries (the values and original hidden indices
+ * of section 3-3's ELL, in ascending column order), the few heavy rows whole
+ * in a dense backup, and a binary routing vector saying which holds each
+ * row.  The up and down projections then run as two separate products that
+ * keep that form (section 3-7: in training they are not fused): the
+ * dense-to-hybrid product (x W_u evaluated only at the stored entries, times
+ * the gate) and the hybrid-to-dense product (h W_d).  The section 4-3
+ * capacities are P = 128 stored entries per row and a backup of at most
+ * M / 8 rows; an overflow of the backup is reported for a retry.
+ *
+ * Common arrays (device, caller-owned, P the sparse row capacity):
+ *   hy_cnt  [M]        int32  the row's number of active neurons (the true
+ *                             count, also for backup rows)
+ *   hy_idx  [M][P]     int32  stored hidden index j of entry s < hy_cnt[m]
+ *   hy_val / hy_u / hy_h [M][P]  fp32  gate value, up value, product of entry s
+ *   route   [M]        uint8  1 if row m lives in the dense backup, else 0
+ *   bk_rows [max(R_max,1)] int32  backup rows, ascending; slot r holds row bk_rows[r]
+ *   bk_count[1]        int32  the true number of backup rows (may exceed R_max)
+ *   bk_g / bk_u / bk_h [R_max][N] bf16  dense gate, up, product of backup slot r
+ * Slots s >= hy_cnt[m] of a sparse row, and every slot of a backup row, are
+ * left untouched.  A backup row past R_max (bk_count > R_max) is in neither
+ * store: read bk_count after the stream has run and retry with a larger
+ * R_max (or P) -- the retry of section 4-3.  Such rows get no output from
+ * tw_hybrid_up or tw_hybrid_down.
+ *
+ * Shapes: as for tw_pack_gate (T in {128, 256}, N a multiple of T, N/T <=
+ * 256, 1 <= C <= T, K a multiple of 128 and at most 4096, M*K < 2^31), and
+ * N a multiple of 128, 1 <= P <= N, 0 <= R_max <= M, N*K < 2^31,
+ * R_max*N < 2^31.
+ */
+
+/*
+ * TwELL -> hybrid.  Reads a TwELL packing of capacity C (tw_pack_gate's or
+ * tw_pack_dense's outputs).  Row m goes to the dense backup when its total
+ * count exceeds P or when one of its tiles held more than C entries (its
+ * TwELL slots then lack entries); otherwise its TwELL entries are copied to
+ * hy_idx / hy_val in ascending column order.  Writes hy_cnt, route and the
+ * backup list.  The backup rows' dense values are produced by tw_hybrid_up.
+ * events: [0] before, [1] after the packing kernel, [2] after the list.
+ */
+tw_status tw_hybrid_pack(int M, int N, int T, int C,
+                         const float *tw_val, const int32_t *tw_idx, const int32_t *tw_cnt,
+                         int P, float *hy_val, int32_t *hy_idx, int32_t *hy_cnt,
+                         uint8_t *route, int32_t *bk_rows, int32_t *bk_count, int R_max,
+                         void *stream, void *const *events);
+
+/*
+ * Dense-to-hybrid product of the up projection, times the gate.
+ * Sparse rows: for each stored entry s (hidden index j, gate g = hy_g),
+ *     hy_u[m][s] = x[m] . wu_t[j]   (fp32),   hy_h[m][s] = hy_u[m][s] * g.
+ * Backup slots r < min(*bk_count, R_max), row m = bk_rows[r], all N columns
+ * on the matrix cores (one GEMM over W_g and W_u, x read once):
+ *     bk_g[r] = bf16(ReLU(x[m] W_g)),  bk_u[r] = bf16(x[m] W_u),
+ *     bk_h[r] = bf16(ReLU(x[m] W_g) * (x[m] W_u))  (product before rounding).
+ * hy_u, bk_g and bk_u may be NULL (not stored); hy_h and bk_h are required.
+ * events: [0] before, [1] after the sparse-row kernel, [2] after the backup GEMM.
+ */
+tw_status tw_hybrid_up(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu_t,
+                       int M, int K, int N, int P,
+                       const float *hy_g, const int32_t *hy_idx, const int32_t *hy_cnt,
+                       const uint8_t *route, const int32_t *bk_rows, const int32_t *bk_count,
+                       int R_max, float *hy_u, float *hy_h,
+                       uint16_t *bk_g, uint16_t *bk_u, uint16_t *bk_h,
+                       void *stream, void *const *events);
+
+/*
+ * Hybrid-to-dense product of the down projection, y = h W_d (fp32 [M][K]).
+ * Sparse rows: y[m] = sum over stored s of hy_h[m][s] * wd[hy_idx[m][s]]
+ * (a row with no entry gets 0).  Backup slots r < min(*bk_count, R_max): the
+ * row bk_rows[r] of y gets bk_h[r] W_d on the matrix cores.  The workspace
+ * holds the backup GEMM's partial tiles: ws_bytes >=
+ * tw_hybrid_down_workspace_bytes(R_max) (ws may be NULL when that is 0).
+ * events: [0] before, [1] after the sparse-row kernel, [2], [3] after the
+ * backup GEMM and the sum of its partial tiles.
+ */
+size_t tw_hybrid_down_workspace_bytes(int R_max);
+tw_status tw_hybrid_down(const uint16_t *wd, int M, int K, int N, int P,
+                         const float *hy_h, const int32_t *hy_idx, const int32_t *hy_cnt,
+                         const uint8_t *route, const int32_t *bk_rows, const int32_t *bk_count,
+                         int R_max, const uint16_t *bk_h, float *y,
+                         void *ws, size_t ws_bytes, void *stream, void *const *events);
 
 #ifdef __cplusplus
 }

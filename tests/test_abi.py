@@ -116,3 +116,30 @@ def test_unfused_entry_points_reject(tw):
     assert L.tw_pack_dense(P, 64, 1024, 128, 8, P, P, P, P, P, 64, P, 8, None, None) == 1
     assert L.tw_pack_dense(None, 64, 1024, 128, 8, P, P, P, P, P, 64, P, ws, None, None) == 1
     assert tw._lib.tw_last_error()
+
+
+def test_hybrid_entry_points_reject(tw):
+    L = tw._lib
+    def H(M=64, N=1024, T=128, C=16, cap=128, R=8, route=P, bk=P, hv=P):
+        return L.tw_hybrid_pack(M, N, T, C, P, P, P, cap, hv, P, P, route, bk, P, R, None, None)
+    assert H(cap=0) == 1 and H(cap=1025) == 1      # sparse capacity outside [1, N]
+    assert H(T=64) == 2 and H(C=0) == 1 and H(N=1000) == 1
+    assert H(R=65) == 1 and H(R=-1) == 1
+    assert H(route=None) == 1 and H(route=P + 1) == 1 and H(bk=None) == 1 and H(hv=None) == 1
+    # backup rows of 4 GiB or more are outside the 32-bit buffer offsets
+    assert H(M=1 << 17, N=1 << 15, R=1 << 17) == 2
+
+    def U(K=256, cap=128, R=8, hy_h=P, bk_h=P, hy_u=None):
+        return L.tw_hybrid_up(P, P, P, 64, K, 1024, cap, P, P, P, P, P, P, R, hy_u, hy_h, None,
+                              None, bk_h, None, None)
+    assert U(K=100) == 2 and U(cap=0) == 1 and U(hy_h=None) == 1
+    assert U(bk_h=None) == 1 and U(hy_u=P + 4) == 1
+
+    nws = L.tw_hybrid_down_workspace_bytes(8)
+    assert nws > 0 and L.tw_hybrid_down_workspace_bytes(0) == 0
+
+    def D(y=P, ws=P, nb=nws, R=8, cap=128):
+        return L.tw_hybrid_down(P, 64, 256, 1024, cap, P, P, P, P, P, P, R, P, y, ws, nb, None,
+                                None)
+    assert D(y=None) == 1 and D(nb=nws - 1) == 1 and D(ws=None) == 1 and D(cap=2048) == 1
+    assert tw._lib.tw_last_error()
