@@ -134,6 +134,121 @@ def cpu_baseline(d, w, budget_s: float):
                             f"{dsecs:.1f} s"}
 
 
+def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, stream, hev,
+                         t_dense, step):
+    """The training forward over hybrid storage: gate + TwELL, TwELL ->
+    hybrid (P = 128 entries per sparse row, backup room M / 8), up at the
+    stored entries (keeping g and u for the backward), down to dense.
+    Timed the same way as the inference step; per-kernel durations from
+    eager launches with HIP events between kernels."""
+    import numpy as np
+
+    M, K, N, T, C = w.M, w.K, w.N, w.T, w.C
+    P, Rh = 128, max(M // 8, 1)
+    hy = tw.alloc_hybrid(M, N, P, Rh, keep=True)
+    wsh = torch.empty((max(tw.tw_hybrid_down_workspace_bytes(Rh), 1),), dtype=torch.uint8,
+                      device="cuda")
+    yh = torch.empty((M, K), dtype=torch.float32, device="cuda")
+
+    def hstep(ev=None, st=stream):
+        # st=None: the current stream (the capture stream inside a graph capture)
+        e = ev or (None, None, None, None)
+        tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"],
+                        bufs["ovf_rows"], bufs["ovf_count"], R_max, ws, stream=st, events=e[0])
+        tw.tw_hybrid_pack(T, C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"], P, hy["hy_g"],
+                          hy["hy_idx"], hy["hy_cnt"], hy["route"], hy["bk_rows"], hy["bk_count"],
+                          Rh, stream=st, events=e[1])
+        tw.tw_hybrid_up(x, wg, wu, P, hy["hy_g"], hy["hy_idx"], hy["hy_cnt"], hy["route"],
+                        hy["bk_rows"], hy["bk_count"], Rh, hy["hy_u"], hy["hy_h"], hy["bk_g"],
+                        hy["bk_u"], hy["bk_h"], stream=st, events=e[2])
+        tw.tw_hybrid_down(wdn, M, P, hy["hy_h"], hy["hy_idx"], hy["hy_cnt"], hy["route"],
+                          hy["bk_rows"], hy["bk_count"], Rh, hy["bk_h"], yh, wsh, stream=st,
+                          events=e[3])
+
+    for _ in range(max(args.warmup, 1)):
+        hstep()
+    torch.cuda.synchronize()
+    bk_count = int(hy["bk_count"].cpu()[0])
+    if bk_count > Rh:
+        return {"skipped": f"{bk_count} backup rows exceed the room of {Rh} (M / 8): the "
+                           f"caller would retry with more storage"}
+    hy_cnt = hy["hy_cnt"].cpu().numpy().astype(np.int64)
+    route = hy["route"].cpu().numpy().astype(bool)
+    nnz_sp = int(hy_cnt[~route].sum())
+    rows_sp = int((~route).sum())
+    rows_sp_act = int(((hy_cnt > 0) & ~route).sum())
+
+    Ks = args.steps
+    evl = [(hev.create(3), hev.create(3), hev.create(3), hev.create(4)) for _ in range(Ks)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(Ks):
+        hstep(evl[i])
+    torch.cuda.synchronize()
+    t_eager = (time.perf_counter() - t0) / Ks
+    if not args.no_graph:
+        G = max(1, min(args.graph_steps, Ks))
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(G):
+                    hstep(st=None)
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()
+        n_rep = max(1, Ks // G)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            g.replay()
+        torch.cuda.synchronize()
+        t_h = (time.perf_counter() - t0) / (n_rep * G)
+        del g
+    else:
+        t_h = t_eager
+
+    def avg(j, i):
+        return sum(hev.ms(e[j][i], e[j][i + 1]) for e in evl) / len(evl) * 1e-3
+
+    kern = {"gate_twell": avg(0, 0), "ovf_compact": avg(0, 1), "hybrid_pack": avg(1, 0),
+            "route_compact": avg(1, 1), "hybrid_up": avg(2, 0), "backup_gateup": avg(2, 1),
+            "hybrid_down": avg(3, 0), "backup_down": avg(3, 1), "backup_reduce": avg(3, 2)}
+    for e in evl:
+        for q in e:
+            hev.destroy(q)
+    NT = N // T
+    # algorithmic bytes per launch: what each kernel must read and write
+    bytes_ = {
+        "hybrid_pack": M * (4 * NT + 4 + 1) + nnz_sp * 16,
+        "hybrid_up": nnz_sp * (2 * K + 4 + 4 + 8) + rows_sp_act * 2 * K + M * 5,
+        "hybrid_down": nnz_sp * (2 * K + 8) + rows_sp * 4 * K + M * 5,
+    }
+    roof = {k: {"bound": "hbm", "achieved": b / kern[k] / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": b / kern[k] / 1e9 / PEAK_HBM_GBS, "bytes": b,
+                "avg_us": kern[k] * 1e6}
+            for k, b in bytes_.items() if kern[k] > 0}
+    for k, f in (("backup_gateup", 4.0), ("backup_down", 2.0)):
+        if kern[k] > 0:
+            a = f * bk_count * K * N / kern[k] / 1e12
+            roof[k] = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS,
+                       "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS, "avg_us": kern[k] * 1e6}
+    storage = M * P * (4 * 4) + M * (4 + 1) + Rh * N * 2 * 3 + Rh * 4
+    return {
+        "ms_per_step": t_h * 1e3, "value": M / t_h, "unit": "tokens/s",
+        "speedup_vs_dense": t_dense / t_h, "eager_ms_per_step": t_eager * 1e3,
+        "P": P, "R_max": Rh, "backup_rows": bk_count,
+        "nnz_per_sparse_row": nnz_sp / max(1, rows_sp),
+        "kernels_us": {k: v * 1e6 for k, v in kern.items()},
+        "stages": roof,
+        "storage_bytes": storage,
+        "dense_activation_bytes": 3 * M * N * 2,
+        "note": "tw_pack_gate + tw_hybrid_pack + tw_hybrid_up (g and u kept) + tw_hybrid_down; "
+                "speedup against tw_ffn_fwd; storage = hybrid g, u, h (sparse rows fp32 with "
+                "indices, backup rows bf16) against dense bf16 g, u, h",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +267,8 @@ def main():
                     help="time eager launches instead of HIP-graph replays")
     ap.add_argument("--no-fusion-ablation", dest="fusion_ablation", action="store_false",
                     help="skip timing the unfused gate + pack path")
+    ap.add_argument("--no-hybrid", dest="hybrid", action="store_false",
+                    help="skip the hybrid training-forward measurement")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="replays for the Infinity-Cache-cold line (0: skip it)")
     ap.add_argument("--graph-steps", type=int, default=5,
@@ -384,6 +501,9 @@ def main():
         t_sparse, t_dense = t_sparse_eager, t_dense_eager
         per_sparse, per_dense, cold, fusion = [t_sparse_eager], [t_dense_eager], None, None
 
+    hybrid = hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, stream,
+                                  hev, t_dense, step) if args.hybrid else None
+
     # ---- sanity line: the same dense FFN on torch.matmul (hipBLASLt) ----
     wgu = torch.cat([wg, wu], dim=0)
     wd_row = wdn  # [N, K]: y = h @ W_d
@@ -475,6 +595,7 @@ def main():
                                               for q in (10, 50, 90)]},
         "cold": cold,
         "fusion": fusion,
+        "hybrid_training_forward": hybrid,
         "eager": {"sparse_ms_per_step": t_sparse_eager * 1e3,
                   "dense_ms_per_step": t_dense_eager * 1e3},
         "timing": (f"HIP graphs of {min(args.graph_steps, Ks)} consecutive steps, "
