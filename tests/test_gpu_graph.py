@@ -60,3 +60,68 @@ def test_graph_replay_matches_eager():
             assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), rep
         tw.ffn(x, wg, wu, wd)  # unrelated eager work between replays
         torch.cuda.synchronize()
+
+
+def test_hybrid_graph_replay_matches_eager():
+    """The training forward over hybrid storage (gate + TwELL, TwELL ->
+    hybrid, up, down) captured once replays to the eager bits."""
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from activation_sparse_feed_gate_amd import tw
+
+    w = synth.WORKLOADS["tiny"].with_(M=700, C=6, sigma_s=0.5, density=0.03)
+    print(f"case {w}", flush=True)
+    dev = parity.upload(synth.make_inputs(w))
+    x, wg, wu, wd = dev["x"], dev["wg_t"], dev["wu_t"], dev["wd"]
+    P, R_max = 32, w.M // 2
+    bufs = tw.alloc_pack(w.M, w.N, w.T, w.C, w.M)
+    ws = tw.workspace(w.M, w.K, w.N, w.T, w.C, w.M)
+    hy = tw.alloc_hybrid(w.M, w.N, P, R_max, keep=True)
+    wsh = torch.empty((tw.tw_hybrid_down_workspace_bytes(R_max),), dtype=torch.uint8,
+                      device="cuda")
+    y = torch.empty((w.M, w.K), dtype=torch.float32, device="cuda")
+
+    def step():
+        tw.tw_pack_gate(x, wg, w.T, w.C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"],
+                        bufs["ovf_rows"], bufs["ovf_count"], w.M, ws)
+        tw.tw_hybrid_pack(w.T, w.C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"], P,
+                          hy["hy_g"], hy["hy_idx"], hy["hy_cnt"], hy["route"], hy["bk_rows"],
+                          hy["bk_count"], R_max)
+        tw.tw_hybrid_up(x, wg, wu, P, hy["hy_g"], hy["hy_idx"], hy["hy_cnt"], hy["route"],
+                        hy["bk_rows"], hy["bk_count"], R_max, hy["hy_u"], hy["hy_h"],
+                        hy["bk_g"], hy["bk_u"], hy["bk_h"])
+        tw.tw_hybrid_down(wd, w.M, P, hy["hy_h"], hy["hy_idx"], hy["hy_cnt"], hy["route"],
+                          hy["bk_rows"], hy["bk_count"], R_max, hy["bk_h"], y, wsh)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        n = int(hy["bk_count"].cpu()[0])
+        return (y.cpu().numpy().copy(), hy["route"].cpu().numpy().copy(),
+                hy["bk_rows"].cpu().numpy()[:n].copy(), hy["bk_h"][:n].cpu().view(torch.int16)
+                .numpy().copy(), n)
+
+    step()
+    ref = snapshot()
+    assert 0 < ref[4] <= R_max  # the backup path is part of the captured work
+
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    torch.cuda.current_stream().wait_stream(cap)
+
+    for rep in range(4):
+        y.fill_(float("nan"))
+        hy["route"].fill_(7)
+        hy["bk_h"].fill_(0)
+        g.replay()
+        got = snapshot()
+        assert got[4] == ref[4], rep
+        for a, b in zip(got[:4], ref[:4]):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), rep
+        tw.ffn(x, wg, wu, wd)  # unrelated eager work between replays
+        torch.cuda.synchronize()
