@@ -21,7 +21,11 @@ that each of these must catch.  The hybrid storage of the training forward
 hand-worked fixture (``tests/golden/handworked_hybrid_4x4x8.txt``), integer
 brute force, scipy's CSR rows and numpy products in the lossless case,
 density 0 and 1, and the composed hybrid forward equalling the dense block
-output bit for bit.
+output bit for bit.  The backward over hybrid storage (``hybrid_bwd``) is
+pinned to torch autograd in float64 on the CPU: exactly on small integer
+problems (including rows past the backup room), within rounding on generator
+inputs, for the input and weight gradients and the gradients of u and z at
+the stored entries.
 """
 from __future__ import annotations
 
@@ -89,9 +93,12 @@ class Oracle:
                                           _U8, _I, _int, _D, _D, _D, _D, _D]
         L.tw_oracle_hybrid_down.argtypes = [_D, _int, _int, _int, _int, _I, _I, _D, _U8, _I,
                                             _int, _D, _D]
+        L.tw_oracle_hybrid_bwd.argtypes = [_D, _D, _D, _D, _D, _int, _int, _int, _int,
+                                           ctypes.c_double, _I, _I, _D, _D, _D, _U8, _I, _int,
+                                           _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
         for f in ("tw_oracle_gate", "tw_oracle_pack", "tw_oracle_dense_ffn",
                   "tw_oracle_sparse_ffn", "tw_oracle_hybrid_pack", "tw_oracle_hybrid_up",
-                  "tw_oracle_hybrid_down"):
+                  "tw_oracle_hybrid_down", "tw_oracle_hybrid_bwd"):
             getattr(L, f).restype = None
 
     def threads(self) -> int:
@@ -231,6 +238,38 @@ class Oracle:
                                        _p(h, _D), _p(route, _U8), _p(bk, _I), nbk, _p(b, _D),
                                        _p(y, _D))
         return y
+
+    def hybrid_bwd(self, x, wg_t, wu_t, wd, dy, hy: dict, acts: dict, l1: float) -> dict:
+        """Backward over hybrid storage: ``hy`` the storage (``hybrid_pack``'s
+        output, or the GPU's arrays), ``acts`` its stored activations (hy_g in
+        ``hy['hy_val']``; ``acts`` holds hy_u, hy_h [M][P] and bk_g, bk_u,
+        bk_h [nbk][N]), ``dy`` [M][K] (bf16 bits or float64), ``l1`` the L1
+        penalty's gradient on a positive gate activation.  Returns hy_du,
+        hy_dz, bk_du, bk_dz, dx (NaN on rows with no stored activation),
+        dwg_t, dwu_t, dwd."""
+        x, wg, wu, w_d, g_y = (widen_bf16(a) for a in (x, wg_t, wu_t, wd, dy))
+        M, K = x.shape
+        N = wg.shape[0]
+        hy_cnt, hy_idx, route, bk, nbk = self._hy_arrays(hy)
+        P = hy_idx.shape[1]
+        f = lambda a, shp: np.ascontiguousarray(np.asarray(a, dtype=np.float64).reshape(shp))
+        hy_g = f(hy["hy_val"], (M, P))
+        hy_u, hy_h = f(acts["hy_u"], (M, P)), f(acts["hy_h"], (M, P))
+        nb1 = max(nbk, 1)
+        pad = lambda a: np.concatenate([f(a, (-1, N))[:nbk], np.zeros((nb1 - nbk, N))])
+        bk_g, bk_u, bk_h = pad(acts["bk_g"]), pad(acts["bk_u"]), pad(acts["bk_h"])
+        hy_du, hy_dz = np.full((M, P), np.nan), np.full((M, P), np.nan)
+        bk_du, bk_dz = np.full((nb1, N), np.nan), np.full((nb1, N), np.nan)
+        dx = np.full((M, K), np.nan)
+        dwg, dwu, dwd = (np.empty((N, K)) for _ in range(3))
+        self.lib.tw_oracle_hybrid_bwd(
+            _p(x, _D), _p(wg, _D), _p(wu, _D), _p(w_d, _D), _p(g_y, _D), M, K, N, P, float(l1),
+            _p(hy_cnt, _I), _p(hy_idx, _I), _p(hy_g, _D), _p(hy_u, _D), _p(hy_h, _D),
+            _p(route, _U8), _p(bk, _I), nbk, _p(bk_g, _D), _p(bk_u, _D), _p(bk_h, _D),
+            _p(hy_du, _D), _p(hy_dz, _D), _p(bk_du, _D), _p(bk_dz, _D), _p(dx, _D),
+            _p(dwg, _D), _p(dwu, _D), _p(dwd, _D))
+        return {"hy_du": hy_du, "hy_dz": hy_dz, "bk_du": bk_du[:nbk], "bk_dz": bk_dz[:nbk],
+                "dx": dx, "dwg_t": dwg, "dwu_t": dwu, "dwd": dwd}
 
 
 _default = None

@@ -337,3 +337,131 @@ void tw_oracle_hybrid_down(const double *wd, int M, int K, int N, int P,
         }
     }
 }
+
+/* Backward of the block over hybrid storage, section 3-7 (the gradients are
+ * formed from the stored sparse activations without rebuilding the dense
+ * hidden state), with the activation L1 penalty of section 3-2 injected into
+ * the gate gradient.
+ *
+ * Given dy = dLoss/dy [M][K] and the forward's stored g (= h_g), u (= h_u)
+ * and h = g u, by the chain rule through section 1-1's equation:
+ *   dh[m][j]  = dy_m . W_d[j, :]                       (dense-to-hybrid)
+ *   du[m][j]  = dh g                                    (gradient of h_u)
+ *   dz[m][j]  = dh u + l1   where g > 0, else 0         (through the ReLU;
+ *               l1 is the L1 penalty's gradient on a positive activation)
+ *   dx_m      = sum_j du W_u[:, j]^T + dz W_g[:, j]^T   (hybrid-to-dense)
+ *   dW_d[j]   = sum_m h[m][j] dy_m
+ *   dW_u[:,j] = sum_m du[m][j] x_m,  dW_g[:,j] = sum_m dz[m][j] x_m
+ * (the weight gradients read the stored activations column by column: the
+ * hybrid transpose).  The transposed weight layouts hold dwu_t[j] = dW_u[:,j]
+ * and dwg_t[j] = dW_g[:,j].  Sparse rows visit their stored entries in slot
+ * order; the first nbk backup rows visit every column j in ascending order
+ * (their dense g, u, h); other backup rows have no stored activation and
+ * contribute nothing (dx rows left unwritten).  Weight-gradient sums run
+ * over rows in ascending order. */
+void tw_oracle_hybrid_bwd(const double *x, const double *wg_t, const double *wu_t,
+                          const double *wd, const double *dy, int M, int K, int N, int P,
+                          double l1, const int32_t *hy_cnt, const int32_t *hy_idx,
+                          const double *hy_g, const double *hy_u, const double *hy_h,
+                          const uint8_t *route, const int32_t *bk_rows, int nbk,
+                          const double *bk_g, const double *bk_u, const double *bk_h,
+                          double *hy_du, double *hy_dz, double *bk_du, double *bk_dz,
+                          double *dx, double *dwg_t, double *dwu_t, double *dwd)
+{
+    /* gradients of the stored activations */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; ++m) {
+        if (route[m])
+            continue;
+        const double *dym = dy + (size_t)m * K;
+        for (int s = 0; s < hy_cnt[m]; ++s) {
+            const size_t e = (size_t)m * P + s;
+            const double dh = dot(dym, wd + (size_t)hy_idx[e] * K, K);
+            hy_du[e] = dh * hy_g[e];
+            hy_dz[e] = dh * hy_u[e] + l1;
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nbk; ++r) {
+        const double *dym = dy + (size_t)bk_rows[r] * K;
+        for (int j = 0; j < N; ++j) {
+            const size_t e = (size_t)r * N + j;
+            const double dh = dot(dym, wd + (size_t)j * K, K);
+            bk_du[e] = dh * bk_g[e];
+            bk_dz[e] = bk_g[e] > 0.0 ? dh * bk_u[e] + l1 : 0.0;
+        }
+    }
+    /* input gradient */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int m = 0; m < M; ++m) {
+        if (route[m])
+            continue;
+        double *dxm = dx + (size_t)m * K;
+        for (int k = 0; k < K; ++k)
+            dxm[k] = 0.0;
+        for (int s = 0; s < hy_cnt[m]; ++s) {
+            const size_t e = (size_t)m * P + s;
+            const double *wu = wu_t + (size_t)hy_idx[e] * K;
+            const double *wg = wg_t + (size_t)hy_idx[e] * K;
+            for (int k = 0; k < K; ++k)
+                dxm[k] += hy_du[e] * wu[k] + hy_dz[e] * wg[k];
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < nbk; ++r) {
+        double *dxm = dx + (size_t)bk_rows[r] * K;
+        for (int k = 0; k < K; ++k)
+            dxm[k] = 0.0;
+        for (int j = 0; j < N; ++j) {
+            const size_t e = (size_t)r * N + j;
+            const double *wu = wu_t + (size_t)j * K;
+            const double *wg = wg_t + (size_t)j * K;
+            for (int k = 0; k < K; ++k)
+                dxm[k] += bk_du[e] * wu[k] + bk_dz[e] * wg[k];
+        }
+    }
+    /* weight gradients: each thread owns a range of hidden columns and walks
+     * every row in ascending order */
+#pragma omp parallel
+    {
+#ifdef _OPENMP
+        const int nt = omp_get_num_threads(), t = omp_get_thread_num();
+#else
+        const int nt = 1, t = 0;
+#endif
+        const int j0 = (int)((long long)N * t / nt), j1 = (int)((long long)N * (t + 1) / nt);
+        for (size_t q = (size_t)j0 * K; q < (size_t)j1 * K; ++q) {
+            dwd[q] = 0.0;
+            dwu_t[q] = 0.0;
+            dwg_t[q] = 0.0;
+        }
+        int r = 0;  /* next backup slot, in ascending row order */
+        for (int m = 0; m < M; ++m) {
+            const double *xm = x + (size_t)m * K;
+            const double *dym = dy + (size_t)m * K;
+            if (!route[m]) {
+                for (int s = 0; s < hy_cnt[m]; ++s) {
+                    const size_t e = (size_t)m * P + s;
+                    const int j = hy_idx[e];
+                    if (j < j0 || j >= j1)
+                        continue;
+                    for (int k = 0; k < K; ++k) {
+                        dwd[(size_t)j * K + k] += hy_h[e] * dym[k];
+                        dwu_t[(size_t)j * K + k] += hy_du[e] * xm[k];
+                        dwg_t[(size_t)j * K + k] += hy_dz[e] * xm[k];
+                    }
+                }
+            } else if (r < nbk && bk_rows[r] == m) {
+                for (int j = j0; j < j1; ++j) {
+                    const size_t e = (size_t)r * N + j;
+                    for (int k = 0; k < K; ++k) {
+                        dwd[(size_t)j * K + k] += bk_h[e] * dym[k];
+                        dwu_t[(size_t)j * K + k] += bk_du[e] * xm[k];
+                        dwg_t[(size_t)j * K + k] += bk_dz[e] * xm[k];
+                    }
+                }
+                ++r;
+            }
+        }
+    }
+}

@@ -547,6 +547,103 @@ def pin_hybrid_extremes(orc) -> None:
         "density 1, P = N: every row sparse and full"
 
 
+# --------------------------------------------------------------------------
+# backward over hybrid storage (section 3-7, L1 of section 3-2)
+# --------------------------------------------------------------------------
+def _autograd(x, wg, wu, wd, dy, l1):
+    """Gradients of sum(y * dy) + l1 * sum(ReLU(x W_g)) by torch autograd in
+    float64 on the CPU (a library routine, independent of the oracle),
+    with the gradients of u = x W_u and z = x W_g kept."""
+    import torch
+
+    t = lambda a: torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+    X, Wg, Wu, Wd = t(x), t(wg), t(wu), t(wd)
+    z = X @ Wg.T
+    u = X @ Wu.T
+    z.retain_grad()
+    u.retain_grad()
+    g = torch.relu(z)
+    y = (g * u) @ Wd
+    loss = (y * torch.tensor(np.asarray(dy, dtype=np.float64))).sum() + l1 * g.sum()
+    loss.backward()
+    return {"dx": X.grad.numpy(), "dwg_t": Wg.grad.numpy(), "dwu_t": Wu.grad.numpy(),
+            "dwd": Wd.grad.numpy(), "du": u.grad.numpy(), "dz": z.grad.numpy()}
+
+
+def _stored_rows(hy):
+    listed = set(int(m) for m in hy["bk_rows"])
+    return np.array([m for m in range(len(hy["route"])) if not hy["route"][m] or m in listed],
+                    dtype=np.int64)
+
+
+def _check_bwd(orc, bx, bg, bu, bd, bdy, T, C, P, R_max, l1, exact):
+    """Hybrid forward then backward on the oracle against autograd over the
+    rows whose activations are stored."""
+    p = orc.pack(orc.gate(bx, bg), T, C, len(bx))
+    hy = orc.hybrid_pack(p, C, P, R_max)
+    up = orc.hybrid_up(bx, bg, bu, hy)
+    b = orc.hybrid_bwd(bx, bg, bu, bd, bdy, hy, up, l1)
+    rows = _stored_rows(hy)
+    X, DY = orc_widen(bx), orc_widen(bdy)
+    ref = _autograd(X[rows], orc_widen(bg), orc_widen(bu), orc_widen(bd), DY[rows], l1)
+    if exact:
+        close = lambda a, r: np.array_equal(a, r)
+    else:
+        close = lambda a, r: np.all(np.abs(a - r) <= 1e-12 * (np.abs(r).max(initial=0) + 1))
+    assert close(b["dx"][rows], ref["dx"]), "dx"
+    assert np.all(np.isnan(np.delete(b["dx"], rows, axis=0))), "rows with nothing stored"
+    for k in ("dwg_t", "dwu_t", "dwd"):
+        assert close(b[k], ref[k]), k
+    pos = {int(m): i for i, m in enumerate(rows)}
+    for m in range(len(hy["route"])):
+        if hy["route"][m]:
+            continue
+        n = int(hy["hy_cnt"][m])
+        ids = hy["hy_idx"][m, :n]
+        i = pos[m]
+        assert close(b["hy_du"][m, :n], ref["du"][i, ids]), "du at the stored entries"
+        assert close(b["hy_dz"][m, :n], ref["dz"][i, ids]), "dz at the stored entries"
+    for r, m in enumerate(hy["bk_rows"]):
+        i = pos[int(m)]
+        assert close(b["bk_du"][r], ref["du"][i]), "backup du"
+        assert close(b["bk_dz"][r], ref["dz"][i]), "backup dz"
+    return hy
+
+
+def pin_hybrid_bwd_exact(orc, cases: int = 30, seed: int = 777) -> None:
+    """Random small integer problems and integer L1 gradients: every gradient
+    exactly torch autograd's (all values are small integers, exact in bf16
+    and double), including a backup room too small for every heavy row."""
+    rnd = random.Random(seed)
+    for _ in range(cases):
+        T = rnd.choice([1, 2, 4])
+        N = T * rnd.randint(1, 3)
+        K = rnd.randint(1, 5)
+        M = rnd.randint(1, 6)
+        C = rnd.randint(1, T)
+        P = rnd.randint(1, N)
+        R_max = rnd.randint(0, M)
+        l1 = rnd.choice([0, 1, 2])
+        draw = lambda r, c: [[rnd.randint(-3, 3) for _ in range(c)] for _ in range(r)]
+        bx, bg, bu, bd, bdy = (_bits(a) for a in (draw(M, K), draw(N, K), draw(N, K),
+                                                  draw(N, K), draw(M, K)))
+        _check_bwd(orc, bx, bg, bu, bd, bdy, T, C, P, R_max, l1, exact=True)
+
+
+def pin_hybrid_bwd_autograd(orc) -> None:
+    """Generator inputs: sparse rows only, many backup rows, and the tile
+    rule, against autograd within rounding."""
+    for C, P, l1 in ((16, 128, 0.0), (12, 40, 0.01), (4, 128, 0.05)):
+        w, d = _tiny(C=C)
+        rng = np.random.default_rng(5)
+        dy = synth.f32_to_bf16_bits(rng.standard_normal((w.M, w.K)).astype(np.float32))
+        hy = _check_bwd(orc, d["x"], d["wg_t"], d["wu_t"], d["wd"], dy, w.T, C, P, w.M, l1,
+                        exact=False)
+        if P == 40:
+            assert hy["bk_count"] > 10, "the backup path is exercised"
+
+
 ALL_PINS = [pin_golden, pin_bruteforce, pin_csr_library, pin_numpy_dense, pin_onehot,
             pin_invariants, pin_density_extremes, pin_hybrid_golden, pin_hybrid_bruteforce,
-            pin_hybrid_library, pin_hybrid_invariants, pin_hybrid_extremes]
+            pin_hybrid_library, pin_hybrid_invariants, pin_hybrid_extremes,
+            pin_hybrid_bwd_exact, pin_hybrid_bwd_autograd]

@@ -82,6 +82,25 @@ MUTANTS = [
     ("hybrid down ignores h", "ym[k] += hy_h[e] * wdj[k];", "ym[k] += wdj[k];"),
     ("backup output to slot row", "double *ym = y + (size_t)bk_rows[r] * K;",
      "double *ym = y + (size_t)r * K;"),
+    # backward over hybrid storage
+    ("gate gradient misses L1", "hy_dz[e] = dh * hy_u[e] + l1;", "hy_dz[e] = dh * hy_u[e];"),
+    ("L1 on inactive backup entries", "bk_dz[e] = bk_g[e] > 0.0 ? dh * bk_u[e] + l1 : 0.0;",
+     "bk_dz[e] = dh * bk_u[e] + l1;"),
+    ("up gradient scaled by u", "hy_du[e] = dh * hy_g[e];", "hy_du[e] = dh * hy_u[e];"),
+    ("dh from up weights", "const double dh = dot(dym, wd + (size_t)hy_idx[e] * K, K);",
+     "const double dh = dot(dym, wu_t + (size_t)hy_idx[e] * K, K);"),
+    ("dx drops the gate term", "dxm[k] += hy_du[e] * wu[k] + hy_dz[e] * wg[k];",
+     "dxm[k] += hy_du[e] * wu[k];"),
+    ("dx swaps the weights", "dxm[k] += bk_du[e] * wu[k] + bk_dz[e] * wg[k];",
+     "dxm[k] += bk_du[e] * wg[k] + bk_dz[e] * wu[k];"),
+    ("down weight gradient from x", "dwd[(size_t)j * K + k] += hy_h[e] * dym[k];",
+     "dwd[(size_t)j * K + k] += hy_h[e] * xm[k];"),
+    ("up weight gradient from dz", "dwu_t[(size_t)j * K + k] += hy_du[e] * xm[k];",
+     "dwu_t[(size_t)j * K + k] += hy_dz[e] * xm[k];"),
+    ("backup rows left out of weight gradients", "} else if (r < nbk && bk_rows[r] == m) {",
+     "} else if (0) {"),
+    ("backup dy by slot", "const double *dym = dy + (size_t)bk_rows[r] * K;",
+     "const double *dym = dy + (size_t)r * K;"),
 ]
 
 
