@@ -39,12 +39,12 @@ __device__ __forceinline__ int rows_of(const int32_t *count, int R_cap) {
 }
 
 // ------------------------------ gate + up ---------------------------------
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, int NB = 2>
 struct GU {
     static constexpr int NW = WM * WN, NTH = NW * 64;
     static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
     static constexpr int FA = TM / 32, FB = TN / 32;  // 32-blocks per wave
-    static constexpr int SR = BM + 2 * BN;            // stage rows: A, then W_g, then W_u
+    static constexpr int SR = BM + NB * BN;           // stage rows: A, then W_g (, then W_u)
     static constexpr int NI = SR / (16 * NW);         // direct loads per wave and stage
     static constexpr int STAGE = SR * kPRow;
     static constexpr int LDS = S * STAGE;
@@ -52,15 +52,24 @@ struct GU {
     static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "each load row group in one operand");
 };
 
-// KEEP: also store bf16(ReLU(g)) and bf16(u) where g_out / u_out are given
-// (the dense backup rows of the hybrid training storage keep both).
-template <int BM, int BN, int WM, int WN, int S, bool KEEP>
+// Epilogue modes:
+//   kGU    h = bf16(ReLU(g) u)
+//   kKeep  h, and bf16(ReLU(g)) / bf16(u) into g_out / u_out where given
+//          (the dense backup rows of the hybrid training storage keep both)
+//   kDh    one weight operand (wg_t = W_d, x = dy): dh = dy_r . W_d[n], then
+//          with the stored bf16 gate and up values of the row (g_in, u_in):
+//          h <- bf16(dh g) (du) and g_out <- bf16(g > 0 ? dh u + l1 : 0) (dz)
+enum { kGU = 0, kKeep = 1, kDh = 2 };
+
+template <int BM, int BN, int WM, int WN, int S, int MODE>
 __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t,
     const uint16_t *__restrict__ wu_t, int K, int N, const int32_t *__restrict__ rowlist,
     const int32_t *__restrict__ count, int R_cap, int xrows, uint16_t *__restrict__ h,
-    uint16_t *__restrict__ g_out, uint16_t *__restrict__ u_out) {
-    using P = GU<BM, BN, WM, WN, S>;
+    uint16_t *__restrict__ g_out, uint16_t *__restrict__ u_out,
+    const uint16_t *__restrict__ g_in, const uint16_t *__restrict__ u_in, float l1) {
+    constexpr int NB = MODE == kDh ? 1 : 2;  // weight operands
+    using P = GU<BM, BN, WM, WN, S, NB>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int rows = rows_of(count, R_cap);
@@ -94,7 +103,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
         // the tile's own; the weight rows are the column block's
         const uint16_t *xb = rowlist ? x : x + (size_t)m0 * K;
         const uint64_t xbytes = (uint64_t)(rowlist ? xrows : rows - m0) * K * 2;
-        const uint16_t *gb = wg_t + (size_t)n0 * K, *ub = wu_t + (size_t)n0 * K;
+        const uint16_t *gb = wg_t + (size_t)n0 * K;
+        const uint16_t *ub = NB == 2 ? wu_t + (size_t)n0 * K : gb;
         // Load j of a wave fetches stage rows [16 (j NW + wave), +16): since
         // BM and BN are multiples of 16 NW, j alone decides the operand.
         uint32_t voff[P::NI];
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
             if (j * P::NW * 16 < BM) {
                 const int r = min(m0 + sr, rows - 1);
                 row_off = rowlist ? (uint32_t)rowlist[r] * K * 2 : (uint32_t)(r - m0) * K * 2;
-            } else if (j * P::NW * 16 < BM + BN) {
+            } else if (NB == 1 || j * P::NW * 16 < BM + BN) {
                 row_off = (uint32_t)(sr - BM) * K * 2;
             } else {
                 row_off = (uint32_t)(sr - BM - BN) * K * 2;
@@ -123,7 +133,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                 const int row0 = (j * P::NW + wave) * 16;
                 char *dst = st + row0 * kPRow;
                 if (j * P::NW * 16 < BM) dma16(rx, voff[j], soff, dst);
-                else if (j * P::NW * 16 < BM + BN) dma16(rg, voff[j], soff, dst);
+                else if (NB == 1 || j * P::NW * 16 < BM + BN) dma16(rg, voff[j], soff, dst);
                 else dma16(ru, voff[j], soff, dst);
             }
         };
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
 #pragma unroll
             for (int b = 0; b < P::FB; ++b) {
                 fg[buf][b] = frag(st, BM + wn * P::TN + b * 32, s, lane);
-                fu[buf][b] = frag(st, BM + BN + wn * P::TN + b * 32, s, lane);
+                if constexpr (NB == 2) fu[buf][b] = frag(st, BM + BN + wn * P::TN + b * 32, s, lane);
             }
         };
         auto mma = [&](int buf) {
@@ -151,7 +161,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
 #pragma unroll
                 for (int b = 0; b < P::FB; ++b) {
                     ag[a][b] = mfma32(fa[buf][a], fg[buf][b], ag[a][b]);
-                    au[a][b] = mfma32(fa[buf][a], fu[buf][b], au[a][b]);
+                    if constexpr (NB == 2) au[a][b] = mfma32(fa[buf][a], fu[buf][b], au[a][b]);
                 }
         };
         kloop_pipelined<S, P::NI>(0, KT, smem, P::STAGE, issue, load, mma);
@@ -163,13 +173,21 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                 if (r < rows) {
 #pragma unroll
                     for (int b = 0; b < P::FB; ++b) {
-                        const float g = ag[a][b][i] > 0.0f ? ag[a][b][i] : 0.0f;
-                        const float u = au[a][b][i];
                         const size_t o = (size_t)r * N + n0 + wn * P::TN + b * 32 + l32;
-                        h[o] = (uint16_t)f32_to_bf16(g * u);
-                        if constexpr (KEEP) {
-                            if (g_out) g_out[o] = (uint16_t)f32_to_bf16(g);
-                            if (u_out) u_out[o] = (uint16_t)f32_to_bf16(u);
+                        if constexpr (MODE == kDh) {
+                            const float dh = ag[a][b][i];
+                            const float gv = __uint_as_float((uint32_t)g_in[o] << 16);
+                            const float uv = __uint_as_float((uint32_t)u_in[o] << 16);
+                            h[o] = (uint16_t)f32_to_bf16(dh * gv);
+                            g_out[o] = (uint16_t)f32_to_bf16(gv > 0.0f ? dh * uv + l1 : 0.0f);
+                        } else {
+                            const float g = ag[a][b][i] > 0.0f ? ag[a][b][i] : 0.0f;
+                            const float u = au[a][b][i];
+                            h[o] = (uint16_t)f32_to_bf16(g * u);
+                            if constexpr (MODE == kKeep) {
+                                if (g_out) g_out[o] = (uint16_t)f32_to_bf16(g);
+                                if (u_out) u_out[o] = (uint16_t)f32_to_bf16(u);
+                            }
                         }
                     }
                 }
@@ -215,7 +233,8 @@ struct DN {
 // positions, i.e. all 64 banks once.
 __device__ __forceinline__ int bsw(int row) { return 4 * (row & 3); }
 
-template <int BM, int BN, int WM, int WN, int STG>
+// ACC: add the product into y (the unsplit epilogue) instead of storing it.
+template <int BM, int BN, int WM, int WN, int STG, bool ACC>
 __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ wd, int K, int N,
     const int32_t *__restrict__ rowlist, const int32_t *__restrict__ count, int R_cap,
@@ -319,8 +338,11 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
                     if (r < rows) {
                         const int yr = rowlist ? rowlist[r] : r;
 #pragma unroll
-                        for (int b = 0; b < P::FB; ++b)
-                            y[(size_t)yr * K + k0 + wn * P::TN + b * 32 + l32] = acc[a][b][i];
+                        for (int b = 0; b < P::FB; ++b) {
+                            float *yp = y + (size_t)yr * K + k0 + wn * P::TN + b * 32 + l32;
+                            if constexpr (ACC) *yp += acc[a][b][i];
+                            else *yp = acc[a][b][i];
+                        }
                     }
                 }
         } else {
@@ -348,7 +370,7 @@ template <int BM, int BN>
 __global__ __launch_bounds__(256) void split_reduce_kernel(
     const float *__restrict__ partial, const int32_t *__restrict__ rowlist,
     const int32_t *__restrict__ count, int R_cap, int K, int N, int grid_down,
-    float *__restrict__ y) {
+    float *__restrict__ y, int accum) {
     constexpr int kMaxSplit = 16;
     const int rows = rows_of(count, R_cap);
     const int nrb = (rows + BM - 1) / BM;
@@ -374,7 +396,15 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
                 sum.z += v[s2].z;
                 sum.w += v[s2].w;
             }
-        *reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col) = sum;
+        float4 *yp = reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col);
+        if (accum) {
+            const float4 old = *yp;
+            sum.x = old.x + sum.x;
+            sum.y = old.y + sum.y;
+            sum.z = old.z + sum.z;
+            sum.w = old.w + sum.w;
+        }
+        *yp = sum;
     }
 }
 
@@ -388,24 +418,26 @@ hipError_t set_lds(F *kernel, int bytes, bool &done) {
 }
 
 // A kernel instantiation with its shape constants.
-template <int BM, int BN, int WM, int WN, int S, bool KEEP = false>
-struct GuCfg : GU<BM, BN, WM, WN, S> {
+template <int BM, int BN, int WM, int WN, int S, int MODE = kGU>
+struct GuCfg : GU<BM, BN, WM, WN, S, MODE == kDh ? 1 : 2> {
     static constexpr int BM_ = BM, BN_ = BN;
-    static constexpr auto kernel = &gateup_kernel<BM, BN, WM, WN, S, KEEP>;
+    static constexpr auto kernel = &gateup_kernel<BM, BN, WM, WN, S, MODE>;
 };
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, bool ACC = false>
 struct DnCfg : DN<BM, BN, WM, WN, S> {
     static constexpr int BM_ = BM, BN_ = BN;
-    static constexpr auto kernel = &down_kernel<BM, BN, WM, WN, S>;
+    static constexpr auto kernel = &down_kernel<BM, BN, WM, WN, S, ACC>;
 };
 
 // dense comparator shapes and overflow-path shapes (the thin overflow
 // tiles do little matrix work per stage, so they keep more stages in flight)
 using GuDense = GuCfg<256, 128, 4, 2, 4>;
 using GuRows = GuCfg<128, 128, 2, 4, 4>;
-using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, true>;
+using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
+using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
 using DnDense = DnCfg<128, 128, 2, 2, 4>;
 using DnRows = DnCfg<128, 128, 2, 4, 6>;
+using DnRowsAcc = DnCfg<128, 128, 2, 4, 6, true>;
 constexpr int kSplitGrid = 256;  // work items of the split down GEMM
 
 }  // namespace
@@ -427,14 +459,16 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
         const int tiles = (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_);
         const int grid = tiles < 256 ? tiles : 256;
         hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
-                           wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr);
+                           wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr, nullptr,
+                           nullptr, 0.0f);
     } else {
         static bool attr = false;
         hipError_t e = set_lds(GuDense::kernel, GuDense::LDS, attr);
         if (e != hipSuccess) return e;
         const int grid = (R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_);
         hipLaunchKernelGGL(GuDense::kernel, dim3(grid), dim3(GuDense::NTH), GuDense::LDS, s, x,
-                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr);
+                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr,
+                           nullptr, nullptr, 0.0f);
     }
     return hipGetLastError();
 }
@@ -451,21 +485,45 @@ hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,
     const int tiles = (R_cap + GuRowsKeep::BM_ - 1) / GuRowsKeep::BM_ * (N / GuRowsKeep::BN_);
     const int grid = tiles < 256 ? tiles : 256;
     hipLaunchKernelGGL(GuRowsKeep::kernel, dim3(grid), dim3(GuRowsKeep::NTH), GuRowsKeep::LDS, s,
-                       x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, g_out, u_out);
+                       x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, g_out, u_out, nullptr,
+                       nullptr, 0.0f);
+    return hipGetLastError();
+}
+
+hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K, int N,
+                            const int32_t *rowlist, const int32_t *count, int R_cap,
+                            const uint16_t *g_in, const uint16_t *u_in, float l1,
+                            uint16_t *du, uint16_t *dz, hipStream_t s) {
+    if (R_cap <= 0) return hipSuccess;
+    static bool attr = false;
+    hipError_t e = set_lds(GuRowsDh::kernel, GuRowsDh::LDS, attr);
+    if (e != hipSuccess) return e;
+    const int tiles = (R_cap + GuRowsDh::BM_ - 1) / GuRowsDh::BM_ * (N / GuRowsDh::BN_);
+    const int grid = tiles < 256 ? tiles : 256;
+    hipLaunchKernelGGL(GuRowsDh::kernel, dim3(grid), dim3(GuRowsDh::NTH), GuRowsDh::LDS, s, dy,
+                       wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz, nullptr, g_in, u_in,
+                       l1);
     return hipGetLastError();
 }
 
 hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
-                       float *partial, hipStream_t s) {
+                       float *partial, hipStream_t s, bool accum) {
     if (R_cap <= 0) return hipSuccess;
-    if (partial) {
+    if (partial && accum) {
+        static bool attr = false;
+        hipError_t e = set_lds(DnRowsAcc::kernel, DnRowsAcc::LDS, attr);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(DnRowsAcc::kernel, dim3(kSplitGrid), dim3(DnRowsAcc::NTH),
+                           DnRowsAcc::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial);
+    } else if (partial) {
         static bool attr = false;
         hipError_t e = set_lds(DnRows::kernel, DnRows::LDS, attr);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(DnRows::kernel, dim3(kSplitGrid), dim3(DnRows::NTH), DnRows::LDS, s, h,
                            wd, K, N, rowlist, count, R_cap, y, partial);
     } else {
+        if (accum) return hipErrorInvalidValue;  // not instantiated: unsplit accumulate
         static bool attr = false;
         hipError_t e = set_lds(DnDense::kernel, DnDense::LDS, attr);
         if (e != hipSuccess) return e;
@@ -478,13 +536,13 @@ hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
 
 hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
                                const int32_t *count, int R_cap, int K, int N, float *y,
-                               hipStream_t s) {
+                               hipStream_t s, bool accum) {
     if (R_cap <= 0) return hipSuccess;
     // enough workgroups for the largest split case: at most kSplitGrid tiles
     int grid = (int)(((size_t)R_cap * K / 4 + 255) / 256);
     grid = grid < 1024 ? grid : 1024;
     hipLaunchKernelGGL((split_reduce_kernel<DnRows::BM_, DnRows::BN_>), dim3(grid), dim3(256), 0, s, partial,
-                       rowlist, count, R_cap, K, N, kSplitGrid, y);
+                       rowlist, count, R_cap, K, N, kSplitGrid, y, (int)accum);
     return hipGetLastError();
 }
 

@@ -43,8 +43,8 @@ __global__ __launch_bounds__(kThreads) void hybrid_pack_kernel(
     float *__restrict__ hy_val, int32_t *__restrict__ hy_idx, int32_t *__restrict__ hy_cnt,
     uint8_t *__restrict__ route) {
     const int lane = threadIdx.x & 63;
-    const int m = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (m >= M) return;  // wave-uniform; no block barrier below
+    const int m = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (m >= M) return;  // no block barrier below
 
     constexpr int kQ = 4;  // 64-tile chunks: N / T <= 256
     int c[kQ];
@@ -138,15 +138,18 @@ __global__ __launch_bounds__(1024) void route_compact_kernel(
     if (tid == 0) *bk_count = running;
 }
 
-// ------------------------ up at the stored entries --------------------------
+// ------------------------ dense-to-hybrid products --------------------------
+// p_s = a_m . w[j_s] at every stored entry s of a sparse row, then
+//   forward  (BWD false): a = x, w = W_u^T:  out1 = p (u, optional), out2 = p g (h)
+//   backward (BWD true):  a = dy, w = W_d:   out1 = p g (du), out2 = p u + l1 (dz)
 constexpr int kUpBatch = 4;  // entries gathered together per wave
 
-template <int KCH>
+template <int KCH, bool BWD>
 __global__ __launch_bounds__(kThreads) void hybrid_up_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wu_t, int K, int N, int P,
-    const float *__restrict__ hy_g, const int32_t *__restrict__ hy_idx,
-    const int32_t *__restrict__ hy_cnt, const uint8_t *__restrict__ route,
-    float *__restrict__ hy_u, float *__restrict__ hy_h) {
+    const float *__restrict__ hy_g, const float *__restrict__ hy_uin, float l1,
+    const int32_t *__restrict__ hy_idx, const int32_t *__restrict__ hy_cnt,
+    const uint8_t *__restrict__ route, float *__restrict__ hy_u, float *__restrict__ hy_h) {
     const int m = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (route[m]) return;  // backup row: the dense path computes it
@@ -166,12 +169,13 @@ __global__ __launch_bounds__(kThreads) void hybrid_up_kernel(
         // lane resolves entry e0 + lane
         const int f = wave + kWaves * (e0 + lane);
         int jl = 0;
-        float gl = 0.0f, ul = 0.0f;
+        float gl = 0.0f, ul = 0.0f, uin = 0.0f;
         if (e0 + lane < ne) {
             // an index outside [0, N) can only come from corrupt storage;
             // clamp it so that the gather stays inside the weights
             jl = min((unsigned)hy_idx[row + f], (unsigned)(N - 1));
             gl = hy_g[row + f];
+            if constexpr (BWD) uin = hy_uin[row + f];
         }
         const int nb = min(64, ne - e0);
         for (int b = 0; b < nb; b += kUpBatch) {
@@ -204,20 +208,29 @@ __global__ __launch_bounds__(kThreads) void hybrid_up_kernel(
             }
         }
         if (e0 + lane < ne) {
-            if (hy_u) hy_u[row + f] = ul;
-            hy_h[row + f] = ul * gl;
+            if constexpr (BWD) {
+                hy_u[row + f] = ul * gl;
+                hy_h[row + f] = ul * uin + l1;
+            } else {
+                if (hy_u) hy_u[row + f] = ul;
+                hy_h[row + f] = ul * gl;
+            }
         }
     }
 }
 
-// ------------------------- down from the stored entries ---------------------
-constexpr int kDnBatch = 4;
-
-template <int KCH>
+// ------------------------- hybrid-to-dense products -------------------------
+// out_m = sum over stored s of v1_s w1[j_s] (+ v2_s w2[j_s] with TWO):
+//   forward:  v1 = h, w1 = W_d (y);  backward: v1 = du, w1 = W_u^T, v2 = dz,
+//   w2 = W_g^T (dx).  TWO gathers two rows per entry, so it takes half as
+//   many entries at a time.
+template <int KCH, bool TWO>
 __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
-    const uint16_t *__restrict__ wd, int K, int N, int P, const float *__restrict__ hy_h,
+    const uint16_t *__restrict__ wd, const uint16_t *__restrict__ w2, int K, int N, int P,
+    const float *__restrict__ hy_h, const float *__restrict__ v2,
     const int32_t *__restrict__ hy_idx, const int32_t *__restrict__ hy_cnt,
     const uint8_t *__restrict__ route, float *__restrict__ y) {
+    constexpr int kDnBatch = TWO ? 2 : 4;
     extern __shared__ __attribute__((aligned(16))) char smem[];  // y staging, fp32
     const int m = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -240,16 +253,17 @@ __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
     const int ne = (n - wave + kWaves - 1) / kWaves;
     for (int e0 = 0; e0 < ne; e0 += 64) {
         int jl = 0;
-        float hl = 0.0f;
+        float hl = 0.0f, hl2 = 0.0f;
         if (e0 + lane < ne) {
             const int f = wave + kWaves * (e0 + lane);
             jl = min((unsigned)hy_idx[row + f], (unsigned)(N - 1));
             hl = hy_h[row + f];
+            if constexpr (TWO) hl2 = v2[row + f];
         }
         const int nb = min(64, ne - e0);
         for (int b = 0; b < nb; b += kDnBatch) {
             int j[kDnBatch];
-            float h[kDnBatch];
+            float h[kDnBatch], h2[kDnBatch];
 #pragma unroll
             for (int u = 0; u < kDnBatch; ++u) {
                 const bool ok = b + u < nb;
@@ -257,8 +271,11 @@ __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
                 j[u] = __builtin_amdgcn_readlane(jl, src);
                 h[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl), src))
                           : 0.0f;
+                h2[u] = ok && TWO
+                            ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl2), src))
+                            : 0.0f;
             }
-            u32x4 wv[kDnBatch][KCH];
+            u32x4 wv[kDnBatch][KCH], wv2[TWO ? kDnBatch : 1][KCH];
 #pragma unroll
             for (int u = 0; u < kDnBatch; ++u) {
                 const uint16_t *pd = wd + (size_t)j[u] * K;
@@ -266,6 +283,14 @@ __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
                 for (int ch = 0; ch < KCH; ++ch) {
                     const int q = lane + 64 * ch;
                     wv[u][ch] = q < KC ? ld16(pd + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+                }
+                if constexpr (TWO) {
+                    const uint16_t *p2 = w2 + (size_t)j[u] * K;
+#pragma unroll
+                    for (int ch = 0; ch < KCH; ++ch) {
+                        const int q = lane + 64 * ch;
+                        wv2[u][ch] = q < KC ? ld16(p2 + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+                    }
                 }
             }
 #pragma unroll
@@ -276,6 +301,10 @@ __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
                     for (int w = 0; w < 4; ++w) {
                         yacc[ch][2 * w] += h[u] * bf_lo(wv[u][ch][w]);
                         yacc[ch][2 * w + 1] += h[u] * bf_hi(wv[u][ch][w]);
+                        if constexpr (TWO) {
+                            yacc[ch][2 * w] += h2[u] * bf_lo(wv2[u][ch][w]);
+                            yacc[ch][2 * w + 1] += h2[u] * bf_hi(wv2[u][ch][w]);
+                        }
                     }
         }
     }
@@ -307,29 +336,259 @@ __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
     }
 }
 
-template <int KCH>
+// ------------------------------ hybrid transpose ----------------------------
+// Column lists of the stored activations, for the weight gradients: every
+// stored entry of a sparse row (id = m P + s) and every active entry of a
+// listed backup row (id = M P + r N + j, active where its bf16 gate is
+// positive), grouped by hidden column j and, within a column, in ascending
+// row order (so the gradient sums have a fixed order).  Counts (atomic, order
+// free), an exclusive scan to column offsets, a scatter through per-column
+// cursors (order within a column depends on timing), then a per-column rank
+// sort by row (rows are unique within a column).
+__global__ __launch_bounds__(kThreads) void fill_i32_kernel(int32_t *__restrict__ p, int n,
+                                                             int32_t v) {
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = v;
+}
+
+__device__ __forceinline__ bool bf16_positive(uint16_t b) { return b != 0 && b < 0x8000u; }
+
+// SCATTER false: count entries per column; true: place (row, id) through the
+// cursors.  Workgroups [0, ceil(M / 4)) take sparse rows (a wave each), the
+// next R_max take backup slots (a workgroup each; slots past the device-side
+// backup count exit).
+template <bool SCATTER>
+__global__ __launch_bounds__(kThreads) void tr_place_kernel(
+    int M, int N, int P, const int32_t *__restrict__ hy_idx, const int32_t *__restrict__ hy_cnt,
+    const uint8_t *__restrict__ route, const int32_t *__restrict__ bk_rows,
+    const int32_t *__restrict__ bk_count, int R_max, const uint16_t *__restrict__ bk_g,
+    int32_t *__restrict__ col, int32_t *__restrict__ ent_row, int32_t *__restrict__ ent_id) {
+    const int nrb = (M + kWaves - 1) / kWaves;
+    const int lane = threadIdx.x & 63;
+    if ((int)blockIdx.x < nrb) {
+        const int m = blockIdx.x * kWaves + (threadIdx.x >> 6);
+        if (m >= M || route[m]) return;
+        const int n = min(hy_cnt[m], P);
+        for (int s = lane; s < n; s += 64) {
+            const int j = min((unsigned)hy_idx[(size_t)m * P + s], (unsigned)(N - 1));
+            if constexpr (SCATTER) {
+                const int pos = atomicAdd(&col[j], 1);
+                ent_row[pos] = m;
+                ent_id[pos] = m * P + s;
+            } else {
+                atomicAdd(&col[j], 1);
+            }
+        }
+        return;
+    }
+    const int r = blockIdx.x - nrb;
+    if (r >= min(*bk_count, R_max)) return;
+    const int m = bk_rows[r];
+    const uint16_t *g = bk_g + (size_t)r * N;
+    for (int j = threadIdx.x; j < N; j += kThreads) {
+        if (!bf16_positive(g[j])) continue;
+        if constexpr (SCATTER) {
+            const int pos = atomicAdd(&col[j], 1);
+            ent_row[pos] = m;
+            ent_id[pos] = M * P + r * N + j;
+        } else {
+            atomicAdd(&col[j], 1);
+        }
+    }
+}
+
+// col_ptr = exclusive scan of the counts (col_ptr[N] = total); the counts
+// become the scatter cursors (each column's start).
+__global__ __launch_bounds__(1024) void tr_scan_kernel(int32_t *__restrict__ col, int N,
+                                                       int32_t *__restrict__ col_ptr) {
+    __shared__ int s_wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int running = 0;
+    for (int base = 0; base < N; base += 1024) {
+        const int j = base + tid;
+        const int c = j < N ? col[j] : 0;
+        int incl = c;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+        }
+        if (lane == 63) s_wsum[wave] = incl;
+        __syncthreads();
+        int wbase = 0, total = 0;
+        for (int q = 0; q < 16; ++q) {
+            const int v = s_wsum[q];
+            if (q < wave) wbase += v;
+            total += v;
+        }
+        if (j < N) {
+            const int start = running + wbase + incl - c;
+            col_ptr[j] = start;
+            col[j] = start;
+        }
+        running += total;
+        __syncthreads();
+    }
+    if (tid == 0) col_ptr[N] = running;
+}
+
+// One wave per column: the rank of an entry is the number of the column's
+// entries with a smaller row; 64 keys at a time are held in a register and
+// compared through lane reads.
+__global__ __launch_bounds__(kThreads) void tr_sort_kernel(
+    int N, const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ ent_row,
+    const int32_t *__restrict__ ent_id, int32_t *__restrict__ srt_row,
+    int32_t *__restrict__ srt_id) {
+    const int j = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (j >= N) return;
+    const int lane = threadIdx.x & 63;
+    const int p0 = col_ptr[j], n = col_ptr[j + 1] - p0;
+    for (int c = 0; c < n; c += 64) {
+        const int i = c + lane;
+        const int my = i < n ? ent_row[p0 + i] : 0x7fffffff;
+        int rank = 0;
+        for (int c2 = 0; c2 < n; c2 += 64) {
+            const int key = c2 + lane < n ? ent_row[p0 + c2 + lane] : 0x7fffffff;
+            const int nk = min(64, n - c2);
+            for (int t = 0; t < nk; ++t) rank += __builtin_amdgcn_readlane(key, t) < my ? 1 : 0;
+        }
+        if (i < n) {
+            srt_row[p0 + rank] = my;
+            srt_id[p0 + rank] = ent_id[p0 + i];
+        }
+    }
+}
+
+// --------------------------- weight gradients --------------------------------
+// One wave per hidden column j (and K-slice of up to KS 16-byte chunks per
+// lane): over the column's entries in ascending row order,
+//   dwd[j] += h dy_m,   dwu_t[j] += du x_m,   dwg_t[j] += dz x_m
+// gathering the dy and x rows (bf16, coalesced 1 KB per wave and chunk);
+// values come from the sparse rows' fp32 storage or the backup rows' bf16
+// rows.  fp32 accumulation; every output row is written (zeros for columns
+// with no entry).
+constexpr int kDwBatch = 2;
+
+__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+template <int KS>
+__global__ __launch_bounds__(kThreads) void dw_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ dy, int M, int K, int N, int P,
+    const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ srt_row,
+    const int32_t *__restrict__ srt_id, const float *__restrict__ hy_h,
+    const float *__restrict__ hy_du, const float *__restrict__ hy_dz,
+    const uint16_t *__restrict__ bk_h, const uint16_t *__restrict__ bk_du,
+    const uint16_t *__restrict__ bk_dz, float *__restrict__ dwg_t, float *__restrict__ dwu_t,
+    float *__restrict__ dwd) {
+    const int j = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (j >= N) return;
+    const int lane = threadIdx.x & 63;
+    const int KC = K >> 3;
+    const int q0 = blockIdx.y * KS * 64;  // first chunk of this K-slice
+    const size_t MP = (size_t)M * P;
+    float ad[KS][8], au[KS][8], ag[KS][8];
+#pragma unroll
+    for (int c = 0; c < KS; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ad[c][e] = au[c][e] = ag[c][e] = 0.0f;
+
+    const int p0 = col_ptr[j], n = col_ptr[j + 1] - p0;
+    for (int e0 = 0; e0 < n; e0 += 64) {
+        int ml = 0;
+        float hl = 0.0f, ul = 0.0f, zl = 0.0f;
+        if (e0 + lane < n) {
+            ml = min((unsigned)srt_row[p0 + e0 + lane], (unsigned)(M - 1));
+            const size_t id = (size_t)srt_id[p0 + e0 + lane];
+            if (id < MP) {
+                hl = hy_h[id];
+                ul = hy_du[id];
+                zl = hy_dz[id];
+            } else {
+                const size_t b = id - MP;
+                hl = bf16_val(bk_h[b]);
+                ul = bf16_val(bk_du[b]);
+                zl = bf16_val(bk_dz[b]);
+            }
+        }
+        const int nb = min(64, n - e0);
+        for (int b = 0; b < nb; b += kDwBatch) {
+            int m[kDwBatch];
+            float h[kDwBatch], du[kDwBatch], dz[kDwBatch];
+#pragma unroll
+            for (int u = 0; u < kDwBatch; ++u) {
+                const bool ok = b + u < nb;
+                const int src = ok ? b + u : b;
+                m[u] = __builtin_amdgcn_readlane(ml, src);
+                h[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl), src)) : 0.0f;
+                du[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ul), src)) : 0.0f;
+                dz[u] = ok ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zl), src)) : 0.0f;
+            }
+            u32x4 gy[kDwBatch][KS], gx[kDwBatch][KS];
+#pragma unroll
+            for (int u = 0; u < kDwBatch; ++u)
+#pragma unroll
+                for (int c = 0; c < KS; ++c) {
+                    const int q = q0 + lane + 64 * c;
+                    const bool in = q < KC;
+                    gy[u][c] = in ? ld16(dy + (size_t)m[u] * K + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+                    gx[u][c] = in ? ld16(x + (size_t)m[u] * K + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+            for (int u = 0; u < kDwBatch; ++u)
+#pragma unroll
+                for (int c = 0; c < KS; ++c)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        ad[c][2 * w] += h[u] * bf_lo(gy[u][c][w]);
+                        ad[c][2 * w + 1] += h[u] * bf_hi(gy[u][c][w]);
+                        au[c][2 * w] += du[u] * bf_lo(gx[u][c][w]);
+                        au[c][2 * w + 1] += du[u] * bf_hi(gx[u][c][w]);
+                        ag[c][2 * w] += dz[u] * bf_lo(gx[u][c][w]);
+                        ag[c][2 * w + 1] += dz[u] * bf_hi(gx[u][c][w]);
+                    }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < KS; ++c) {
+        const int q = q0 + lane + 64 * c;
+        if (q >= KC) continue;
+        const size_t o = (size_t)j * K + 8 * q;
+        float *outs[3] = {dwd + o, dwu_t + o, dwg_t + o};
+        const float(*acc[3])[8] = {ad, au, ag};
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            st16(outs[t], u32x4{__float_as_uint(acc[t][c][0]), __float_as_uint(acc[t][c][1]),
+                                __float_as_uint(acc[t][c][2]), __float_as_uint(acc[t][c][3])});
+            st16(outs[t] + 4, u32x4{__float_as_uint(acc[t][c][4]), __float_as_uint(acc[t][c][5]),
+                                    __float_as_uint(acc[t][c][6]), __float_as_uint(acc[t][c][7])});
+        }
+    }
+}
+
+template <int KCH, bool BWD>
 hipError_t launch_up_k(const uint16_t *x, const uint16_t *wu_t, int M, int K, int N, int P,
-                       const float *hy_g, const int32_t *hy_idx, const int32_t *hy_cnt,
-                       const uint8_t *route, float *hy_u, float *hy_h, hipStream_t s) {
-    hipLaunchKernelGGL(hybrid_up_kernel<KCH>, dim3(M), dim3(kThreads), 0, s, x, wu_t, K, N, P,
-                       hy_g, hy_idx, hy_cnt, route, hy_u, hy_h);
+                       const float *hy_g, const float *hy_uin, float l1, const int32_t *hy_idx,
+                       const int32_t *hy_cnt, const uint8_t *route, float *hy_u, float *hy_h,
+                       hipStream_t s) {
+    hipLaunchKernelGGL((hybrid_up_kernel<KCH, BWD>), dim3(M), dim3(kThreads), 0, s, x, wu_t, K,
+                       N, P, hy_g, hy_uin, l1, hy_idx, hy_cnt, route, hy_u, hy_h);
     return hipGetLastError();
 }
 
-template <int KCH>
-hipError_t launch_down_k(const uint16_t *wd, int M, int K, int N, int P, const float *hy_h,
-                         const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
-                         float *y, hipStream_t s) {
+template <int KCH, bool TWO>
+hipError_t launch_down_k(const uint16_t *wd, const uint16_t *w2, int M, int K, int N, int P,
+                         const float *hy_h, const float *v2, const int32_t *hy_idx,
+                         const int32_t *hy_cnt, const uint8_t *route, float *y, hipStream_t s) {
     const size_t lds = (size_t)kWaves * KCH * 512 * sizeof(float);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&hybrid_down_kernel<KCH>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&hybrid_down_kernel<KCH, TWO>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(hybrid_down_kernel<KCH>, dim3(M), dim3(kThreads), lds, s, wd, K, N, P,
-                       hy_h, hy_idx, hy_cnt, route, y);
+    hipLaunchKernelGGL((hybrid_down_kernel<KCH, TWO>), dim3(M), dim3(kThreads), lds, s, wd, w2,
+                       K, N, P, hy_h, v2, hy_idx, hy_cnt, route, y);
     return hipGetLastError();
 }
 
@@ -367,18 +626,117 @@ hipError_t launch_hybrid_up(const uint16_t *x, const uint16_t *wu_t, int M, int 
                             const float *hy_g, const int32_t *hy_idx, const int32_t *hy_cnt,
                             const uint8_t *route, float *hy_u, float *hy_h, hipStream_t s) {
     if (M == 0) return hipSuccess;
-#define TW_UP(k) launch_up_k<k>(x, wu_t, M, K, N, P, hy_g, hy_idx, hy_cnt, route, hy_u, hy_h, s)
+#define TW_UP(k) \
+    launch_up_k<k, false>(x, wu_t, M, K, N, P, hy_g, nullptr, 0.0f, hy_idx, hy_cnt, route, hy_u, \
+                          hy_h, s)
     TW_KCH_SWITCH(K, TW_UP)
 #undef TW_UP
+}
+
+hipError_t launch_hybrid_dh(const uint16_t *dy, const uint16_t *wd, int M, int K, int N, int P,
+                            const float *hy_g, const float *hy_u, float l1, const int32_t *hy_idx,
+                            const int32_t *hy_cnt, const uint8_t *route, float *hy_du,
+                            float *hy_dz, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+#define TW_DH(k) \
+    launch_up_k<k, true>(dy, wd, M, K, N, P, hy_g, hy_u, l1, hy_idx, hy_cnt, route, hy_du, \
+                         hy_dz, s)
+    TW_KCH_SWITCH(K, TW_DH)
+#undef TW_DH
 }
 
 hipError_t launch_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const float *hy_h,
                               const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
                               float *y, hipStream_t s) {
     if (M == 0) return hipSuccess;
-#define TW_DN(k) launch_down_k<k>(wd, M, K, N, P, hy_h, hy_idx, hy_cnt, route, y, s)
+#define TW_DN(k) \
+    launch_down_k<k, false>(wd, nullptr, M, K, N, P, hy_h, nullptr, hy_idx, hy_cnt, route, y, s)
     TW_KCH_SWITCH(K, TW_DN)
 #undef TW_DN
+}
+
+hipError_t launch_hybrid_dx(const uint16_t *wu_t, const uint16_t *wg_t, int M, int K, int N,
+                            int P, const float *hy_du, const float *hy_dz,
+                            const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                            float *dx, hipStream_t s) {
+    if (M == 0) return hipSuccess;
+#define TW_DX(k) \
+    launch_down_k<k, true>(wu_t, wg_t, M, K, N, P, hy_du, hy_dz, hy_idx, hy_cnt, route, dx, s)
+    TW_KCH_SWITCH(K, TW_DX)
+#undef TW_DX
+}
+
+size_t hybrid_transpose_bytes(int M, int N, int P, int R_max) {
+    const size_t cap = (size_t)M * P + (size_t)R_max * N;
+    auto up = [](size_t v) { return (v + 63) / 64 * 64; };
+    return up((size_t)N * 4) + up((size_t)(N + 1) * 4) + 4 * up(cap * 4);
+}
+
+hipError_t launch_hybrid_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
+                            const float *hy_h, const float *hy_du, const float *hy_dz,
+                            const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                            const int32_t *bk_rows, const int32_t *bk_count, int R_max,
+                            const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
+                            const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
+                            void *ws, hipStream_t s, hipEvent_t ev_mid) {
+    const size_t cap = (size_t)M * P + (size_t)R_max * N;
+    auto up = [](size_t v) { return (v + 63) / 64 * 64; };
+    char *w = static_cast<char *>(ws);
+    int32_t *col = reinterpret_cast<int32_t *>(w);
+    w += up((size_t)N * 4);
+    int32_t *col_ptr = reinterpret_cast<int32_t *>(w);
+    w += up((size_t)(N + 1) * 4);
+    int32_t *ent_row = reinterpret_cast<int32_t *>(w);
+    w += up(cap * 4);
+    int32_t *ent_id = reinterpret_cast<int32_t *>(w);
+    w += up(cap * 4);
+    int32_t *srt_row = reinterpret_cast<int32_t *>(w);
+    w += up(cap * 4);
+    int32_t *srt_id = reinterpret_cast<int32_t *>(w);
+
+    const int fill_grid = (N + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_grid < 1024 ? fill_grid : 1024), dim3(kThreads),
+                       0, s, col, N, 0);
+    const int place_grid = (M + kWaves - 1) / kWaves + R_max;
+    if (place_grid > 0) {
+        hipLaunchKernelGGL(tr_place_kernel<false>, dim3(place_grid), dim3(kThreads), 0, s, M, N,
+                           P, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max, bk_g, col, ent_row,
+                           ent_id);
+    }
+    hipLaunchKernelGGL(tr_scan_kernel, dim3(1), dim3(1024), 0, s, col, N, col_ptr);
+    if (place_grid > 0) {
+        hipLaunchKernelGGL(tr_place_kernel<true>, dim3(place_grid), dim3(kThreads), 0, s, M, N, P,
+                           hy_idx, hy_cnt, route, bk_rows, bk_count, R_max, bk_g, col, ent_row,
+                           ent_id);
+    }
+    const int cgrid = (N + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(tr_sort_kernel, dim3(cgrid), dim3(kThreads), 0, s, N, col_ptr, ent_row,
+                       ent_id, srt_row, srt_id);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (ev_mid) {
+        e = hipEventRecord(ev_mid, s);
+        if (e != hipSuccess) return e;
+    }
+    const int KCH = (K + 511) / 512;
+    if (KCH <= 4) {
+#define TW_DW(ks)                                                                               \
+    hipLaunchKernelGGL(dw_kernel<ks>, dim3(cgrid, 1), dim3(kThreads), 0, s, x, dy, M, K, N, P,   \
+                       col_ptr, srt_row, srt_id, hy_h, hy_du, hy_dz, bk_h, bk_du, bk_dz, dwg_t, \
+                       dwu_t, dwd)
+        switch (KCH) {
+        case 1: TW_DW(1); break;
+        case 2: TW_DW(2); break;
+        case 3: TW_DW(3); break;
+        default: TW_DW(4); break;
+        }
+#undef TW_DW
+    } else {
+        hipLaunchKernelGGL(dw_kernel<4>, dim3(cgrid, (KCH + 3) / 4), dim3(kThreads), 0, s, x, dy,
+                           M, K, N, P, col_ptr, srt_row, srt_id, hy_h, hy_du, hy_dz, bk_h, bk_du,
+                           bk_dz, dwg_t, dwu_t, dwd);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace tw

@@ -405,4 +405,144 @@ tw_status tw_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const f
     return TW_OK;
 }
 
+tw_status tw_hybrid_bwd_dh(const uint16_t *dy, const uint16_t *wd, int M, int K, int N, int P,
+                           float l1, const float *hy_g, const float *hy_u, const int32_t *hy_idx,
+                           const int32_t *hy_cnt, const uint8_t *route, const int32_t *bk_rows,
+                           const int32_t *bk_count, int R_max, const uint16_t *bk_g,
+                           const uint16_t *bk_u, float *hy_du, float *hy_dz, uint16_t *bk_du,
+                           uint16_t *bk_dz, void *stream, void *const *events) {
+    TW_TRY(check_hybrid(M, K, N, 128, 1, P, R_max));
+    TW_NEED_M(dy);
+    TW_NEED(wd);
+    TW_NEED_M(hy_g);
+    TW_NEED_M(hy_u);
+    TW_NEED_M(hy_idx);
+    TW_NEED_M(hy_cnt);
+    TW_NEED_M(route);
+    TW_NEED(bk_rows);
+    TW_NEED(bk_count);
+    TW_NEED_M(hy_du);
+    TW_NEED_M(hy_dz);
+    if (R_max > 0) {
+        TW_NEED(bk_g);
+        TW_NEED(bk_u);
+        TW_NEED(bk_du);
+        TW_NEED(bk_dz);
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_hybrid_dh(dy, wd, M, K, N, P, hy_g, hy_u, l1, hy_idx, hy_cnt, route,
+                                         hy_du, hy_dz, s),
+                    "hybrid dh launch"));
+    TW_TRY(record(events, 1, s));
+    if (R_max > 0)
+        TW_TRY(launched(tw::launch_backup_dh(dy, M, wd, K, N, bk_rows, bk_count, R_max, bk_g, bk_u,
+                                             l1, bk_du, bk_dz, s),
+                        "backup dh launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+size_t tw_hybrid_bwd_dx_workspace_bytes(int R_max) { return tw_hybrid_down_workspace_bytes(R_max); }
+
+tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, int K, int N, int P,
+                           const float *hy_du, const float *hy_dz, const int32_t *hy_idx,
+                           const int32_t *hy_cnt, const uint8_t *route, const int32_t *bk_rows,
+                           const int32_t *bk_count, int R_max, const uint16_t *bk_du,
+                           const uint16_t *bk_dz, float *dx, void *ws, size_t ws_bytes,
+                           void *stream, void *const *events) {
+    TW_TRY(check_hybrid(M, K, N, 128, 1, P, R_max));
+    TW_NEED(wg_t);
+    TW_NEED(wu_t);
+    TW_NEED_M(hy_du);
+    TW_NEED_M(hy_dz);
+    TW_NEED_M(hy_idx);
+    TW_NEED_M(hy_cnt);
+    TW_NEED_M(route);
+    TW_NEED(bk_rows);
+    TW_NEED(bk_count);
+    TW_NEED_M(dx);
+    const size_t need = tw_hybrid_bwd_dx_workspace_bytes(R_max);
+    if (R_max > 0) {
+        TW_NEED(bk_du);
+        TW_NEED(bk_dz);
+        TW_NEED(ws);
+    }
+    if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_hybrid_dx(wu_t, wg_t, M, K, N, P, hy_du, hy_dz, hy_idx, hy_cnt,
+                                         route, dx, s),
+                    "hybrid dx launch"));
+    TW_TRY(record(events, 1, s));
+    if (R_max > 0) {
+        // dx = du W_u^T, then dx += dz W_g^T: two split GEMMs over the backup
+        // rows, each summed in split order
+        float *partial = static_cast<float *>(ws);
+        TW_TRY(launched(tw::launch_down(bk_du, wu_t, K, N, bk_rows, bk_count, R_max, dx, partial, s),
+                        "backup dx (up) launch"));
+        TW_TRY(launched(tw::launch_split_reduce(partial, bk_rows, bk_count, R_max, K, N, dx, s),
+                        "backup dx (up) split-reduce launch"));
+        TW_TRY(launched(tw::launch_down(bk_dz, wg_t, K, N, bk_rows, bk_count, R_max, dx, partial, s,
+                                        true),
+                        "backup dx (gate) launch"));
+        TW_TRY(launched(tw::launch_split_reduce(partial, bk_rows, bk_count, R_max, K, N, dx, s,
+                                                true),
+                        "backup dx (gate) split-reduce launch"));
+    }
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+size_t tw_hybrid_bwd_dw_workspace_bytes(int M, int N, int P, int R_max) {
+    if (M < 0 || N <= 0 || P < 1 || R_max < 0) return 0;
+    return tw::hybrid_transpose_bytes(M, N, P, R_max) + 256;
+}
+
+tw_status tw_hybrid_bwd_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
+                           const float *hy_h, const float *hy_du, const float *hy_dz,
+                           const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                           const int32_t *bk_rows, const int32_t *bk_count, int R_max,
+                           const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
+                           const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
+                           void *ws, size_t ws_bytes, void *stream, void *const *events) {
+    TW_TRY(check_hybrid(M, K, N, 128, 1, P, R_max));
+    if ((int64_t)M * P + (int64_t)R_max * N >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "M*P + R_max*N = %lld stored entries: at most 2^31 - 1",
+                    (long long)M * P + (long long)R_max * N);
+    TW_NEED_M(x);
+    TW_NEED_M(dy);
+    TW_NEED_M(hy_h);
+    TW_NEED_M(hy_du);
+    TW_NEED_M(hy_dz);
+    TW_NEED_M(hy_idx);
+    TW_NEED_M(hy_cnt);
+    TW_NEED_M(route);
+    TW_NEED(bk_rows);
+    TW_NEED(bk_count);
+    TW_NEED(dwg_t);
+    TW_NEED(dwu_t);
+    TW_NEED(dwd);
+    TW_NEED(ws);
+    if (R_max > 0) {
+        TW_NEED(bk_g);
+        TW_NEED(bk_h);
+        TW_NEED(bk_du);
+        TW_NEED(bk_dz);
+    }
+    const size_t need = tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max);
+    if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    TW_TRY(record(events, 0, s));
+    hipEvent_t mid = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+    TW_TRY(launched(tw::launch_hybrid_dw(x, dy, M, K, N, P, hy_h, hy_du, hy_dz, hy_idx, hy_cnt,
+                                         route, bk_rows, bk_count, R_max, bk_g, bk_h, bk_du,
+                                         bk_dz, dwg_t, dwu_t, dwd, ws, s, mid),
+                    "weight-gradient launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
 }  // extern "C"

@@ -53,16 +53,25 @@ hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,
                               const int32_t *count, int R_cap, uint16_t *h, uint16_t *g_out,
                               uint16_t *u_out, hipStream_t s);
 
+// Backward of the backup rows' activations: dh = dy_r . wd[n] on the matrix
+// cores (one weight operand), then du[r][n] = bf16(dh g) and dz[r][n] =
+// bf16(g > 0 ? dh u + l1 : 0) with the row's stored bf16 g_in, u_in.
+hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K, int N,
+                            const int32_t *rowlist, const int32_t *count, int R_cap,
+                            const uint16_t *g_in, const uint16_t *u_in, float l1,
+                            uint16_t *du, uint16_t *dz, hipStream_t s);
+
 // y[row_r][k] = sum_n h[r][n] * wd[n][k] (fp32) for r < rows, with row_r =
-// rowlist[r] or r as above.  With a `partial` buffer (split_partial_bytes())
-// the reduction is split when there are few rows, and launch_split_reduce
-// must follow on the stream to sum the partial tiles into y.
+// rowlist[r] or r as above (accum: y[row_r][k] += that sum instead).  With a
+// `partial` buffer (split_partial_bytes()) the reduction is split when there
+// are few rows, and launch_split_reduce (with the same accum) must follow on
+// the stream to sum the partial tiles into y.
 hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
-                       float *partial, hipStream_t s);
+                       float *partial, hipStream_t s, bool accum = false);
 hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
                                const int32_t *count, int R_cap, int K, int N, float *y,
-                               hipStream_t s);
+                               hipStream_t s, bool accum = false);
 size_t split_partial_bytes();
 
 // Hybrid storage of the training forward (hybrid.hip).
@@ -77,5 +86,23 @@ hipError_t launch_hybrid_up(const uint16_t *x, const uint16_t *wu_t, int M, int 
 hipError_t launch_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const float *hy_h,
                               const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
                               float *y, hipStream_t s);
+// Backward over hybrid storage: du, dz at the stored entries of sparse rows;
+// dx of sparse rows; the transpose and weight gradients (all rows).
+hipError_t launch_hybrid_dh(const uint16_t *dy, const uint16_t *wd, int M, int K, int N, int P,
+                            const float *hy_g, const float *hy_u, float l1, const int32_t *hy_idx,
+                            const int32_t *hy_cnt, const uint8_t *route, float *hy_du,
+                            float *hy_dz, hipStream_t s);
+hipError_t launch_hybrid_dx(const uint16_t *wu_t, const uint16_t *wg_t, int M, int K, int N,
+                            int P, const float *hy_du, const float *hy_dz,
+                            const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                            float *dx, hipStream_t s);
+size_t hybrid_transpose_bytes(int M, int N, int P, int R_max);
+hipError_t launch_hybrid_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
+                            const float *hy_h, const float *hy_du, const float *hy_dz,
+                            const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                            const int32_t *bk_rows, const int32_t *bk_count, int R_max,
+                            const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
+                            const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
+                            void *ws, hipStream_t s, hipEvent_t ev_mid);
 
 }  // namespace tw

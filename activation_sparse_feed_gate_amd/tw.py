@@ -9,8 +9,10 @@ Low-level functions carry the C names and take preallocated tensors:
 ``tw_pack_gate``, ``tw_sparse_ffn_fwd``, ``tw_ffn_fwd``, ``tw_workspace_bytes``,
 ``tw_ffn_workspace_bytes``, ``tw_gate_dense``, ``tw_pack_dense`` and the
 hybrid training storage ``tw_hybrid_pack``, ``tw_hybrid_up``,
-``tw_hybrid_down``.  ``pack_gate``, ``pack_unfused``, ``sparse_ffn``, ``ffn``
-and ``hybrid_forward`` allocate their outputs and return them.
+``tw_hybrid_down`` with its backward ``tw_hybrid_bwd_dh``, ``tw_hybrid_bwd_dx``,
+``tw_hybrid_bwd_dw``.  ``pack_gate``, ``pack_unfused``, ``sparse_ffn``, ``ffn``,
+``hybrid_forward`` and ``hybrid_backward`` allocate their outputs and return
+them.
 """
 from __future__ import annotations
 
@@ -66,6 +68,19 @@ _lib.tw_hybrid_down_workspace_bytes.argtypes = [_i]
 _lib.tw_hybrid_down.restype = _i
 _lib.tw_hybrid_down.argtypes = [_vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp,
                                 _vp, _sz, _vp, _vp]
+_lib.tw_hybrid_bwd_dh.restype = _i
+_lib.tw_hybrid_bwd_dh.argtypes = [_vp, _vp, _i, _i, _i, _i, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.tw_hybrid_bwd_dx_workspace_bytes.restype = _sz
+_lib.tw_hybrid_bwd_dx_workspace_bytes.argtypes = [_i]
+_lib.tw_hybrid_bwd_dx.restype = _i
+_lib.tw_hybrid_bwd_dx.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _i, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
+_lib.tw_hybrid_bwd_dw_workspace_bytes.restype = _sz
+_lib.tw_hybrid_bwd_dw_workspace_bytes.argtypes = [_i] * 4
+_lib.tw_hybrid_bwd_dw.restype = _i
+_lib.tw_hybrid_bwd_dw.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
 
 TW_OK, TW_EINVAL, TW_EUNSUPPORTED, TW_EHIP = 0, 1, 2, 3
 
@@ -229,6 +244,61 @@ def tw_hybrid_down(wd, M, P, hy_h, hy_idx, hy_cnt, route, bk_rows, bk_count, R_m
     _check(st, "tw_hybrid_down")
 
 
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def tw_hybrid_bwd_dh(dy, wd, P, l1, hy_g, hy_u, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max,
+                     bk_g, bk_u, hy_du, hy_dz, bk_du, bk_dz, stream=None, events=None) -> None:
+    M, K = dy.shape
+    N = wd.shape[0]
+    _dtype(dy, torch.bfloat16, "dy")
+    _dtype(wd, torch.bfloat16, "wd")
+    ev = _events(events)
+    st = _lib.tw_hybrid_bwd_dh(_ptr(dy), _ptr(wd), M, K, N, P, float(l1), _ptr(hy_g), _ptr(hy_u),
+                               _ptr(hy_idx), _ptr(hy_cnt), _ptr(route), _ptr(bk_rows),
+                               _ptr(bk_count), R_max, _ptr(bk_g), _ptr(bk_u), _ptr(hy_du),
+                               _ptr(hy_dz), _ptr(bk_du), _ptr(bk_dz), _stream(stream),
+                               ev[0] if ev else None)
+    _check(st, "tw_hybrid_bwd_dh")
+
+
+def tw_hybrid_bwd_dx_workspace_bytes(R_max) -> int:
+    return int(_lib.tw_hybrid_bwd_dx_workspace_bytes(R_max))
+
+
+def tw_hybrid_bwd_dx(wg_t, wu_t, M, P, hy_du, hy_dz, hy_idx, hy_cnt, route, bk_rows, bk_count,
+                     R_max, bk_du, bk_dz, dx, ws, stream=None, events=None) -> None:
+    N, K = wg_t.shape
+    _dtype(dx, torch.float32, "dx")
+    ev = _events(events)
+    st = _lib.tw_hybrid_bwd_dx(_ptr(wg_t), _ptr(wu_t), M, K, N, P, _ptr(hy_du), _ptr(hy_dz),
+                               _ptr(hy_idx), _ptr(hy_cnt), _ptr(route), _ptr(bk_rows),
+                               _ptr(bk_count), R_max, _ptr(bk_du), _ptr(bk_dz), _ptr(dx), _ptr(ws),
+                               _nbytes(ws), _stream(stream), ev[0] if ev else None)
+    _check(st, "tw_hybrid_bwd_dx")
+
+
+def tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max) -> int:
+    return int(_lib.tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max))
+
+
+def tw_hybrid_bwd_dw(x, dy, P, hy_h, hy_du, hy_dz, hy_idx, hy_cnt, route, bk_rows, bk_count,
+                     R_max, bk_g, bk_h, bk_du, bk_dz, dwg_t, dwu_t, dwd, ws, stream=None,
+                     events=None) -> None:
+    M, K = x.shape
+    N = dwd.shape[0]
+    _dtype(x, torch.bfloat16, "x")
+    _dtype(dy, torch.bfloat16, "dy")
+    ev = _events(events)
+    st = _lib.tw_hybrid_bwd_dw(_ptr(x), _ptr(dy), M, K, N, P, _ptr(hy_h), _ptr(hy_du),
+                               _ptr(hy_dz), _ptr(hy_idx), _ptr(hy_cnt), _ptr(route),
+                               _ptr(bk_rows), _ptr(bk_count), R_max, _ptr(bk_g), _ptr(bk_h),
+                               _ptr(bk_du), _ptr(bk_dz), _ptr(dwg_t), _ptr(dwu_t), _ptr(dwd),
+                               _ptr(ws), _nbytes(ws), _stream(stream), ev[0] if ev else None)
+    _check(st, "tw_hybrid_bwd_dw")
+
+
 # ------------------------------------------------------------- allocating --
 def alloc_pack(M, N, T, C, R_max, device="cuda"):
     """Output buffers of tw_pack_gate."""
@@ -350,6 +420,44 @@ def hybrid_forward(x, wg_t, wu_t, wd, packed, P=128, R_max=None, keep=True, hy=N
     tw_hybrid_down(wd, M, P, hy["hy_h"], hy["hy_idx"], hy["hy_cnt"], hy["route"], hy["bk_rows"],
                    hy["bk_count"], R_max, hy["bk_h"], y, ws)
     return y, hy
+
+
+def hybrid_backward(x, wg_t, wu_t, wd, dy, hy, l1=0.0):
+    """Backward over the hybrid storage ``hy`` of ``hybrid_forward`` (with
+    ``keep=True``): returns a dict with dx [M][K], dwg_t, dwu_t, dwd [N][K]
+    (fp32) and the activations' gradients (hy_du, hy_dz, bk_du, bk_dz)."""
+    M, K = x.shape
+    N = wg_t.shape[0]
+    P, R_max = hy["P"], hy["R_max"]
+    if hy["hy_u"] is None:
+        raise ValueError("the forward did not keep u and g (keep=False)")
+    dev = x.device
+    R1 = max(R_max, 1)
+    out = {
+        "hy_du": torch.empty((M, P), dtype=torch.float32, device=dev),
+        "hy_dz": torch.empty((M, P), dtype=torch.float32, device=dev),
+        "bk_du": torch.empty((R1, N), dtype=torch.bfloat16, device=dev),
+        "bk_dz": torch.empty((R1, N), dtype=torch.bfloat16, device=dev),
+        "dx": torch.empty((M, K), dtype=torch.float32, device=dev),
+        "dwg_t": torch.empty((N, K), dtype=torch.float32, device=dev),
+        "dwu_t": torch.empty((N, K), dtype=torch.float32, device=dev),
+        "dwd": torch.empty((N, K), dtype=torch.float32, device=dev),
+    }
+    tw_hybrid_bwd_dh(dy, wd, P, l1, hy["hy_g"], hy["hy_u"], hy["hy_idx"], hy["hy_cnt"],
+                     hy["route"], hy["bk_rows"], hy["bk_count"], R_max, hy["bk_g"], hy["bk_u"],
+                     out["hy_du"], out["hy_dz"], out["bk_du"], out["bk_dz"])
+    nx = tw_hybrid_bwd_dx_workspace_bytes(R_max)
+    wsx = torch.empty((nx,), dtype=torch.uint8, device=dev) if nx else None
+    tw_hybrid_bwd_dx(wg_t, wu_t, M, P, out["hy_du"], out["hy_dz"], hy["hy_idx"], hy["hy_cnt"],
+                     hy["route"], hy["bk_rows"], hy["bk_count"], R_max, out["bk_du"],
+                     out["bk_dz"], out["dx"], wsx)
+    wsw = torch.empty((tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max),), dtype=torch.uint8,
+                      device=dev)
+    tw_hybrid_bwd_dw(x, dy, P, hy["hy_h"], out["hy_du"], out["hy_dz"], hy["hy_idx"],
+                     hy["hy_cnt"], hy["route"], hy["bk_rows"], hy["bk_count"], R_max, hy["bk_g"],
+                     hy["bk_h"], out["bk_du"], out["bk_dz"], out["dwg_t"], out["dwu_t"],
+                     out["dwd"], wsw)
+    return out
 
 
 def library_path() -> str:

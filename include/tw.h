@@ -23,7 +23,8 @@
  * path is measured against.  tw_gate_dense + tw_pack_dense are the unfused
  * equivalent of tw_pack_gate (dense gate written to memory, then packed).
  * tw_hybrid_pack, tw_hybrid_up and tw_hybrid_down are the training forward
- * over the hybrid storage of sections 3-6 and 3-7 (declared at the end).
+ * over the hybrid storage of sections 3-6 and 3-7, and tw_hybrid_bwd_dh,
+ * tw_hybrid_bwd_dx and tw_hybrid_bwd_dw its backward (declared at the end).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -285,6 +286,70 @@ tw_status tw_hybrid_down(const uint16_t *wd, int M, int K, int N, int P,
                          const uint8_t *route, const int32_t *bk_rows, const int32_t *bk_count,
                          int R_max, const uint16_t *bk_h, float *y,
                          void *ws, size_t ws_bytes, void *stream, void *const *events);
+
+/*
+ * Backward over the hybrid storage (section 3-7: the gradients are formed
+ * from the stored sparse activations, without rebuilding a dense hidden
+ * state; L1 gradient injection; the hybrid transpose for the weight
+ * gradients), for the forward of tw_hybrid_pack / tw_hybrid_up /
+ * tw_hybrid_down with g, u (hy_u, bk_g, bk_u) kept.  With dy = dLoss/dy
+ * [M][K] (bf16) and the L1 penalty of section 3-2 on the gate activation,
+ * whose gradient on a positive activation is the caller's `l1` (lambda
+ * divided by the layer count and M N, in the pages' normalisation):
+ *   dh = dy W_d^T,   du = dh g,   dz = (dh u + l1) where g > 0, else 0,
+ *   dx = du W_u^T + dz W_g^T,
+ *   dwd[j] = sum_m h[m][j] dy[m],  dwu_t[j] = sum_m du[m][j] x[m],
+ *   dwg_t[j] = sum_m dz[m][j] x[m]
+ * (dwu_t, dwg_t: gradients of W_u and W_g in their transposed [N][K] layout,
+ * dwd of W_d [N][K]; all fp32).  Rows routed to the backup but past its room
+ * (bk_count > R_max) stored nothing: they get no dx and add nothing to the
+ * weight gradients.  Shapes as for the hybrid forward.
+ *
+ * tw_hybrid_bwd_dh (dense-to-hybrid): hy_du, hy_dz [M][P] fp32 at the stored
+ * entries of sparse rows; bk_du, bk_dz [R_max][N] bf16 for backup slots (on
+ * the matrix cores, from the row's stored bf16 bk_g, bk_u).  events: [0]
+ * before, [1] after the sparse-row kernel, [2] after the backup GEMM.
+ */
+tw_status tw_hybrid_bwd_dh(const uint16_t *dy, const uint16_t *wd, int M, int K, int N, int P,
+                           float l1, const float *hy_g, const float *hy_u, const int32_t *hy_idx,
+                           const int32_t *hy_cnt, const uint8_t *route, const int32_t *bk_rows,
+                           const int32_t *bk_count, int R_max, const uint16_t *bk_g,
+                           const uint16_t *bk_u, float *hy_du, float *hy_dz, uint16_t *bk_du,
+                           uint16_t *bk_dz, void *stream, void *const *events);
+
+/*
+ * tw_hybrid_bwd_dx (hybrid-to-dense): dx [M][K] fp32 for sparse rows and the
+ * listed backup rows (the latter on the matrix cores: dx = du W_u^T, then
+ * dx += dz W_g^T).  ws_bytes >= tw_hybrid_bwd_dx_workspace_bytes(R_max) (ws
+ * may be NULL when that is 0).  events: [0] before, [1] after the sparse-row
+ * kernel, [2] after the backup rows' kernels.
+ */
+size_t tw_hybrid_bwd_dx_workspace_bytes(int R_max);
+tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, int K, int N, int P,
+                           const float *hy_du, const float *hy_dz, const int32_t *hy_idx,
+                           const int32_t *hy_cnt, const uint8_t *route, const int32_t *bk_rows,
+                           const int32_t *bk_count, int R_max, const uint16_t *bk_du,
+                           const uint16_t *bk_dz, float *dx, void *ws, size_t ws_bytes,
+                           void *stream, void *const *events);
+
+/*
+ * tw_hybrid_bwd_dw: the three weight gradients, every row of dwg_t, dwu_t
+ * and dwd written.  The workspace holds the hybrid transpose: the stored
+ * entries (sparse rows' slots, and the listed backup rows' entries whose
+ * gate is positive) grouped by hidden column in ascending row order, so
+ * every gradient is a fixed-order sum (bit-identical run to run).
+ * ws_bytes >= tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max) (about
+ * 16 (M P + R_max N) bytes); M P + R_max N < 2^31.  events: [0] before,
+ * [1] after the transpose, [2] after the gradient kernel.
+ */
+size_t tw_hybrid_bwd_dw_workspace_bytes(int M, int N, int P, int R_max);
+tw_status tw_hybrid_bwd_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
+                           const float *hy_h, const float *hy_du, const float *hy_dz,
+                           const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
+                           const int32_t *bk_rows, const int32_t *bk_count, int R_max,
+                           const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
+                           const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
+                           void *ws, size_t ws_bytes, void *stream, void *const *events);
 
 #ifdef __cplusplus
 }

@@ -143,3 +143,32 @@ def test_hybrid_entry_points_reject(tw):
                                 None)
     assert D(y=None) == 1 and D(nb=nws - 1) == 1 and D(ws=None) == 1 and D(cap=2048) == 1
     assert tw._lib.tw_last_error()
+
+
+def test_hybrid_backward_entry_points_reject(tw):
+    L = tw._lib
+
+    def DH(K=256, cap=128, R=8, bk_g=P, du=P):
+        return L.tw_hybrid_bwd_dh(P, P, 64, K, 1024, cap, 0.01, P, P, P, P, P, P, P, R, bk_g, P,
+                                  du, P, P, P, None, None)
+    assert DH(K=100) == 2 and DH(cap=0) == 1 and DH(R=65) == 1
+    assert DH(bk_g=None) == 1 and DH(du=None) == 1 and DH(du=P + 4) == 1
+
+    nx = L.tw_hybrid_bwd_dx_workspace_bytes(8)
+    assert nx > 0 and L.tw_hybrid_bwd_dx_workspace_bytes(0) == 0
+
+    def DX(dx=P, nb=nx, ws=P, bk=P):
+        return L.tw_hybrid_bwd_dx(P, P, 64, 256, 1024, 128, P, P, P, P, P, P, P, 8, bk, P, dx, ws,
+                                  nb, None, None)
+    assert DX(dx=None) == 1 and DX(nb=nx - 1) == 1 and DX(ws=None) == 1 and DX(bk=None) == 1
+
+    nw = L.tw_hybrid_bwd_dw_workspace_bytes(64, 1024, 128, 8)
+    assert nw >= 16 * (64 * 128 + 8 * 1024)
+
+    def DW(M=64, N=1024, cap=128, R=8, nb=nw, dwd=P):
+        return L.tw_hybrid_bwd_dw(P, P, M, 256, N, cap, P, P, P, P, P, P, P, P, R, P, P, P, P, P,
+                                  P, dwd, P, nb, None, None)
+    assert DW(nb=nw - 1) == 1 and DW(dwd=None) == 1 and DW(cap=2048) == 1
+    # more stored entries than 32-bit entry ids can name
+    assert DW(M=1 << 20, N=1 << 15, cap=1 << 12, R=0, nb=1 << 62) == 2
+    assert tw._lib.tw_last_error()
