@@ -408,6 +408,169 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
     }
 }
 
+// ----------------------- weight gradients of backup rows -------------------
+// out[n][k] += sum over r < rows of T[r][n] G[r][k]: a GEMM whose reduction
+// runs over the (few) backup slots, so both operands are stored
+// reduction-major.  Both land in LDS in their natural row layout (as W_d
+// does in the down GEMM) and both fragments are read with the transposing
+// ds_read_b64_tr_b16.  T rows past `rows` are clamped to a valid row; G is
+// zero-padded to the 32-row stage by gather_rows_kernel, so the last partial
+// stage adds exactly zero.
+// Tiles of BM (n) x BN (k), both multiples of 128; each operand's stage is
+// BM/128 (resp. BN/128) regions of 32 reduction rows x 128 columns (256 B
+// rows, chunk c of row r at c ^ bsw(r)), filled by 1 KB direct loads of 4
+// rows each.  Three GEMMs (blockIdx.y) share one launch: they have the same
+// shape and the tiles of all three fill the chip together.
+template <int BM, int BN, int WM, int WN, int S>
+struct WGR {
+    static constexpr int NW = WM * WN, NTH = NW * 64;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FA = TM / 32, FB = TN / 32;
+    static constexpr int REG = kPK * 256;             // one 32 x 128 region
+    static constexpr int A_BYTES = BM / 128 * REG, B_BYTES = BN / 128 * REG;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = S * STAGE;
+    static constexpr int LPR = kPK / 4;               // 1 KB loads per region
+    static constexpr int NIA = BM / 128 * LPR / NW, NIB = BN / 128 * LPR / NW;
+    static constexpr int NI = NIA + NIB;
+    static_assert(BM % 128 == 0 && BN % 128 == 0, "128-column regions");
+    static_assert((BM / 128 * LPR) % NW == 0 && (BN / 128 * LPR) % NW == 0, "stage split");
+    static_assert(TM % 32 == 0 && TN % 32 == 0 && 128 % TN == 0 && 128 % TM == 0,
+                  "a wave tile inside one region");
+};
+
+// One fragment of a reduction-major region (rows = reduction, 128 columns):
+// lane (g4, i16) receives column col32 + 16 (g4 % 2) + i16 at reduction rows
+// 16 s + 8 (g4 / 2) .. +7.
+__device__ __forceinline__ u32x4 tr_frag(const char *region, int col32, int s, int lane) {
+    const int g4 = (lane >> 4) & 3, i16 = lane & 15;
+    const int c0 = col32 + 16 * (g4 & 1) + 4 * (i16 & 3);
+    i16x4 v[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int row = 16 * s + 8 * (g4 >> 1) + 4 * hh + (i16 >> 2);
+        const uint32_t off = row * 256 + (((c0 >> 3) ^ bsw(row)) << 4) + (c0 & 7) * 2;
+        v[hh] = lds_tr16((const lds_i16x4 *)(region + off));
+    }
+    const u32x2 lo = __builtin_bit_cast(u32x2, v[0]);
+    const u32x2 hi = __builtin_bit_cast(u32x2, v[1]);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// out_z[n][k] += sum over r < rows of T_z[r][n] G_z[r][k] for z = blockIdx.y
+// (T_z [rows][N], G_z [padded rows][K] bf16).  T rows past `rows` are
+// clamped to a valid row; G is zero-padded to the 32-row stage by
+// gather_rows_kernel, so the last partial stage adds exactly zero.
+template <int BM, int BN, int WM, int WN, int STG>
+__global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
+    const uint16_t *__restrict__ T0, const uint16_t *__restrict__ T1,
+    const uint16_t *__restrict__ T2, const uint16_t *__restrict__ G0,
+    const uint16_t *__restrict__ G1, const uint16_t *__restrict__ G2, int N, int K,
+    const int32_t *__restrict__ count, int R_cap, float *__restrict__ out0,
+    float *__restrict__ out1, float *__restrict__ out2) {
+    using P = WGR<BM, BN, WM, WN, STG>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int rows = rows_of(count, R_cap);
+    if (rows <= 0) return;
+    const int z = blockIdx.y;
+    const uint16_t *T = z == 0 ? T0 : (z == 1 ? T1 : T2);
+    const uint16_t *G = z == 0 ? G0 : (z == 1 ? G1 : G2);
+    float *out = z == 0 ? out0 : (z == 1 ? out1 : out2);
+    const int NS = (rows + kPK - 1) / kPK;
+    const int nrb = N / BM, ncb = K / BN, tiles = nrb * ncb;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WN, wn = wave % WN;
+    const int l32 = lane & 31;
+    const int rl = lane >> 4;  // row within a 1 KB load
+
+    for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
+        int nb, kb;
+        xcd_tile(t, nrb, ncb, nb, kb);
+        const int n0 = nb * BM, k0 = kb * BN;
+        const rsrc_t rt = make_rsrc(T + n0, ((uint64_t)rows * N - n0) * 2);
+        const rsrc_t rg = make_rsrc(G + k0, ((uint64_t)NS * kPK * K - k0) * 2);
+        auto issue = [&](int kt, char *st) {
+#pragma unroll
+            for (int j = 0; j < P::NIA; ++j) {
+                const int li = wave * P::NIA + j;             // load index in the stage
+                const int reg = li / P::LPR, row = (li % P::LPR) * 4;
+                const int r = min(kt * kPK + row + rl, rows - 1);
+                const uint32_t vo = (uint32_t)r * N * 2 + reg * 256 +
+                                    (uint32_t)(((lane & 15) ^ bsw(row + rl)) << 4);
+                dma16(rt, vo, 0, st + reg * P::REG + row * 256);
+            }
+#pragma unroll
+            for (int j = 0; j < P::NIB; ++j) {
+                const int li = wave * P::NIB + j;
+                const int reg = li / P::LPR, row = (li % P::LPR) * 4;
+                const uint32_t vo = (uint32_t)(kt * kPK + row + rl) * K * 2 + reg * 256 +
+                                    (uint32_t)(((lane & 15) ^ bsw(row + rl)) << 4);
+                dma16(rg, vo, 0, st + P::A_BYTES + reg * P::REG + row * 256);
+            }
+        };
+        f32x16 acc[P::FA][P::FB];
+#pragma unroll
+        for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) acc[a][b] = f32x16{};
+        u32x4 fa[2][P::FA], fb[2][P::FB];
+        // the wave's columns lie inside one region of each operand
+        const int ca = wm * P::TM, cb = wn * P::TN;
+        auto load = [&](const char *st, int s, int buf) {
+            const char *ra = st + (ca / 128) * P::REG;
+            const char *rb = st + P::A_BYTES + (cb / 128) * P::REG;
+#pragma unroll
+            for (int a = 0; a < P::FA; ++a) fa[buf][a] = tr_frag(ra, ca % 128 + a * 32, s, lane);
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) fb[buf][b] = tr_frag(rb, cb % 128 + b * 32, s, lane);
+        };
+        auto mma = [&](int buf) {
+#pragma unroll
+            for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
+        };
+        kloop_pipelined<STG, P::NI>(0, NS, smem, P::STAGE, issue, load, mma);
+#pragma unroll
+        for (int a = 0; a < P::FA; ++a)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int n = n0 + ca + a * 32 + mfma32_row(i, lane);
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b)
+                    out[(size_t)n * K + k0 + cb + b * 32 + l32] += acc[a][b][i];
+            }
+        __syncthreads();  // the next tile refills the ring
+    }
+}
+
+// dst[r] = src[rowlist[r]] (K bf16) for r < rows, zeros for rows <= r <
+// rows rounded up to the 32-row stage; one workgroup per slot.
+__global__ __launch_bounds__(256) void gather_rows_kernel(
+    const uint16_t *__restrict__ src0, const uint16_t *__restrict__ src1, int K,
+    const int32_t *__restrict__ rowlist, const int32_t *__restrict__ count, int R_cap,
+    uint16_t *__restrict__ dst0, uint16_t *__restrict__ dst1) {
+    const int rows = rows_of(count, R_cap);
+    const int r = blockIdx.x;
+    const int pad = (rows + kPK - 1) / kPK * kPK;
+    if (r >= pad) return;
+    const int KC = K >> 3;
+    const size_t d = (size_t)r * K;
+    if (r < rows) {
+        const size_t sidx = (size_t)rowlist[r] * K;
+        for (int q = threadIdx.x; q < KC; q += 256) {
+            st16(dst0 + d + 8 * q, ld16(src0 + sidx + 8 * q));
+            st16(dst1 + d + 8 * q, ld16(src1 + sidx + 8 * q));
+        }
+    } else {
+        for (int q = threadIdx.x; q < KC; q += 256) {
+            st16(dst0 + d + 8 * q, u32x4{0u, 0u, 0u, 0u});
+            st16(dst1 + d + 8 * q, u32x4{0u, 0u, 0u, 0u});
+        }
+    }
+}
+
 template <typename F>
 hipError_t set_lds(F *kernel, int bytes, bool &done) {
     if (done) return hipSuccess;
@@ -440,7 +603,47 @@ using DnRows = DnCfg<128, 128, 2, 4, 6>;
 using DnRowsAcc = DnCfg<128, 128, 2, 4, 6, true>;
 constexpr int kSplitGrid = 256;  // work items of the split down GEMM
 
+using WgCfg = WGR<256, 256, 2, 4, 4>;
+constexpr auto kWgrad = &wgrad_kernel<256, 256, 2, 4, 4>;
+constexpr auto kWgradSmall = &wgrad_kernel<128, 128, 2, 2, 4>;
+using WgSmall = WGR<128, 128, 2, 2, 4>;
+
 }  // namespace
+
+size_t backup_gather_bytes(int R_max, int K) {
+    return (size_t)(R_max + kPK - 1) / kPK * kPK * K * 2;
+}
+
+hipError_t launch_backup_wgrad(const uint16_t *dy, const uint16_t *x, int K, int N,
+                               const int32_t *rowlist, const int32_t *count, int R_cap,
+                               const uint16_t *bk_h, const uint16_t *bk_du,
+                               const uint16_t *bk_dz, uint16_t *dy_bk, uint16_t *x_bk,
+                               float *dwd, float *dwu_t, float *dwg_t, hipStream_t s) {
+    if (R_cap <= 0) return hipSuccess;
+    const int pad = (R_cap + kPK - 1) / kPK * kPK;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3(pad), dim3(256), 0, s, dy, x, K, rowlist, count,
+                       R_cap, dy_bk, x_bk);
+    // 256 x 256 tiles (twice the flops per loaded byte of 128 x 128) when
+    // they fill the chip, else 128 x 128
+    if ((N % 256) == 0 && (K % 256) == 0 && 3 * (N / 256) * (K / 256) >= 128) {
+        static bool attr = false;
+        hipError_t e = set_lds(kWgrad, WgCfg::LDS, attr);
+        if (e != hipSuccess) return e;
+        const int tiles = (N / 256) * (K / 256);
+        hipLaunchKernelGGL(kWgrad, dim3(tiles < 1024 ? tiles : 1024, 3), dim3(WgCfg::NTH),
+                           WgCfg::LDS, s, bk_h, bk_du, bk_dz, dy_bk, x_bk, x_bk, N, K, count,
+                           R_cap, dwd, dwu_t, dwg_t);
+    } else {
+        static bool attr = false;
+        hipError_t e = set_lds(kWgradSmall, WgSmall::LDS, attr);
+        if (e != hipSuccess) return e;
+        const int tiles = (N / 128) * (K / 128);
+        hipLaunchKernelGGL(kWgradSmall, dim3(tiles < 1024 ? tiles : 1024, 3), dim3(WgSmall::NTH),
+                           WgSmall::LDS, s, bk_h, bk_du, bk_dz, dy_bk, x_bk, x_bk, N, K, count,
+                           R_cap, dwd, dwu_t, dwg_t);
+    }
+    return hipGetLastError();
+}
 
 size_t split_partial_bytes() {
     return (size_t)kSplitGrid * DnRows::BM_ * DnRows::BN_ * sizeof(float);

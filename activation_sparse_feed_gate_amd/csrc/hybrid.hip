@@ -337,59 +337,35 @@ __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
 }
 
 // ------------------------------ hybrid transpose ----------------------------
-// Column lists of the stored activations, for the weight gradients: every
-// stored entry of a sparse row (id = m P + s) and every active entry of a
-// listed backup row (id = M P + r N + j, active where its bf16 gate is
-// positive), grouped by hidden column j and, within a column, in ascending
-// row order (so the gradient sums have a fixed order).  Counts (atomic, order
-// free), an exclusive scan to column offsets, a scatter through per-column
-// cursors (order within a column depends on timing), then a per-column rank
-// sort by row (rows are unique within a column).
+// Column lists of the sparse rows' stored entries (id = m P + s), for the
+// weight gradients: grouped by hidden column j and, within a column, in
+// ascending row order (so the gradient sums have a fixed order).  Counts
+// (atomic, order free), an exclusive scan to column offsets, a scatter
+// through per-column cursors (order within a column depends on timing), then
+// a per-column rank sort by row (a row appears at most once in a column).
+// The backup rows' contributions are dense products on the matrix cores.
 __global__ __launch_bounds__(kThreads) void fill_i32_kernel(int32_t *__restrict__ p, int n,
                                                              int32_t v) {
     for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) p[i] = v;
 }
 
-__device__ __forceinline__ bool bf16_positive(uint16_t b) { return b != 0 && b < 0x8000u; }
-
 // SCATTER false: count entries per column; true: place (row, id) through the
-// cursors.  Workgroups [0, ceil(M / 4)) take sparse rows (a wave each), the
-// next R_max take backup slots (a workgroup each; slots past the device-side
-// backup count exit).
+// cursors.  One wave per sparse row.
 template <bool SCATTER>
 __global__ __launch_bounds__(kThreads) void tr_place_kernel(
     int M, int N, int P, const int32_t *__restrict__ hy_idx, const int32_t *__restrict__ hy_cnt,
-    const uint8_t *__restrict__ route, const int32_t *__restrict__ bk_rows,
-    const int32_t *__restrict__ bk_count, int R_max, const uint16_t *__restrict__ bk_g,
-    int32_t *__restrict__ col, int32_t *__restrict__ ent_row, int32_t *__restrict__ ent_id) {
-    const int nrb = (M + kWaves - 1) / kWaves;
+    const uint8_t *__restrict__ route, int32_t *__restrict__ col, int32_t *__restrict__ ent_row,
+    int32_t *__restrict__ ent_id) {
     const int lane = threadIdx.x & 63;
-    if ((int)blockIdx.x < nrb) {
-        const int m = blockIdx.x * kWaves + (threadIdx.x >> 6);
-        if (m >= M || route[m]) return;
-        const int n = min(hy_cnt[m], P);
-        for (int s = lane; s < n; s += 64) {
-            const int j = min((unsigned)hy_idx[(size_t)m * P + s], (unsigned)(N - 1));
-            if constexpr (SCATTER) {
-                const int pos = atomicAdd(&col[j], 1);
-                ent_row[pos] = m;
-                ent_id[pos] = m * P + s;
-            } else {
-                atomicAdd(&col[j], 1);
-            }
-        }
-        return;
-    }
-    const int r = blockIdx.x - nrb;
-    if (r >= min(*bk_count, R_max)) return;
-    const int m = bk_rows[r];
-    const uint16_t *g = bk_g + (size_t)r * N;
-    for (int j = threadIdx.x; j < N; j += kThreads) {
-        if (!bf16_positive(g[j])) continue;
+    const int m = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
+    if (m >= M || route[m]) return;
+    const int n = min(hy_cnt[m], P);
+    for (int s = lane; s < n; s += 64) {
+        const int j = min((unsigned)hy_idx[(size_t)m * P + s], (unsigned)(N - 1));
         if constexpr (SCATTER) {
             const int pos = atomicAdd(&col[j], 1);
             ent_row[pos] = m;
-            ent_id[pos] = M * P + r * N + j;
+            ent_id[pos] = m * P + s;
         } else {
             atomicAdd(&col[j], 1);
         }
@@ -461,30 +437,25 @@ __global__ __launch_bounds__(kThreads) void tr_sort_kernel(
 // --------------------------- weight gradients --------------------------------
 // One wave per hidden column j (and K-slice of up to KS 16-byte chunks per
 // lane): over the column's entries in ascending row order,
-//   dwd[j] += h dy_m,   dwu_t[j] += du x_m,   dwg_t[j] += dz x_m
-// gathering the dy and x rows (bf16, coalesced 1 KB per wave and chunk);
-// values come from the sparse rows' fp32 storage or the backup rows' bf16
-// rows.  fp32 accumulation; every output row is written (zeros for columns
-// with no entry).
+//   dwd[j] = sum h dy_m,   dwu_t[j] = sum du x_m,   dwg_t[j] = sum dz x_m
+// gathering the dy and x rows (bf16, coalesced 1 KB per wave and chunk) with
+// the sparse rows' fp32 values.  fp32 accumulation; every output row is
+// written (zeros for columns with no entry).
 constexpr int kDwBatch = 2;
-
-__device__ __forceinline__ float bf16_val(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 template <int KS>
 __global__ __launch_bounds__(kThreads) void dw_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ dy, int M, int K, int N, int P,
     const int32_t *__restrict__ col_ptr, const int32_t *__restrict__ srt_row,
     const int32_t *__restrict__ srt_id, const float *__restrict__ hy_h,
-    const float *__restrict__ hy_du, const float *__restrict__ hy_dz,
-    const uint16_t *__restrict__ bk_h, const uint16_t *__restrict__ bk_du,
-    const uint16_t *__restrict__ bk_dz, float *__restrict__ dwg_t, float *__restrict__ dwu_t,
-    float *__restrict__ dwd) {
+    const float *__restrict__ hy_du, const float *__restrict__ hy_dz, float *__restrict__ dwg_t,
+    float *__restrict__ dwu_t, float *__restrict__ dwd) {
     const int j = __builtin_amdgcn_readfirstlane(blockIdx.x * kWaves + (threadIdx.x >> 6));
     if (j >= N) return;
     const int lane = threadIdx.x & 63;
     const int KC = K >> 3;
     const int q0 = blockIdx.y * KS * 64;  // first chunk of this K-slice
-    const size_t MP = (size_t)M * P;
+    const int MP = M * P;
     float ad[KS][8], au[KS][8], ag[KS][8];
 #pragma unroll
     for (int c = 0; c < KS; ++c)
@@ -497,17 +468,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(
         float hl = 0.0f, ul = 0.0f, zl = 0.0f;
         if (e0 + lane < n) {
             ml = min((unsigned)srt_row[p0 + e0 + lane], (unsigned)(M - 1));
-            const size_t id = (size_t)srt_id[p0 + e0 + lane];
-            if (id < MP) {
-                hl = hy_h[id];
-                ul = hy_du[id];
-                zl = hy_dz[id];
-            } else {
-                const size_t b = id - MP;
-                hl = bf16_val(bk_h[b]);
-                ul = bf16_val(bk_du[b]);
-                zl = bf16_val(bk_dz[b]);
-            }
+            const int id = min((unsigned)srt_id[p0 + e0 + lane], (unsigned)(MP - 1));
+            hl = hy_h[id];
+            ul = hy_du[id];
+            zl = hy_dz[id];
         }
         const int nb = min(64, n - e0);
         for (int b = 0; b < nb; b += kDwBatch) {
@@ -666,21 +630,25 @@ hipError_t launch_hybrid_dx(const uint16_t *wu_t, const uint16_t *wg_t, int M, i
 #undef TW_DX
 }
 
-size_t hybrid_transpose_bytes(int M, int N, int P, int R_max) {
-    const size_t cap = (size_t)M * P + (size_t)R_max * N;
-    auto up = [](size_t v) { return (v + 63) / 64 * 64; };
-    return up((size_t)N * 4) + up((size_t)(N + 1) * 4) + 4 * up(cap * 4);
+// workspace of launch_hybrid_dw: column counts / cursors, column offsets,
+// the scattered and the sorted (row, id) lists of the M P stored slots, then
+// the backup rows' gathered dy and x (32-row padded)
+size_t hybrid_dw_bytes(int M, int K, int N, int P, int R_max) {
+    const size_t cap = (size_t)M * P;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    return up((size_t)N * 4) + up((size_t)(N + 1) * 4) + 4 * up(cap * 4) +
+           2 * up(backup_gather_bytes(R_max, K));
 }
 
 hipError_t launch_hybrid_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
                             const float *hy_h, const float *hy_du, const float *hy_dz,
                             const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
                             const int32_t *bk_rows, const int32_t *bk_count, int R_max,
-                            const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
-                            const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
-                            void *ws, hipStream_t s, hipEvent_t ev_mid) {
-    const size_t cap = (size_t)M * P + (size_t)R_max * N;
-    auto up = [](size_t v) { return (v + 63) / 64 * 64; };
+                            const uint16_t *bk_h, const uint16_t *bk_du, const uint16_t *bk_dz,
+                            float *dwg_t, float *dwu_t, float *dwd, void *ws, hipStream_t s,
+                            hipEvent_t ev_transposed, hipEvent_t ev_sparse) {
+    const size_t cap = (size_t)M * P;
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     char *w = static_cast<char *>(ws);
     int32_t *col = reinterpret_cast<int32_t *>(w);
     w += up((size_t)N * 4);
@@ -693,50 +661,44 @@ hipError_t launch_hybrid_dw(const uint16_t *x, const uint16_t *dy, int M, int K,
     int32_t *srt_row = reinterpret_cast<int32_t *>(w);
     w += up(cap * 4);
     int32_t *srt_id = reinterpret_cast<int32_t *>(w);
+    w += up(cap * 4);
+    uint16_t *dy_bk = reinterpret_cast<uint16_t *>(w);
+    w += up(backup_gather_bytes(R_max, K));
+    uint16_t *x_bk = reinterpret_cast<uint16_t *>(w);
 
     const int fill_grid = (N + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(fill_i32_kernel, dim3(fill_grid < 1024 ? fill_grid : 1024), dim3(kThreads),
                        0, s, col, N, 0);
-    const int place_grid = (M + kWaves - 1) / kWaves + R_max;
-    if (place_grid > 0) {
+    const int place_grid = (M + kWaves - 1) / kWaves;
+    if (place_grid > 0)
         hipLaunchKernelGGL(tr_place_kernel<false>, dim3(place_grid), dim3(kThreads), 0, s, M, N,
-                           P, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max, bk_g, col, ent_row,
-                           ent_id);
-    }
+                           P, hy_idx, hy_cnt, route, col, ent_row, ent_id);
     hipLaunchKernelGGL(tr_scan_kernel, dim3(1), dim3(1024), 0, s, col, N, col_ptr);
-    if (place_grid > 0) {
+    if (place_grid > 0)
         hipLaunchKernelGGL(tr_place_kernel<true>, dim3(place_grid), dim3(kThreads), 0, s, M, N, P,
-                           hy_idx, hy_cnt, route, bk_rows, bk_count, R_max, bk_g, col, ent_row,
-                           ent_id);
-    }
+                           hy_idx, hy_cnt, route, col, ent_row, ent_id);
     const int cgrid = (N + kWaves - 1) / kWaves;
     hipLaunchKernelGGL(tr_sort_kernel, dim3(cgrid), dim3(kThreads), 0, s, N, col_ptr, ent_row,
                        ent_id, srt_row, srt_id);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (ev_mid) {
-        e = hipEventRecord(ev_mid, s);
-        if (e != hipSuccess) return e;
-    }
+    if (ev_transposed && (e = hipEventRecord(ev_transposed, s)) != hipSuccess) return e;
     const int KCH = (K + 511) / 512;
-    if (KCH <= 4) {
-#define TW_DW(ks)                                                                               \
-    hipLaunchKernelGGL(dw_kernel<ks>, dim3(cgrid, 1), dim3(kThreads), 0, s, x, dy, M, K, N, P,   \
-                       col_ptr, srt_row, srt_id, hy_h, hy_du, hy_dz, bk_h, bk_du, bk_dz, dwg_t, \
-                       dwu_t, dwd)
-        switch (KCH) {
-        case 1: TW_DW(1); break;
-        case 2: TW_DW(2); break;
-        case 3: TW_DW(3); break;
-        default: TW_DW(4); break;
-        }
-#undef TW_DW
-    } else {
-        hipLaunchKernelGGL(dw_kernel<4>, dim3(cgrid, (KCH + 3) / 4), dim3(kThreads), 0, s, x, dy,
-                           M, K, N, P, col_ptr, srt_row, srt_id, hy_h, hy_du, hy_dz, bk_h, bk_du,
-                           bk_dz, dwg_t, dwu_t, dwd);
+#define TW_DW(ks, slices)                                                                        \
+    hipLaunchKernelGGL(dw_kernel<ks>, dim3(cgrid, slices), dim3(kThreads), 0, s, x, dy, M, K, N, \
+                       P, col_ptr, srt_row, srt_id, hy_h, hy_du, hy_dz, dwg_t, dwu_t, dwd)
+    switch (KCH) {
+    case 1: TW_DW(1, 1); break;
+    case 2: TW_DW(2, 1); break;
+    case 3: TW_DW(3, 1); break;
+    default: TW_DW(4, (KCH + 3) / 4); break;
     }
-    return hipGetLastError();
+#undef TW_DW
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev_sparse && (e = hipEventRecord(ev_sparse, s)) != hipSuccess) return e;
+    // the backup rows: dW += T^T G on the matrix cores
+    return launch_backup_wgrad(dy, x, K, N, bk_rows, bk_count, R_max, bk_h, bk_du, bk_dz, dy_bk,
+                               x_bk, dwd, dwu_t, dwg_t, s);
 }
 
 }  // namespace tw

@@ -495,22 +495,22 @@ tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, in
     return TW_OK;
 }
 
-size_t tw_hybrid_bwd_dw_workspace_bytes(int M, int N, int P, int R_max) {
-    if (M < 0 || N <= 0 || P < 1 || R_max < 0) return 0;
-    return tw::hybrid_transpose_bytes(M, N, P, R_max) + 256;
+size_t tw_hybrid_bwd_dw_workspace_bytes(int M, int K, int N, int P, int R_max) {
+    if (M < 0 || K <= 0 || N <= 0 || P < 1 || R_max < 0) return 0;
+    return tw::hybrid_dw_bytes(M, K, N, P, R_max) + 256;
 }
 
 tw_status tw_hybrid_bwd_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
                            const float *hy_h, const float *hy_du, const float *hy_dz,
                            const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
                            const int32_t *bk_rows, const int32_t *bk_count, int R_max,
-                           const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
-                           const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
-                           void *ws, size_t ws_bytes, void *stream, void *const *events) {
+                           const uint16_t *bk_h, const uint16_t *bk_du, const uint16_t *bk_dz,
+                           float *dwg_t, float *dwu_t, float *dwd, void *ws, size_t ws_bytes,
+                           void *stream, void *const *events) {
     TW_TRY(check_hybrid(M, K, N, 128, 1, P, R_max));
-    if ((int64_t)M * P + (int64_t)R_max * N >= (int64_t(1) << 31))
-        return fail(TW_EUNSUPPORTED, "M*P + R_max*N = %lld stored entries: at most 2^31 - 1",
-                    (long long)M * P + (long long)R_max * N);
+    if ((int64_t)M * P >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "M*P = %lld stored slots: at most 2^31 - 1",
+                    (long long)M * P);
     TW_NEED_M(x);
     TW_NEED_M(dy);
     TW_NEED_M(hy_h);
@@ -526,22 +526,22 @@ tw_status tw_hybrid_bwd_dw(const uint16_t *x, const uint16_t *dy, int M, int K, 
     TW_NEED(dwd);
     TW_NEED(ws);
     if (R_max > 0) {
-        TW_NEED(bk_g);
         TW_NEED(bk_h);
         TW_NEED(bk_du);
         TW_NEED(bk_dz);
     }
-    const size_t need = tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max);
+    const size_t need = tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max);
     if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     TW_TRY(record(events, 0, s));
-    hipEvent_t mid = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+    hipEvent_t e1 = events ? static_cast<hipEvent_t>(events[1]) : nullptr;
+    hipEvent_t e2 = events ? static_cast<hipEvent_t>(events[2]) : nullptr;
     TW_TRY(launched(tw::launch_hybrid_dw(x, dy, M, K, N, P, hy_h, hy_du, hy_dz, hy_idx, hy_cnt,
-                                         route, bk_rows, bk_count, R_max, bk_g, bk_h, bk_du,
-                                         bk_dz, dwg_t, dwu_t, dwd, ws, s, mid),
+                                         route, bk_rows, bk_count, R_max, bk_h, bk_du, bk_dz,
+                                         dwg_t, dwu_t, dwd, ws, s, e1, e2),
                     "weight-gradient launch"));
-    TW_TRY(record(events, 2, s));
+    TW_TRY(record(events, 3, s));
     return TW_OK;
 }
 

@@ -96,13 +96,22 @@ hipError_t launch_hybrid_dx(const uint16_t *wu_t, const uint16_t *wg_t, int M, i
                             int P, const float *hy_du, const float *hy_dz,
                             const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
                             float *dx, hipStream_t s);
-size_t hybrid_transpose_bytes(int M, int N, int P, int R_max);
+size_t hybrid_dw_bytes(int M, int K, int N, int P, int R_max);
 hipError_t launch_hybrid_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
                             const float *hy_h, const float *hy_du, const float *hy_dz,
                             const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
                             const int32_t *bk_rows, const int32_t *bk_count, int R_max,
-                            const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
-                            const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
-                            void *ws, hipStream_t s, hipEvent_t ev_mid);
+                            const uint16_t *bk_h, const uint16_t *bk_du, const uint16_t *bk_dz,
+                            float *dwg_t, float *dwu_t, float *dwd, void *ws, hipStream_t s,
+                            hipEvent_t ev_transposed, hipEvent_t ev_sparse);
+// Weight gradients of the backup rows, added into dwd / dwu_t / dwg_t:
+// dwd += bk_h^T dy_bk, dwu_t += bk_du^T x_bk, dwg_t += bk_dz^T x_bk, with the
+// rows' dy and x first gathered into dy_bk / x_bk (backup_gather_bytes each).
+size_t backup_gather_bytes(int R_max, int K);
+hipError_t launch_backup_wgrad(const uint16_t *dy, const uint16_t *x, int K, int N,
+                               const int32_t *rowlist, const int32_t *count, int R_cap,
+                               const uint16_t *bk_h, const uint16_t *bk_du,
+                               const uint16_t *bk_dz, uint16_t *dy_bk, uint16_t *x_bk,
+                               float *dwd, float *dwu_t, float *dwg_t, hipStream_t s);
 
 }  // namespace tw

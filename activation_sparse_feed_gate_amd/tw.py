@@ -77,10 +77,10 @@ _lib.tw_hybrid_bwd_dx.restype = _i
 _lib.tw_hybrid_bwd_dx.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                   _i, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
 _lib.tw_hybrid_bwd_dw_workspace_bytes.restype = _sz
-_lib.tw_hybrid_bwd_dw_workspace_bytes.argtypes = [_i] * 4
+_lib.tw_hybrid_bwd_dw_workspace_bytes.argtypes = [_i] * 5
 _lib.tw_hybrid_bwd_dw.restype = _i
 _lib.tw_hybrid_bwd_dw.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                  _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
+                                  _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _vp]
 
 TW_OK, TW_EINVAL, TW_EUNSUPPORTED, TW_EHIP = 0, 1, 2, 3
 
@@ -279,12 +279,12 @@ def tw_hybrid_bwd_dx(wg_t, wu_t, M, P, hy_du, hy_dz, hy_idx, hy_cnt, route, bk_r
     _check(st, "tw_hybrid_bwd_dx")
 
 
-def tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max) -> int:
-    return int(_lib.tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max))
+def tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max) -> int:
+    return int(_lib.tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max))
 
 
 def tw_hybrid_bwd_dw(x, dy, P, hy_h, hy_du, hy_dz, hy_idx, hy_cnt, route, bk_rows, bk_count,
-                     R_max, bk_g, bk_h, bk_du, bk_dz, dwg_t, dwu_t, dwd, ws, stream=None,
+                     R_max, bk_h, bk_du, bk_dz, dwg_t, dwu_t, dwd, ws, stream=None,
                      events=None) -> None:
     M, K = x.shape
     N = dwd.shape[0]
@@ -293,7 +293,7 @@ def tw_hybrid_bwd_dw(x, dy, P, hy_h, hy_du, hy_dz, hy_idx, hy_cnt, route, bk_row
     ev = _events(events)
     st = _lib.tw_hybrid_bwd_dw(_ptr(x), _ptr(dy), M, K, N, P, _ptr(hy_h), _ptr(hy_du),
                                _ptr(hy_dz), _ptr(hy_idx), _ptr(hy_cnt), _ptr(route),
-                               _ptr(bk_rows), _ptr(bk_count), R_max, _ptr(bk_g), _ptr(bk_h),
+                               _ptr(bk_rows), _ptr(bk_count), R_max, _ptr(bk_h),
                                _ptr(bk_du), _ptr(bk_dz), _ptr(dwg_t), _ptr(dwu_t), _ptr(dwd),
                                _ptr(ws), _nbytes(ws), _stream(stream), ev[0] if ev else None)
     _check(st, "tw_hybrid_bwd_dw")
@@ -451,10 +451,10 @@ def hybrid_backward(x, wg_t, wu_t, wd, dy, hy, l1=0.0):
     tw_hybrid_bwd_dx(wg_t, wu_t, M, P, out["hy_du"], out["hy_dz"], hy["hy_idx"], hy["hy_cnt"],
                      hy["route"], hy["bk_rows"], hy["bk_count"], R_max, out["bk_du"],
                      out["bk_dz"], out["dx"], wsx)
-    wsw = torch.empty((tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max),), dtype=torch.uint8,
+    wsw = torch.empty((tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max),), dtype=torch.uint8,
                       device=dev)
     tw_hybrid_bwd_dw(x, dy, P, hy["hy_h"], out["hy_du"], out["hy_dz"], hy["hy_idx"],
-                     hy["hy_cnt"], hy["route"], hy["bk_rows"], hy["bk_count"], R_max, hy["bk_g"],
+                     hy["hy_cnt"], hy["route"], hy["bk_rows"], hy["bk_count"], R_max,
                      hy["bk_h"], out["bk_du"], out["bk_dz"], out["dwg_t"], out["dwu_t"],
                      out["dwd"], wsw)
     return out

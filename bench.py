@@ -234,6 +234,7 @@ def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, st
             roof[k] = {"bound": "mfma", "achieved": a, "peak": PEAK_BF16_TFLOPS,
                        "unit": "TFLOP/s", "frac": a / PEAK_BF16_TFLOPS, "avg_us": kern[k] * 1e6}
     storage = M * P * (4 * 4) + M * (4 + 1) + Rh * N * 2 * 3 + Rh * 4
+    bwd = hybrid_backward_bench(args, tw, torch, w, x, wg, wu, wdn, hy, Rh, P, hev)
     return {
         "ms_per_step": t_h * 1e3, "value": M / t_h, "unit": "tokens/s",
         "speedup_vs_dense": t_dense / t_h, "eager_ms_per_step": t_eager * 1e3,
@@ -243,10 +244,120 @@ def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, st
         "stages": roof,
         "storage_bytes": storage,
         "dense_activation_bytes": 3 * M * N * 2,
+        "backward": bwd,
         "note": "tw_pack_gate + tw_hybrid_pack + tw_hybrid_up (g and u kept) + tw_hybrid_down; "
                 "speedup against tw_ffn_fwd; storage = hybrid g, u, h (sparse rows fp32 with "
                 "indices, backup rows bf16) against dense bf16 g, u, h",
     }
+
+
+def hybrid_backward_bench(args, tw, torch, w, x, wg, wu, wdn, hy, Rh, P, hev):
+    """Backward over the stored hybrid activations (dh with L1 injection,
+    dx, transpose + weight gradients) for a seeded dy, against the same
+    backward on torch.matmul (hipBLASLt) from dense bf16 g and u."""
+    import numpy as np
+
+    M, K, N = w.M, w.K, w.N
+    l1 = 2e-5  # the L1 gradient on a positive activation (any value: same work)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    dy = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+    R1 = max(Rh, 1)
+    o = {"hy_du": torch.empty((M, P), dtype=torch.float32, device="cuda"),
+         "hy_dz": torch.empty((M, P), dtype=torch.float32, device="cuda"),
+         "bk_du": torch.empty((R1, N), dtype=torch.bfloat16, device="cuda"),
+         "bk_dz": torch.empty((R1, N), dtype=torch.bfloat16, device="cuda"),
+         "dx": torch.empty((M, K), dtype=torch.float32, device="cuda"),
+         "dwg": torch.empty((N, K), dtype=torch.float32, device="cuda"),
+         "dwu": torch.empty((N, K), dtype=torch.float32, device="cuda"),
+         "dwd": torch.empty((N, K), dtype=torch.float32, device="cuda")}
+    wsx = torch.empty((max(tw.tw_hybrid_bwd_dx_workspace_bytes(Rh), 1),), dtype=torch.uint8,
+                      device="cuda")
+    wsw = torch.empty((tw.tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, Rh),), dtype=torch.uint8,
+                      device="cuda")
+
+    def bstep(ev=None, st=torch.cuda.current_stream()):
+        e = ev or (None, None, None)
+        tw.tw_hybrid_bwd_dh(dy, wdn, P, l1, hy["hy_g"], hy["hy_u"], hy["hy_idx"], hy["hy_cnt"],
+                            hy["route"], hy["bk_rows"], hy["bk_count"], Rh, hy["bk_g"],
+                            hy["bk_u"], o["hy_du"], o["hy_dz"], o["bk_du"], o["bk_dz"], stream=st,
+                            events=e[0])
+        tw.tw_hybrid_bwd_dx(wg, wu, M, P, o["hy_du"], o["hy_dz"], hy["hy_idx"], hy["hy_cnt"],
+                            hy["route"], hy["bk_rows"], hy["bk_count"], Rh, o["bk_du"],
+                            o["bk_dz"], o["dx"], wsx, stream=st, events=e[1])
+        tw.tw_hybrid_bwd_dw(x, dy, P, hy["hy_h"], o["hy_du"], o["hy_dz"], hy["hy_idx"],
+                            hy["hy_cnt"], hy["route"], hy["bk_rows"], hy["bk_count"], Rh,
+                            hy["bk_h"], o["bk_du"], o["bk_dz"], o["dwg"], o["dwu"],
+                            o["dwd"], wsw, stream=st, events=e[2])
+
+    # dense reference backward on hipBLASLt from dense bf16 g, u (as a dense
+    # training step would keep them)
+    gd = torch.relu(x @ wg.t()).to(torch.bfloat16)
+    ud = (x @ wu.t()).to(torch.bfloat16)
+    hd = gd * ud
+    wgu_k = torch.cat([wu, wg], dim=0)  # [2N, K]: dx = [du dz] @ [W_u^T; W_g^T]
+
+    def dense_bwd():
+        dh = dy @ wdn.t()
+        du = dh * gd
+        dz = torch.where(gd > 0, dh * ud + l1, torch.zeros_like(dh))
+        dx = torch.cat([du, dz], dim=1) @ wgu_k
+        dwd = hd.t() @ dy
+        dwu = du.t() @ x
+        dwg = dz.t() @ x
+        return dx, dwd, dwu, dwg
+
+    for _ in range(max(args.warmup, 1)):
+        bstep()
+        dense_bwd()
+    torch.cuda.synchronize()
+    Ks = args.steps
+    evl = [(hev.create(3), hev.create(3), hev.create(4)) for _ in range(Ks)]
+    t0 = time.perf_counter()
+    for i in range(Ks):
+        bstep(evl[i])
+    torch.cuda.synchronize()
+    t_eager = (time.perf_counter() - t0) / Ks
+    t_b = t_eager
+    if not args.no_graph:
+        G = max(1, min(args.graph_steps, Ks))
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for _ in range(G):
+                    bstep(st=None)
+        torch.cuda.current_stream().wait_stream(cap)
+        g.replay()
+        n_rep = max(1, Ks // G)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_rep):
+            g.replay()
+        torch.cuda.synchronize()
+        t_b = (time.perf_counter() - t0) / (n_rep * G)
+        del g
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(Ks):
+        dense_bwd()
+    torch.cuda.synchronize()
+    t_dense = (time.perf_counter() - t0) / Ks
+
+    def avg(j, i):
+        return sum(hev.ms(e[j][i], e[j][i + 1]) for e in evl) / len(evl) * 1e-3
+
+    kern = {"hybrid_dh": avg(0, 0), "backup_dh": avg(0, 1), "hybrid_dx": avg(1, 0),
+            "backup_dx": avg(1, 1), "transpose": avg(2, 0), "weight_grads": avg(2, 1),
+            "backup_weight_grads": avg(2, 2)}
+    for e in evl:
+        for q in e:
+            hev.destroy(q)
+    return {"ms_per_step": t_b * 1e3, "eager_ms_per_step": t_eager * 1e3,
+            "hipblaslt_dense_ms": t_dense * 1e3, "speedup_vs_hipblaslt_dense": t_dense / t_b,
+            "kernels_us": {k: v * 1e6 for k, v in kern.items()},
+            "note": "tw_hybrid_bwd_dh + tw_hybrid_bwd_dx + tw_hybrid_bwd_dw; the reference is "
+                    "the same backward on torch.matmul from dense bf16 g and u"}
 
 
 def main():

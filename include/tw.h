@@ -334,22 +334,25 @@ tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, in
 
 /*
  * tw_hybrid_bwd_dw: the three weight gradients, every row of dwg_t, dwu_t
- * and dwd written.  The workspace holds the hybrid transpose: the stored
- * entries (sparse rows' slots, and the listed backup rows' entries whose
- * gate is positive) grouped by hidden column in ascending row order, so
- * every gradient is a fixed-order sum (bit-identical run to run).
- * ws_bytes >= tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max) (about
- * 16 (M P + R_max N) bytes); M P + R_max N < 2^31.  events: [0] before,
- * [1] after the transpose, [2] after the gradient kernel.
+ * and dwd written.  The sparse rows' part goes through the hybrid transpose
+ * kept in the workspace: their stored entries grouped by hidden column in
+ * ascending row order, so each column's gradient is a fixed-order sum; the
+ * listed backup rows' part is three products on the matrix cores
+ * (dwd += bk_h^T dy, dwu_t += bk_du^T x, dwg_t += bk_dz^T x over the backup
+ * slots).  Results are bit-identical run to run.  ws_bytes >=
+ * tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max) (about 16 M P +
+ * 4 R_max K bytes); M P < 2^31.  events: [0] before, [1] after the
+ * transpose, [2] after the sparse rows' gradients, [3] after the backup
+ * rows' products.
  */
-size_t tw_hybrid_bwd_dw_workspace_bytes(int M, int N, int P, int R_max);
+size_t tw_hybrid_bwd_dw_workspace_bytes(int M, int K, int N, int P, int R_max);
 tw_status tw_hybrid_bwd_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
                            const float *hy_h, const float *hy_du, const float *hy_dz,
                            const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
                            const int32_t *bk_rows, const int32_t *bk_count, int R_max,
-                           const uint16_t *bk_g, const uint16_t *bk_h, const uint16_t *bk_du,
-                           const uint16_t *bk_dz, float *dwg_t, float *dwu_t, float *dwd,
-                           void *ws, size_t ws_bytes, void *stream, void *const *events);
+                           const uint16_t *bk_h, const uint16_t *bk_du, const uint16_t *bk_dz,
+                           float *dwg_t, float *dwu_t, float *dwd, void *ws, size_t ws_bytes,
+                           void *stream, void *const *events);
 
 #ifdef __cplusplus
 }

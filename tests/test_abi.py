@@ -162,12 +162,12 @@ def test_hybrid_backward_entry_points_reject(tw):
                                   nb, None, None)
     assert DX(dx=None) == 1 and DX(nb=nx - 1) == 1 and DX(ws=None) == 1 and DX(bk=None) == 1
 
-    nw = L.tw_hybrid_bwd_dw_workspace_bytes(64, 1024, 128, 8)
-    assert nw >= 16 * (64 * 128 + 8 * 1024)
+    nw = L.tw_hybrid_bwd_dw_workspace_bytes(64, 256, 1024, 128, 8)
+    assert nw >= 16 * 64 * 128 + 4 * 32 * 256
 
     def DW(M=64, N=1024, cap=128, R=8, nb=nw, dwd=P):
         return L.tw_hybrid_bwd_dw(P, P, M, 256, N, cap, P, P, P, P, P, P, P, P, R, P, P, P, P, P,
-                                  P, dwd, P, nb, None, None)
+                                  dwd, P, nb, None, None)
     assert DW(nb=nw - 1) == 1 and DW(dwd=None) == 1 and DW(cap=2048) == 1
     # more stored entries than 32-bit entry ids can name
     assert DW(M=1 << 20, N=1 << 15, cap=1 << 12, R=0, nb=1 << 62) == 2

@@ -80,11 +80,11 @@ def _run(tw, dev, w, P, R_max, l1, dy_dev, twice=False):
         tw.tw_hybrid_bwd_dx(dev["wg_t"], dev["wu_t"], M, P, o["hy_du"], o["hy_dz"], hy["hy_idx"],
                             hy["hy_cnt"], hy["route"], hy["bk_rows"], hy["bk_count"], R_max,
                             o["bk_du"], o["bk_dz"], o["dx"], wsx)
-        wsw = torch.empty((tw.tw_hybrid_bwd_dw_workspace_bytes(M, N, P, R_max),),
+        wsw = torch.empty((tw.tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max),),
                           dtype=torch.uint8, device="cuda")
         tw.tw_hybrid_bwd_dw(dev["x"], dy_dev, P, hy["hy_h"], o["hy_du"], o["hy_dz"],
                             hy["hy_idx"], hy["hy_cnt"], hy["route"], hy["bk_rows"],
-                            hy["bk_count"], R_max, hy["bk_g"], hy["bk_h"], o["bk_du"], o["bk_dz"],
+                            hy["bk_count"], R_max, hy["bk_h"], o["bk_du"], o["bk_dz"],
                             o["dwg_t"], o["dwu_t"], o["dwd"], wsw)
         outs.append(o)
     torch.cuda.synchronize()
