@@ -165,6 +165,40 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
                 }
         };
         kloop_pipelined<S, P::NI>(0, KT, smem, P::STAGE, issue, load, mma);
+        if constexpr (MODE == kDh) {
+            // per 32-row block: every stored g, u is loaded before the first
+            // store (one memory round trip per block, not one per row)
+#pragma unroll
+            for (int a = 0; a < P::FA; ++a) {
+                uint16_t gi[16][P::FB], ui[16][P::FB];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = min(m0 + wm * P::TM + a * 32 + mfma32_row(i, lane), rows - 1);
+#pragma unroll
+                    for (int b = 0; b < P::FB; ++b) {
+                        const size_t o = (size_t)r * N + n0 + wn * P::TN + b * 32 + l32;
+                        gi[i][b] = g_in[o];
+                        ui[i][b] = u_in[o];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = m0 + wm * P::TM + a * 32 + mfma32_row(i, lane);
+                    if (r >= rows) continue;
+#pragma unroll
+                    for (int b = 0; b < P::FB; ++b) {
+                        const size_t o = (size_t)r * N + n0 + wn * P::TN + b * 32 + l32;
+                        const float dh = ag[a][b][i];
+                        const float gv = __uint_as_float((uint32_t)gi[i][b] << 16);
+                        const float uv = __uint_as_float((uint32_t)ui[i][b] << 16);
+                        h[o] = (uint16_t)f32_to_bf16(dh * gv);
+                        g_out[o] = (uint16_t)f32_to_bf16(gv > 0.0f ? dh * uv + l1 : 0.0f);
+                    }
+                }
+            }
+            __syncthreads();  // the next tile refills the ring
+            continue;
+        }
 #pragma unroll
         for (int a = 0; a < P::FA; ++a)
 #pragma unroll
@@ -174,13 +208,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
 #pragma unroll
                     for (int b = 0; b < P::FB; ++b) {
                         const size_t o = (size_t)r * N + n0 + wn * P::TN + b * 32 + l32;
-                        if constexpr (MODE == kDh) {
-                            const float dh = ag[a][b][i];
-                            const float gv = __uint_as_float((uint32_t)g_in[o] << 16);
-                            const float uv = __uint_as_float((uint32_t)u_in[o] << 16);
-                            h[o] = (uint16_t)f32_to_bf16(dh * gv);
-                            g_out[o] = (uint16_t)f32_to_bf16(gv > 0.0f ? dh * uv + l1 : 0.0f);
-                        } else {
+                        {
                             const float g = ag[a][b][i] > 0.0f ? ag[a][b][i] : 0.0f;
                             const float u = au[a][b][i];
                             h[o] = (uint16_t)f32_to_bf16(g * u);
@@ -330,21 +358,39 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
         kloop_pipelined<STG, P::NI>(kt0, kt1, smem, P::STAGE, issue, load, mma);
 
         if (S == 1) {
+            // per 32-row block: the row indices (and with ACC the old values)
+            // are all loaded before the first store
 #pragma unroll
-            for (int a = 0; a < P::FA; ++a)
+            for (int a = 0; a < P::FA; ++a) {
+                // rows past `rows` read a valid row (clamped) and store nothing
+                int yr[16];
+                bool ok[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int r = m0 + wm * P::TM + a * 32 + mfma32_row(i, lane);
-                    if (r < rows) {
-                        const int yr = rowlist ? rowlist[r] : r;
+                    ok[i] = r < rows;
+                    const int rr = min(r, rows - 1);
+                    yr[i] = rowlist ? rowlist[rr] : rr;
+                }
+                float old[ACC ? 16 : 1][P::FB];
+                if constexpr (ACC) {
 #pragma unroll
-                        for (int b = 0; b < P::FB; ++b) {
-                            float *yp = y + (size_t)yr * K + k0 + wn * P::TN + b * 32 + l32;
-                            if constexpr (ACC) *yp += acc[a][b][i];
-                            else *yp = acc[a][b][i];
-                        }
+                    for (int i = 0; i < 16; ++i)
+#pragma unroll
+                        for (int b = 0; b < P::FB; ++b)
+                            old[i][b] = y[(size_t)yr[i] * K + k0 + wn * P::TN + b * 32 + l32];
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (!ok[i]) continue;
+#pragma unroll
+                    for (int b = 0; b < P::FB; ++b) {
+                        float *yp = y + (size_t)yr[i] * K + k0 + wn * P::TN + b * 32 + l32;
+                        if constexpr (ACC) *yp = old[i][b] + acc[a][b][i];
+                        else *yp = acc[a][b][i];
                     }
                 }
+            }
         } else {
             // partial tile of split sp, summed by split_reduce_kernel
             float *pt = partial + ((size_t)sp * tiles + tile) * (BM * BN);
@@ -532,15 +578,26 @@ __global__ __launch_bounds__(WM * WN * 64) void wgrad_kernel(
                 for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
         };
         kloop_pipelined<STG, P::NI>(0, NS, smem, P::STAGE, issue, load, mma);
+        // add into out: per 32-row block, every old value is loaded before
+        // the first store (a store may alias a later load of the same array,
+        // so interleaving them would serialise one round trip per element)
 #pragma unroll
-        for (int a = 0; a < P::FA; ++a)
+        for (int a = 0; a < P::FA; ++a) {
+            float old[16][P::FB];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int n = n0 + ca + a * 32 + mfma32_row(i, lane);
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b) old[i][b] = out[(size_t)n * K + k0 + cb + b * 32 + l32];
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int n = n0 + ca + a * 32 + mfma32_row(i, lane);
 #pragma unroll
                 for (int b = 0; b < P::FB; ++b)
-                    out[(size_t)n * K + k0 + cb + b * 32 + l32] += acc[a][b][i];
+                    out[(size_t)n * K + k0 + cb + b * 32 + l32] = old[i][b] + acc[a][b][i];
             }
+        }
         __syncthreads();  // the next tile refills the ring
     }
 }
