@@ -20,6 +20,10 @@
 //   per wave): larger batches hold more registers and leave fewer waves
 //   resident, which measured slower at every shape (at K = 1024, 78 VGPRs
 //   and six waves per SIMD against 112 and four).
+// - Batches of at most 256 rows cannot fill the chip with 4 waves per row,
+//   and the heaviest row's serial chain of gathers sets the kernel time, so
+//   such rows are spread over 16 waves (8 when K > 2048) that take one
+//   entry at a time.
 // - The dot product is reduced across the wave with DPP (no LDS), its
 //   product with g is the scalar h_j, and h_j * W_d[j] is added lane-wise.
 // - The four partial y rows are summed in LDS in a fixed order (the result
@@ -31,17 +35,21 @@
 namespace tw {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kBatch = 2;  // active neurons gathered together per wave
+constexpr int kSmallBatchRows = 256;  // at most this many rows: 16 waves per row
 
-template <int KCH>
-__global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
+// NWV waves per token row: 4 for large batches; small batches have too few
+// rows to fill the chip, and a heavy row's entries then form the critical
+// path, so they spread each row over 8 or 16 waves (one entry at a time per
+// wave: registers for occupancy rather than loads in flight).
+template <int KCH, int NWV>
+__global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wu_t,
     const uint16_t *__restrict__ wd, int K, int N, int NT, int C,
     const float *__restrict__ tw_val,
     const int32_t *__restrict__ tw_idx, const int32_t *__restrict__ tw_cnt,
     float *__restrict__ y) {
+    constexpr int kThreads = NWV * 64, kWaves = NWV;
+    constexpr int kBatch = NWV >= 8 ? 1 : 2;  // active neurons gathered together per wave
     extern __shared__ __attribute__((aligned(16))) char smem[];  // y staging, fp32
     __shared__ int s_off[kThreads + 1];
     __shared__ int s_wtot[kWaves];
@@ -193,22 +201,37 @@ __global__ __launch_bounds__(kThreads) void sparse_updown_kernel(
     }
 }
 
-template <int KCH>
-hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
-                    int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
-                    const int32_t *tw_cnt, float *y, hipStream_t s) {
-    const size_t lds = (size_t)kWaves * KCH * 512 * sizeof(float);  // y staging
+template <int KCH, int NWV>
+hipError_t launch_kw(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
+                     int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
+                     const int32_t *tw_cnt, float *y, hipStream_t s) {
+    const size_t lds = (size_t)NWV * KCH * 512 * sizeof(float);  // y staging
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_updown_kernel<KCH>),
+            hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_updown_kernel<KCH, NWV>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(sparse_updown_kernel<KCH>, dim3(M), dim3(kThreads), lds, s, x, wu_t, wd, K,
-                       N, NT, C, tw_val, tw_idx, tw_cnt, y);
+    hipLaunchKernelGGL((sparse_updown_kernel<KCH, NWV>), dim3(M), dim3(NWV * 64), lds, s, x,
+                       wu_t, wd, K, N, NT, C, tw_val, tw_idx, tw_cnt, y);
     return hipGetLastError();
+}
+
+// waves per row by batch size (measured: 16 pays off only while the rows
+// alone cannot fill the chip)
+template <int KCH>
+hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
+                    int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
+                    const int32_t *tw_cnt, float *y, hipStream_t s) {
+    // 16 waves cap a lane at 128 registers and the y staging at 16 KCH KB:
+    // wide rows take 8
+    constexpr int kSmallWaves = KCH <= 4 ? 16 : 8;
+    if (M <= kSmallBatchRows)
+        return launch_kw<KCH, kSmallWaves>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt,
+                                           y, s);
+    return launch_kw<KCH, 4>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
 }
 
 }  // namespace
