@@ -225,6 +225,167 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
     if (tid < 8 && m0 + 32 * tid < M) oflag[(size_t)bn * MW + (m0 >> 5) + tid] = s_flag[tid];
 }
 
+// ------------------------- small batches (decode) ---------------------------
+// With few token rows the 256-row macro tile is mostly padding, so its
+// matrix work, not the weights, sets the time (and only N / 256 workgroups
+// run).  This variant takes 64 rows x one TwELL tile (T columns) per
+// workgroup of 4 waves: every wave holds the 64 rows x T / 4 columns, the
+// operands stream through the same 4-stage direct-to-LDS ring, and the
+// epilogue stages the 64 x T tile in LDS and packs one row at a time per
+// wave (lane l holds T / 64 consecutive columns; a wave-wide scan of the
+// lanes' counts gives the slots in ascending column order).  The row
+// overflow bits go to oflag[tile][row word]: N / T column blocks.
+constexpr int kSmallBM = 64;
+constexpr int kSmallThreads = 256;
+
+template <int T>
+struct SmallGate {
+    static constexpr int NW = 4, WC = T / NW;          // columns per wave
+    static constexpr int FB = WC / 32;                  // 32-column blocks per wave
+    static constexpr int SR = kSmallBM + T;             // stage rows: x, then W_g
+    static constexpr int NI = SR / (16 * NW);           // direct loads per wave and stage
+    static constexpr int STAGE = SR * kPRow;
+    static constexpr int RING = kStages * STAGE;
+    static constexpr int PITCH = T + 4;                 // staged row, floats
+    static constexpr int EPI = kSmallBM * PITCH * 4;
+    static constexpr int LDS = (RING > EPI ? RING : EPI) + 16;
+    static_assert(SR % (16 * NW) == 0 && kSmallBM % (16 * NW) == 0, "load slots");
+};
+
+template <int T>
+__global__ __launch_bounds__(kSmallThreads) void gate_small_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t, int M, int K, int N,
+    int C, int NRB, float *__restrict__ tw_val, int32_t *__restrict__ tw_idx,
+    int32_t *__restrict__ tw_cnt, uint32_t *__restrict__ oflag, float *__restrict__ zdbg) {
+    using P = SmallGate<T>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint32_t *s_flag = reinterpret_cast<uint32_t *>(smem + P::LDS - 16);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int rb = blockIdx.x % NRB, tc = blockIdx.x / NRB;  // row block, tile
+    const int m0 = rb * kSmallBM, n0 = tc * T;
+    const int NT = N / T;
+
+    // load slot j of a wave: stage rows [16 (4 j + wave), +16); slot 0 is x
+    const rsrc_t ra = make_rsrc(x + (size_t)m0 * K, (uint64_t)(M - m0) * K * 2);
+    const rsrc_t rw = make_rsrc(wg_t + (size_t)n0 * K, (uint64_t)T * K * 2);
+    uint32_t voff[P::NI];
+#pragma unroll
+    for (int j = 0; j < P::NI; ++j) {
+        const int row0 = (j * P::NW + wave) * 16;
+        const int sr = row0 + (lane >> 2);
+        const uint32_t row_off = j == 0 ? (uint32_t)(min(m0 + sr, M - 1) - m0) * K * 2
+                                        : (uint32_t)(sr - kSmallBM) * K * 2;
+        voff[j] = rows16_voff(row_off, lane, row0);
+    }
+    auto issue = [&](int kt, char *st) {
+        const uint32_t soff = kt * kPK * 2;
+#pragma unroll
+        for (int j = 0; j < P::NI; ++j) {
+            const int row0 = (j * P::NW + wave) * 16;
+            if (j == 0) dma16(ra, voff[j], soff, st + row0 * kPRow);
+            else dma16(rw, voff[j], soff, st + row0 * kPRow);
+        }
+    };
+    f32x16 acc[2][P::FB];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < P::FB; ++b) acc[a][b] = f32x16{};
+    u32x4 fa[2][2], fb[2][P::FB];
+    auto load = [&](const char *st, int s, int buf) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) fa[buf][a] = frag(st, a * 32, s, lane);
+#pragma unroll
+        for (int b = 0; b < P::FB; ++b)
+            fb[buf][b] = frag(st, kSmallBM + wave * P::WC + b * 32, s, lane);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
+    };
+    settle_scalars(tw_val, tw_idx, tw_cnt, oflag, zdbg);
+    kloop_pipelined<kStages, P::NI>(0, K / kPK, smem, P::STAGE, issue, load, mma);
+    __syncthreads();  // the ring becomes the tile staging
+
+    float *zs = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < P::FB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                zs[(a * 32 + mfma32_row(i, lane)) * P::PITCH + wave * P::WC + b * 32 + (lane & 31)] =
+                    acc[a][b][i];
+    if (tid < 2) s_flag[tid] = 0u;
+    __syncthreads();
+
+    constexpr int CPL = T / 64;  // columns per lane
+    uint64_t over = 0;           // bit r: row r of the block overflows (wave-uniform)
+    for (int r = wave; r < kSmallBM; r += P::NW) {
+        const int m = m0 + r;
+        if (m >= M) break;  // wave-uniform
+        float v[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) v[k] = zs[r * P::PITCH + lane * CPL + k];
+        uint32_t bits = 0;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) bits |= (v[k] > 0.0f ? 1u : 0u) << k;
+        const int cnt = __popc(bits);
+        int incl = cnt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int u = __shfl_up(incl, d);
+            if (lane >= d) incl += u;
+        }
+        const int total = __shfl(incl, 63);
+        const size_t tb = ((size_t)m * NT + tc) * C;
+        int slot = incl - cnt;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k)
+            if ((bits >> k) & 1u) {
+                if (slot < C) {
+                    tw_idx[tb + slot] = n0 + lane * CPL + k;
+                    tw_val[tb + slot] = v[k];
+                }
+                ++slot;
+            }
+        if (lane == 0) tw_cnt[(size_t)m * NT + tc] = total;
+        if (zdbg) {
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) zdbg[(size_t)m * N + n0 + lane * CPL + k] = v[k];
+        }
+        if (total > C) over |= 1ull << r;
+    }
+    if (lane == 0 && over) {
+        if ((uint32_t)over) atomicOr(&s_flag[0], (uint32_t)over);
+        if ((uint32_t)(over >> 32)) atomicOr(&s_flag[1], (uint32_t)(over >> 32));
+    }
+    __syncthreads();
+    const int MW = (M + 31) >> 5;
+    if (tid < 2 && m0 + 32 * tid < M) oflag[(size_t)tc * MW + (m0 >> 5) + tid] = s_flag[tid];
+}
+
+template <int T>
+hipError_t launch_gate_small(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int C,
+                             float *tw_val, int32_t *tw_idx, int32_t *tw_cnt, uint32_t *oflag,
+                             float *z_debug, hipStream_t s) {
+    using P = SmallGate<T>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gate_small_kernel<T>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int NRB = (M + kSmallBM - 1) / kSmallBM;
+    hipLaunchKernelGGL(gate_small_kernel<T>, dim3(NRB * (N / T)), dim3(kSmallThreads), P::LDS, s,
+                       x, wg_t, M, K, N, C, NRB, tw_val, tw_idx, tw_cnt, oflag, z_debug);
+    return hipGetLastError();
+}
+
 // Ascending list of the rows whose bit is set in any column block.  One
 // workgroup, 1024 words (32768 rows) at a time: the (word, column block)
 // pairs of a chunk are spread over all threads, each issuing its loads
@@ -310,10 +471,21 @@ hipError_t launch_gate_t(const uint16_t *x, const uint16_t *wg_t, int M, int K, 
 
 }  // namespace
 
+int gate_flag_blocks(int M, int N, int T) {
+    return M <= kGateSmallM ? N / T : gate_col_blocks(N);
+}
+
 hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
                              int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
                              uint32_t *oflag, float *z_debug, hipStream_t s) {
     if (M == 0) return hipSuccess;
+    if (M <= kGateSmallM) {
+        if (T == 128)
+            return launch_gate_small<128>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
+                                          z_debug, s);
+        return launch_gate_small<256>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug,
+                                      s);
+    }
     if (T == 128)
         return launch_gate_t<128, true>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
                                         z_debug, s);

@@ -61,8 +61,10 @@ tw_status check_hybrid(int M, int K, int N, int T, int C, int P, int R_max) {
     return TW_OK;
 }
 
+// row-overflow bits: at most N / 128 column blocks (the small-batch gate
+// kernel with T = 128) by ceil(M / 32) words
 size_t pack_ws(int M, int N) {
-    return round_up((size_t)tw::gate_col_blocks(N) * tw::row_words(M) * 4, 256);
+    return round_up((size_t)((N + 127) / 128) * tw::row_words(M) * 4, 256);
 }
 // overflow path: h rows [R_max][N] bf16, then the split partial tiles
 size_t sparse_ws(int R_max, int N) {
@@ -155,8 +157,8 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t, int M, int K, in
                                           z_debug, s),
                     "gate_twell launch"));
     TW_TRY(record(events, 1, s));
-    TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_col_blocks(N), tw::row_words(M), R_max,
-                                           ovf_rows, ovf_count, s),
+    TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_flag_blocks(M, N, T), tw::row_words(M),
+                                           R_max, ovf_rows, ovf_count, s),
                     "ovf_compact launch"));
     TW_TRY(record(events, 2, s));
     return TW_OK;

@@ -15,6 +15,13 @@ constexpr int kGateBN = 256;
 inline int gate_col_blocks(int N) { return (N + kGateBN - 1) / kGateBN; }
 inline int row_words(int M) { return (M + 31) / 32; }
 
+// Batches of at most this many rows take the small-batch gate kernel (64-row
+// tiles of one TwELL tile each), whose row-overflow bits come in N / T
+// column blocks instead of N / 256.
+constexpr int kGateSmallM = 128;
+// Column blocks of the row-overflow bits launch_gate_twell writes.
+int gate_flag_blocks(int M, int N, int T);
+
 hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
                              int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
                              uint32_t *oflag, float *z_debug, hipStream_t s);
