@@ -653,6 +653,9 @@ struct DnCfg : DN<BM, BN, WM, WN, S> {
 // tiles do little matrix work per stage, so they keep more stages in flight)
 using GuDense = GuCfg<256, 128, 4, 2, 4>;
 using GuRows = GuCfg<128, 128, 2, 4, 4>;
+// at most kSmallRows rows (decode-size batches): 64 x 64 tiles, twice the
+// workgroups of 128-column tiles and a quarter of the padded rows
+using GuSmall = GuCfg<64, 64, 2, 2, 4>;
 using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
 using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
 using DnDense = DnCfg<128, 128, 2, 2, 4>;
@@ -710,7 +713,16 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
                          int K, int N, const int32_t *rowlist, const int32_t *count, int R_cap,
                          uint16_t *h, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    if (rowlist) {
+    if (R_cap <= kSmallRows) {
+        static bool attr = false;
+        hipError_t e = set_lds(GuSmall::kernel, GuSmall::LDS, attr);
+        if (e != hipSuccess) return e;
+        const int tiles = (R_cap + GuSmall::BM_ - 1) / GuSmall::BM_ * (N / GuSmall::BN_);
+        const int grid = tiles < 1024 ? tiles : 1024;
+        hipLaunchKernelGGL(GuSmall::kernel, dim3(grid), dim3(GuSmall::NTH), GuSmall::LDS, s, x,
+                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr,
+                           nullptr, nullptr, 0.0f);
+    } else if (rowlist) {
         static bool attr = false;
         hipError_t e = set_lds(GuRows::kernel, GuRows::LDS, attr);
         if (e != hipSuccess) return e;

@@ -128,9 +128,11 @@ size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max) {
     return (a > b ? a : b) + 256;
 }
 
+// h [M][N] bf16, and for decode-size batches the down GEMM's split partials
 size_t tw_ffn_workspace_bytes(int M, int K, int N) {
     if (M < 0 || K <= 0 || N <= 0) return 0;
-    return round_up((size_t)M * N * 2, 256) + 256;
+    const size_t split = M <= tw::kSmallRows ? tw::split_partial_bytes() : 0;
+    return round_up((size_t)M * N * 2, 256) + split + 256;
 }
 
 tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int T,
@@ -292,8 +294,18 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu
     TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, nullptr, nullptr, M, h, s),
                     "dense gate+up launch"));
     TW_TRY(record(events, 1, s));
-    TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, nullptr, s),
-                    "dense down launch"));
+    if (M <= tw::kSmallRows) {
+        // few rows: split the reduction over N so that every CU has work
+        float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) +
+                                                   round_up((size_t)M * N * 2, 256));
+        TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, partial, s),
+                        "dense down launch"));
+        TW_TRY(launched(tw::launch_split_reduce(partial, nullptr, nullptr, M, K, N, y, s),
+                        "dense down split-reduce launch"));
+    } else {
+        TW_TRY(launched(tw::launch_down(h, wd, K, N, nullptr, nullptr, M, y, nullptr, s),
+                        "dense down launch"));
+    }
     TW_TRY(record(events, 2, s));
     return TW_OK;
 }

@@ -44,6 +44,10 @@ hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const u
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
                                 hipStream_t s);
 
+// Dense GEMMs over at most this many rows take small tiles (gate+up) and a
+// split reduction (down): decode-size batches.
+constexpr int kSmallRows = 64;
+
 // h[r][n] = bf16(ReLU(x_r . wg_t[n]) * (x_r . wu_t[n])) for r < rows, where
 // x_r is x[rowlist[r]] (rowlist != nullptr, rows = min(*count, R_cap)) or
 // x[r] (rowlist == nullptr, rows = R_cap).  x has M rows; with a row list
