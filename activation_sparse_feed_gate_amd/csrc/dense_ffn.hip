@@ -653,7 +653,8 @@ struct DnCfg : DN<BM, BN, WM, WN, S> {
 // tiles do little matrix work per stage, so they keep more stages in flight)
 using GuDense = GuCfg<256, 128, 4, 2, 4>;
 using GuRows = GuCfg<128, 128, 2, 4, 4>;
-// at most kSmallRows rows (decode-size batches): 64 x 64 tiles, twice the
+// 64 x 64 tiles for row lists of capacity at most kSmallRows and for
+// all-rows GEMMs too small for 128-row tiles to fill the chip: twice the
 // workgroups of 128-column tiles and a quarter of the padded rows
 using GuSmall = GuCfg<64, 64, 2, 2, 4>;
 using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
@@ -662,6 +663,7 @@ using DnDense = DnCfg<128, 128, 2, 2, 4>;
 using DnRows = DnCfg<128, 128, 2, 4, 6>;
 using DnRowsAcc = DnCfg<128, 128, 2, 4, 6, true>;
 constexpr int kSplitGrid = 256;  // work items of the split down GEMM
+constexpr int kFillTiles = 256;  // output tiles that fill the chip (one per CU)
 
 using WgCfg = WGR<256, 256, 2, 4, 4>;
 constexpr auto kWgrad = &wgrad_kernel<256, 256, 2, 4, 4>;
@@ -713,7 +715,13 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
                          int K, int N, const int32_t *rowlist, const int32_t *count, int R_cap,
                          uint16_t *h, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    if (R_cap <= kSmallRows) {
+    // row list: small tiles up to kSmallRows of capacity (the actual count is
+    // on the device; overflow rows are a small share of the batch).  All
+    // rows: the largest tiles that still fill the chip.
+    const bool small = rowlist
+                           ? R_cap <= kSmallRows
+                           : (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_) < kFillTiles;
+    if (small) {
         static bool attr = false;
         hipError_t e = set_lds(GuSmall::kernel, GuSmall::LDS, attr);
         if (e != hipSuccess) return e;
@@ -733,7 +741,7 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
         hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
                            wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr, nullptr,
                            nullptr, 0.0f);
-    } else {
+    } else if ((R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_) >= kFillTiles) {
         static bool attr = false;
         hipError_t e = set_lds(GuDense::kernel, GuDense::LDS, attr);
         if (e != hipSuccess) return e;
@@ -741,8 +749,21 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
         hipLaunchKernelGGL(GuDense::kernel, dim3(grid), dim3(GuDense::NTH), GuDense::LDS, s, x,
                            wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr,
                            nullptr, nullptr, 0.0f);
+    } else {
+        // all rows, too few 256-row tiles to fill the chip: 128-row tiles
+        static bool attr = false;
+        hipError_t e = set_lds(GuRows::kernel, GuRows::LDS, attr);
+        if (e != hipSuccess) return e;
+        const int grid = (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_);
+        hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
+                           wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr, nullptr,
+                           nullptr, 0.0f);
     }
     return hipGetLastError();
+}
+
+bool dense_down_split(int M, int K) {
+    return (size_t)((M + DnDense::BM_ - 1) / DnDense::BM_) * (K / DnDense::BN_) < kFillTiles;
 }
 
 hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,

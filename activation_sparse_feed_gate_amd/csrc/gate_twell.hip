@@ -472,14 +472,14 @@ hipError_t launch_gate_t(const uint16_t *x, const uint16_t *wg_t, int M, int K, 
 }  // namespace
 
 int gate_flag_blocks(int M, int N, int T) {
-    return M <= kGateSmallM ? N / T : gate_col_blocks(N);
+    return gate_small(M, N) ? N / T : gate_col_blocks(N);
 }
 
 hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
                              int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
                              uint32_t *oflag, float *z_debug, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    if (M <= kGateSmallM) {
+    if (gate_small(M, N)) {
         if (T == 128)
             return launch_gate_small<128>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
                                           z_debug, s);

@@ -128,10 +128,10 @@ size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max) {
     return (a > b ? a : b) + 256;
 }
 
-// h [M][N] bf16, and for decode-size batches the down GEMM's split partials
+// h [M][N] bf16, and when the down GEMM splits its reduction its partials
 size_t tw_ffn_workspace_bytes(int M, int K, int N) {
     if (M < 0 || K <= 0 || N <= 0) return 0;
-    const size_t split = M <= tw::kSmallRows ? tw::split_partial_bytes() : 0;
+    const size_t split = tw::dense_down_split(M, K) ? tw::split_partial_bytes() : 0;
     return round_up((size_t)M * N * 2, 256) + split + 256;
 }
 
@@ -294,7 +294,7 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint16_t *wu
     TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, nullptr, nullptr, M, h, s),
                     "dense gate+up launch"));
     TW_TRY(record(events, 1, s));
-    if (M <= tw::kSmallRows) {
+    if (tw::dense_down_split(M, K)) {
         // few rows: split the reduction over N so that every CU has work
         float *partial = reinterpret_cast<float *>(static_cast<char *>(ws) +
                                                    round_up((size_t)M * N * 2, 256));

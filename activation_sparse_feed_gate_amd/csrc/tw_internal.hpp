@@ -15,10 +15,13 @@ constexpr int kGateBN = 256;
 inline int gate_col_blocks(int N) { return (N + kGateBN - 1) / kGateBN; }
 inline int row_words(int M) { return (M + 31) / 32; }
 
-// Batches of at most this many rows take the small-batch gate kernel (64-row
-// tiles of one TwELL tile each), whose row-overflow bits come in N / T
+// Whether a batch of M rows takes the small-batch gate kernel (64-row tiles
+// of one TwELL tile each): while the 256 x 256 macro tiles would number
+// fewer than 64 (measured crossover).  Its row-overflow bits come in N / T
 // column blocks instead of N / 256.
-constexpr int kGateSmallM = 128;
+inline bool gate_small(int M, int N) {
+    return (long long)((M + kGateBM - 1) / kGateBM) * gate_col_blocks(N) < 64;
+}
 // Column blocks of the row-overflow bits launch_gate_twell writes.
 int gate_flag_blocks(int M, int N, int T);
 
@@ -44,9 +47,12 @@ hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const u
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
                                 hipStream_t s);
 
-// Dense GEMMs over at most this many rows take small tiles (gate+up) and a
-// split reduction (down): decode-size batches.
-constexpr int kSmallRows = 64;
+// Row-list gate+up GEMMs with a capacity of at most this many rows take
+// 64 x 64 tiles (measured faster up to 2048 at every shape here).
+constexpr int kSmallRows = 2048;
+// Whether the all-rows down GEMM of M rows splits its reduction (too few
+// output tiles to fill the chip); it then needs split_partial_bytes().
+bool dense_down_split(int M, int K);
 
 // h[r][n] = bf16(ReLU(x_r . wg_t[n]) * (x_r . wu_t[n])) for r < rows, where
 // x_r is x[rowlist[r]] (rowlist != nullptr, rows = min(*count, R_cap)) or

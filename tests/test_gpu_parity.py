@@ -60,6 +60,10 @@ def _full_check(tw, w, R_max=None, dense=True):
     dict(M=300, K=384, N=1152, T=128, C=8, density=0.02, sigma_s=0.5),  # ragged M, half column block
     dict(M=513, K=512, N=2048, T=256, C=12, density=0.01, sigma_s=0.7, seed=3),
     dict(M=1, K=128, N=128, T=128, C=3, density=0.1),
+    # batches large enough for the 256 x 256 gate kernel (the others take the
+    # small-batch one): a half-empty last column block, and T = 256
+    dict(M=4096, K=256, N=1152, T=128, C=8, density=0.02, sigma_s=0.5),
+    dict(M=2048, K=256, N=2048, T=256, C=12, density=0.01, sigma_s=0.7, seed=5),
 ])
 def test_tiny_all_rows(tw, kw):
     _full_check(tw, W["tiny"].with_(**kw))
