@@ -628,15 +628,6 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
     }
 }
 
-template <typename F>
-hipError_t set_lds(F *kernel, int bytes, bool &done) {
-    if (done) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess) done = true;
-    return e;
-}
-
 // A kernel instantiation with its shape constants.
 template <int BM, int BN, int WM, int WN, int S, int MODE = kGU>
 struct GuCfg : GU<BM, BN, WM, WN, S, MODE == kDh ? 1 : 2> {
@@ -688,16 +679,14 @@ hipError_t launch_backup_wgrad(const uint16_t *dy, const uint16_t *x, int K, int
     // 256 x 256 tiles (twice the flops per loaded byte of 128 x 128) when
     // they fill the chip, else 128 x 128
     if ((N % 256) == 0 && (K % 256) == 0 && 3 * (N / 256) * (K / 256) >= 128) {
-        static bool attr = false;
-        hipError_t e = set_lds(kWgrad, WgCfg::LDS, attr);
+        hipError_t e = lds_limit_once<kWgrad>(WgCfg::LDS);
         if (e != hipSuccess) return e;
         const int tiles = (N / 256) * (K / 256);
         hipLaunchKernelGGL(kWgrad, dim3(tiles < 1024 ? tiles : 1024, 3), dim3(WgCfg::NTH),
                            WgCfg::LDS, s, bk_h, bk_du, bk_dz, dy_bk, x_bk, x_bk, N, K, count,
                            R_cap, dwd, dwu_t, dwg_t);
     } else {
-        static bool attr = false;
-        hipError_t e = set_lds(kWgradSmall, WgSmall::LDS, attr);
+        hipError_t e = lds_limit_once<kWgradSmall>(WgSmall::LDS);
         if (e != hipSuccess) return e;
         const int tiles = (N / 128) * (K / 128);
         hipLaunchKernelGGL(kWgradSmall, dim3(tiles < 1024 ? tiles : 1024, 3), dim3(WgSmall::NTH),
@@ -722,8 +711,7 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
                            ? R_cap <= kSmallRows
                            : (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_) < kFillTiles;
     if (small) {
-        static bool attr = false;
-        hipError_t e = set_lds(GuSmall::kernel, GuSmall::LDS, attr);
+        hipError_t e = lds_limit_once<GuSmall::kernel>(GuSmall::LDS);
         if (e != hipSuccess) return e;
         const int tiles = (R_cap + GuSmall::BM_ - 1) / GuSmall::BM_ * (N / GuSmall::BN_);
         const int grid = tiles < 1024 ? tiles : 1024;
@@ -731,8 +719,7 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
                            wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr,
                            nullptr, nullptr, 0.0f);
     } else if (rowlist) {
-        static bool attr = false;
-        hipError_t e = set_lds(GuRows::kernel, GuRows::LDS, attr);
+        hipError_t e = lds_limit_once<GuRows::kernel>(GuRows::LDS);
         if (e != hipSuccess) return e;
         // one workgroup per CU at most: the grid is sized for the capacity
         // and most of it would find no rows
@@ -742,8 +729,7 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
                            wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr, nullptr,
                            nullptr, 0.0f);
     } else if ((R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_) >= kFillTiles) {
-        static bool attr = false;
-        hipError_t e = set_lds(GuDense::kernel, GuDense::LDS, attr);
+        hipError_t e = lds_limit_once<GuDense::kernel>(GuDense::LDS);
         if (e != hipSuccess) return e;
         const int grid = (R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_);
         hipLaunchKernelGGL(GuDense::kernel, dim3(grid), dim3(GuDense::NTH), GuDense::LDS, s, x,
@@ -751,8 +737,7 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
                            nullptr, nullptr, 0.0f);
     } else {
         // all rows, too few 256-row tiles to fill the chip: 128-row tiles
-        static bool attr = false;
-        hipError_t e = set_lds(GuRows::kernel, GuRows::LDS, attr);
+        hipError_t e = lds_limit_once<GuRows::kernel>(GuRows::LDS);
         if (e != hipSuccess) return e;
         const int grid = (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_);
         hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
@@ -772,8 +757,7 @@ hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,
                               uint16_t *u_out, hipStream_t s) {
     if (!g_out && !u_out) return launch_gateup(x, M, wg_t, wu_t, K, N, rowlist, count, R_cap, h, s);
     if (R_cap <= 0) return hipSuccess;
-    static bool attr = false;
-    hipError_t e = set_lds(GuRowsKeep::kernel, GuRowsKeep::LDS, attr);
+    hipError_t e = lds_limit_once<GuRowsKeep::kernel>(GuRowsKeep::LDS);
     if (e != hipSuccess) return e;
     const int tiles = (R_cap + GuRowsKeep::BM_ - 1) / GuRowsKeep::BM_ * (N / GuRowsKeep::BN_);
     const int grid = tiles < 256 ? tiles : 256;
@@ -788,8 +772,7 @@ hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K
                             const uint16_t *g_in, const uint16_t *u_in, float l1,
                             uint16_t *du, uint16_t *dz, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    static bool attr = false;
-    hipError_t e = set_lds(GuRowsDh::kernel, GuRowsDh::LDS, attr);
+    hipError_t e = lds_limit_once<GuRowsDh::kernel>(GuRowsDh::LDS);
     if (e != hipSuccess) return e;
     const int tiles = (R_cap + GuRowsDh::BM_ - 1) / GuRowsDh::BM_ * (N / GuRowsDh::BN_);
     const int grid = tiles < 256 ? tiles : 256;
@@ -804,21 +787,18 @@ hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        float *partial, hipStream_t s, bool accum) {
     if (R_cap <= 0) return hipSuccess;
     if (partial && accum) {
-        static bool attr = false;
-        hipError_t e = set_lds(DnRowsAcc::kernel, DnRowsAcc::LDS, attr);
+        hipError_t e = lds_limit_once<DnRowsAcc::kernel>(DnRowsAcc::LDS);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(DnRowsAcc::kernel, dim3(kSplitGrid), dim3(DnRowsAcc::NTH),
                            DnRowsAcc::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial);
     } else if (partial) {
-        static bool attr = false;
-        hipError_t e = set_lds(DnRows::kernel, DnRows::LDS, attr);
+        hipError_t e = lds_limit_once<DnRows::kernel>(DnRows::LDS);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(DnRows::kernel, dim3(kSplitGrid), dim3(DnRows::NTH), DnRows::LDS, s, h,
                            wd, K, N, rowlist, count, R_cap, y, partial);
     } else {
         if (accum) return hipErrorInvalidValue;  // not instantiated: unsplit accumulate
-        static bool attr = false;
-        hipError_t e = set_lds(DnDense::kernel, DnDense::LDS, attr);
+        hipError_t e = lds_limit_once<DnDense::kernel>(DnDense::LDS);
         if (e != hipSuccess) return e;
         const int tiles = (R_cap + DnDense::BM_ - 1) / DnDense::BM_ * (K / DnDense::BN_);
         hipLaunchKernelGGL(DnDense::kernel, dim3(tiles), dim3(DnDense::NTH), DnDense::LDS, s, h,

@@ -373,12 +373,9 @@ hipError_t launch_gate_small(const uint16_t *x, const uint16_t *wg_t, int M, int
                              float *tw_val, int32_t *tw_idx, int32_t *tw_cnt, uint32_t *oflag,
                              float *z_debug, hipStream_t s) {
     using P = SmallGate<T>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&gate_small_kernel<T>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, P::LDS);
+    {
+        const hipError_t e = lds_limit_once<&gate_small_kernel<T>>(P::LDS);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int NRB = (M + kSmallBM - 1) / kSmallBM;
     hipLaunchKernelGGL(gate_small_kernel<T>, dim3(NRB * (N / T)), dim3(kSmallThreads), P::LDS, s,
@@ -454,13 +451,9 @@ template <int T, bool PACK>
 hipError_t launch_gate_t(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int C,
                          float *tw_val, int32_t *tw_idx, int32_t *tw_cnt, uint32_t *oflag,
                          float *z_debug, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void *>(&gate_twell_kernel<T, PACK>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    {
+        const hipError_t e = lds_limit_once<&gate_twell_kernel<T, PACK>>(kLdsBytes);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     const int NBN = gate_col_blocks(N);
     const int NBM = (M + kGateBM - 1) / kGateBM;

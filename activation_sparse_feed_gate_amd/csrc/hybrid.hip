@@ -543,13 +543,9 @@ hipError_t launch_down_k(const uint16_t *wd, const uint16_t *w2, int M, int K, i
                          const float *hy_h, const float *v2, const int32_t *hy_idx,
                          const int32_t *hy_cnt, const uint8_t *route, float *y, hipStream_t s) {
     const size_t lds = (size_t)kWaves * KCH * 512 * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&hybrid_down_kernel<KCH, TWO>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    {
+        const hipError_t e = lds_limit_once<&hybrid_down_kernel<KCH, TWO>>((int)lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL((hybrid_down_kernel<KCH, TWO>), dim3(M), dim3(kThreads), lds, s, wd, w2,
                        K, N, P, hy_h, v2, hy_idx, hy_cnt, route, y);

@@ -206,13 +206,9 @@ hipError_t launch_kw(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd
                      int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
                      const int32_t *tw_cnt, float *y, hipStream_t s) {
     const size_t lds = (size_t)NWV * KCH * 512 * sizeof(float);  // y staging
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e =
-            hipFuncSetAttribute(reinterpret_cast<const void *>(&sparse_updown_kernel<KCH, NWV>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    {
+        const hipError_t e = lds_limit_once<&sparse_updown_kernel<KCH, NWV>>((int)lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     hipLaunchKernelGGL((sparse_updown_kernel<KCH, NWV>), dim3(M), dim3(NWV * 64), lds, s, x,
                        wu_t, wd, K, N, NT, C, tw_val, tw_idx, tw_cnt, y);

@@ -89,4 +89,15 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Raise a kernel's dynamic LDS limit once per process: the first call sets
+// the attribute and every later call returns that result (a function-local
+// static is initialised exactly once, also when several host threads launch
+// concurrently).
+template <auto Kernel>
+inline hipError_t lds_limit_once(int bytes) {
+    static const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return e;
+}
+
 }  // namespace tw
