@@ -261,12 +261,14 @@ struct DN {
 // positions, i.e. all 64 banks once.
 __device__ __forceinline__ int bsw(int row) { return 4 * (row & 3); }
 
-// ACC: add the product into y (the unsplit epilogue) instead of storing it.
-template <int BM, int BN, int WM, int WN, int STG, bool ACC>
+// PAIRS = 2: y = h W_d + h2 W_d2, the reduction running over the first pair's
+// stages, then the second's (same shapes), in one GEMM.
+template <int BM, int BN, int WM, int WN, int STG, int PAIRS>
 __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
     const uint16_t *__restrict__ h, const uint16_t *__restrict__ wd, int K, int N,
     const int32_t *__restrict__ rowlist, const int32_t *__restrict__ count, int R_cap,
-    float *__restrict__ y, float *__restrict__ partial) {
+    float *__restrict__ y, float *__restrict__ partial, const uint16_t *__restrict__ h2,
+    const uint16_t *__restrict__ wd2) {
     using P = DN<BM, BN, WM, WN, STG>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -274,7 +276,8 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
     const int nrb = (rows + BM - 1) / BM;
     const int ncb = K / BN;
     const int tiles = nrb * ncb;
-    const int NS = N / kPK;  // stages over the whole reduction
+    const int NS1 = N / kPK;     // stages of one pair's reduction
+    const int NS = PAIRS * NS1;  // stages over the whole reduction
     const int S = partial ? split_count(tiles, gridDim.x, NS) : 1;  // reduction splits
     const int work = tiles * S;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -293,6 +296,9 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
 
         const rsrc_t rh = make_rsrc(h + (size_t)m0 * N, (uint64_t)(rows - m0) * N * 2);
         const rsrc_t rd = make_rsrc(wd + k0, ((uint64_t)N * K - k0) * 2);
+        const rsrc_t rh2 =
+            PAIRS == 2 ? make_rsrc(h2 + (size_t)m0 * N, (uint64_t)(rows - m0) * N * 2) : rh;
+        const rsrc_t rd2 = PAIRS == 2 ? make_rsrc(wd2 + k0, ((uint64_t)N * K - k0) * 2) : rd;
         uint32_t aoff[P::NIA], boff[P::NIB];
 #pragma unroll
         for (int j = 0; j < P::NIA; ++j) {
@@ -307,19 +313,25 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
             const int row = (wave * P::NIB + j) * P::BR_PER + brl;
             boff[j] = (uint32_t)row * K * 2 + (uint32_t)(((lane & 15) ^ bsw(row)) << 4);
         }
-        auto issue = [&](int kt, char *st) {
-            const uint32_t soff_a = kt * kPK * 2;
-            const uint32_t soff_b = (uint32_t)kt * kPK * K * 2;
+        // one pair's stage kk into ring slot st (each call site passes fixed
+        // descriptors: the pair is chosen by a uniform branch, not a select)
+        auto put = [&](const rsrc_t ra, const rsrc_t rb, int kk, char *st) {
+            const uint32_t soff_a = kk * kPK * 2;
+            const uint32_t soff_b = (uint32_t)kk * kPK * K * 2;
 #pragma unroll
             for (int j = 0; j < P::NIA; ++j) {
                 const int row0 = (wave * P::NIA + j) * 16;
-                dma16(rh, aoff[j], soff_a, st + row0 * kPRow);
+                dma16(ra, aoff[j], soff_a, st + row0 * kPRow);
             }
 #pragma unroll
             for (int j = 0; j < P::NIB; ++j) {
                 const int row = (wave * P::NIB + j) * P::BR_PER;
-                dma16(rd, boff[j], soff_b, st + P::A_BYTES + row * P::BROW);
+                dma16(rb, boff[j], soff_b, st + P::A_BYTES + row * P::BROW);
             }
+        };
+        auto issue = [&](int kt, char *st) {
+            if (PAIRS == 2 && kt >= NS1) put(rh2, rd2, kt - NS1, st);
+            else put(rh, rd, kt, st);
         };
         f32x16 acc[P::FA][P::FB];
 #pragma unroll
@@ -358,8 +370,8 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
         kloop_pipelined<STG, P::NI>(kt0, kt1, smem, P::STAGE, issue, load, mma);
 
         if (S == 1) {
-            // per 32-row block: the row indices (and with ACC the old values)
-            // are all loaded before the first store
+            // per 32-row block: the row indices are all loaded before the
+            // first store
 #pragma unroll
             for (int a = 0; a < P::FA; ++a) {
                 // rows past `rows` read a valid row (clamped) and store nothing
@@ -372,22 +384,12 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
                     const int rr = min(r, rows - 1);
                     yr[i] = rowlist ? rowlist[rr] : rr;
                 }
-                float old[ACC ? 16 : 1][P::FB];
-                if constexpr (ACC) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-#pragma unroll
-                        for (int b = 0; b < P::FB; ++b)
-                            old[i][b] = y[(size_t)yr[i] * K + k0 + wn * P::TN + b * 32 + l32];
-                }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     if (!ok[i]) continue;
 #pragma unroll
                     for (int b = 0; b < P::FB; ++b) {
-                        float *yp = y + (size_t)yr[i] * K + k0 + wn * P::TN + b * 32 + l32;
-                        if constexpr (ACC) *yp = old[i][b] + acc[a][b][i];
-                        else *yp = acc[a][b][i];
+                        y[(size_t)yr[i] * K + k0 + wn * P::TN + b * 32 + l32] = acc[a][b][i];
                     }
                 }
             }
@@ -416,7 +418,7 @@ template <int BM, int BN>
 __global__ __launch_bounds__(256) void split_reduce_kernel(
     const float *__restrict__ partial, const int32_t *__restrict__ rowlist,
     const int32_t *__restrict__ count, int R_cap, int K, int N, int grid_down,
-    float *__restrict__ y, int accum) {
+    float *__restrict__ y) {
     constexpr int kMaxSplit = 16;
     const int rows = rows_of(count, R_cap);
     const int nrb = (rows + BM - 1) / BM;
@@ -442,15 +444,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(
                 sum.z += v[s2].z;
                 sum.w += v[s2].w;
             }
-        float4 *yp = reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col);
-        if (accum) {
-            const float4 old = *yp;
-            sum.x = old.x + sum.x;
-            sum.y = old.y + sum.y;
-            sum.z = old.z + sum.z;
-            sum.w = old.w + sum.w;
-        }
-        *yp = sum;
+        *reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col) = sum;
     }
 }
 
@@ -634,10 +628,10 @@ struct GuCfg : GU<BM, BN, WM, WN, S, MODE == kDh ? 1 : 2> {
     static constexpr int BM_ = BM, BN_ = BN;
     static constexpr auto kernel = &gateup_kernel<BM, BN, WM, WN, S, MODE>;
 };
-template <int BM, int BN, int WM, int WN, int S, bool ACC = false>
+template <int BM, int BN, int WM, int WN, int S, int PAIRS = 1>
 struct DnCfg : DN<BM, BN, WM, WN, S> {
     static constexpr int BM_ = BM, BN_ = BN;
-    static constexpr auto kernel = &down_kernel<BM, BN, WM, WN, S, ACC>;
+    static constexpr auto kernel = &down_kernel<BM, BN, WM, WN, S, PAIRS>;
 };
 
 // dense comparator shapes and overflow-path shapes (the thin overflow
@@ -652,7 +646,7 @@ using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
 using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
 using DnDense = DnCfg<128, 128, 2, 2, 4>;
 using DnRows = DnCfg<128, 128, 2, 4, 6>;
-using DnRowsAcc = DnCfg<128, 128, 2, 4, 6, true>;
+using DnRowsPair = DnCfg<128, 128, 2, 4, 6, 2>;
 constexpr int kSplitGrid = 256;  // work items of the split down GEMM
 constexpr int kFillTiles = 256;  // output tiles that fill the chip (one per CU)
 
@@ -784,38 +778,47 @@ hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K
 
 hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
-                       float *partial, hipStream_t s, bool accum) {
+                       float *partial, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    if (partial && accum) {
-        hipError_t e = lds_limit_once<DnRowsAcc::kernel>(DnRowsAcc::LDS);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(DnRowsAcc::kernel, dim3(kSplitGrid), dim3(DnRowsAcc::NTH),
-                           DnRowsAcc::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial);
-    } else if (partial) {
+    if (partial) {
         hipError_t e = lds_limit_once<DnRows::kernel>(DnRows::LDS);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(DnRows::kernel, dim3(kSplitGrid), dim3(DnRows::NTH), DnRows::LDS, s, h,
-                           wd, K, N, rowlist, count, R_cap, y, partial);
+                           wd, K, N, rowlist, count, R_cap, y, partial, nullptr, nullptr);
     } else {
-        if (accum) return hipErrorInvalidValue;  // not instantiated: unsplit accumulate
         hipError_t e = lds_limit_once<DnDense::kernel>(DnDense::LDS);
         if (e != hipSuccess) return e;
         const int tiles = (R_cap + DnDense::BM_ - 1) / DnDense::BM_ * (K / DnDense::BN_);
         hipLaunchKernelGGL(DnDense::kernel, dim3(tiles), dim3(DnDense::NTH), DnDense::LDS, s, h,
-                           wd, K, N, rowlist, count, R_cap, y, partial);
+                           wd, K, N, rowlist, count, R_cap, y, partial, nullptr, nullptr);
     }
     return hipGetLastError();
 }
 
+hipError_t launch_down_pair(const uint16_t *h, const uint16_t *wd, const uint16_t *h2,
+                            const uint16_t *wd2, int K, int N, const int32_t *rowlist,
+                            const int32_t *count, int R_cap, float *y, float *partial,
+                            hipStream_t s) {
+    if (R_cap <= 0) return hipSuccess;
+    hipError_t e = lds_limit_once<DnRowsPair::kernel>(DnRowsPair::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(DnRowsPair::kernel, dim3(kSplitGrid), dim3(DnRowsPair::NTH),
+                       DnRowsPair::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial, h2,
+                       wd2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the split count follows the whole reduction: 2 N / kPK stages
+    return launch_split_reduce(partial, rowlist, count, R_cap, K, 2 * N, y, s);
+}
+
 hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
                                const int32_t *count, int R_cap, int K, int N, float *y,
-                               hipStream_t s, bool accum) {
+                               hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
     // enough workgroups for the largest split case: at most kSplitGrid tiles
     int grid = (int)(((size_t)R_cap * K / 4 + 255) / 256);
     grid = grid < 1024 ? grid : 1024;
     hipLaunchKernelGGL((split_reduce_kernel<DnRows::BM_, DnRows::BN_>), dim3(grid), dim3(256), 0, s, partial,
-                       rowlist, count, R_cap, K, N, kSplitGrid, y, (int)accum);
+                       rowlist, count, R_cap, K, N, kSplitGrid, y);
     return hipGetLastError();
 }
 

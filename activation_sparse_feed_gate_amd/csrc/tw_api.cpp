@@ -491,19 +491,12 @@ tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, in
                     "hybrid dx launch"));
     TW_TRY(record(events, 1, s));
     if (R_max > 0) {
-        // dx = du W_u^T, then dx += dz W_g^T: two split GEMMs over the backup
-        // rows, each summed in split order
+        // dx = du W_u^T + dz W_g^T: one split GEMM whose reduction runs over
+        // both products, summed in split order
         float *partial = static_cast<float *>(ws);
-        TW_TRY(launched(tw::launch_down(bk_du, wu_t, K, N, bk_rows, bk_count, R_max, dx, partial, s),
-                        "backup dx (up) launch"));
-        TW_TRY(launched(tw::launch_split_reduce(partial, bk_rows, bk_count, R_max, K, N, dx, s),
-                        "backup dx (up) split-reduce launch"));
-        TW_TRY(launched(tw::launch_down(bk_dz, wg_t, K, N, bk_rows, bk_count, R_max, dx, partial, s,
-                                        true),
-                        "backup dx (gate) launch"));
-        TW_TRY(launched(tw::launch_split_reduce(partial, bk_rows, bk_count, R_max, K, N, dx, s,
-                                                true),
-                        "backup dx (gate) split-reduce launch"));
+        TW_TRY(launched(tw::launch_down_pair(bk_du, wu_t, bk_dz, wg_t, K, N, bk_rows, bk_count,
+                                             R_max, dx, partial, s),
+                        "backup dx launch"));
     }
     TW_TRY(record(events, 2, s));
     return TW_OK;

@@ -79,17 +79,22 @@ hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K
                             uint16_t *du, uint16_t *dz, hipStream_t s);
 
 // y[row_r][k] = sum_n h[r][n] * wd[n][k] (fp32) for r < rows, with row_r =
-// rowlist[r] or r as above (accum: y[row_r][k] += that sum instead).  With a
-// `partial` buffer (split_partial_bytes()) the reduction is split when there
-// are few rows, and launch_split_reduce (with the same accum) must follow on
-// the stream to sum the partial tiles into y.
+// rowlist[r] or r as above.  With a `partial` buffer (split_partial_bytes())
+// the reduction is split when there are few rows, and launch_split_reduce
+// must follow on the stream to sum the partial tiles into y.
 hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
                        const int32_t *rowlist, const int32_t *count, int R_cap, float *y,
-                       float *partial, hipStream_t s, bool accum = false);
+                       float *partial, hipStream_t s);
 hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
                                const int32_t *count, int R_cap, int K, int N, float *y,
-                               hipStream_t s, bool accum = false);
+                               hipStream_t s);
 size_t split_partial_bytes();
+// y[row_r] = h[r] W_d + h2[r] W_d2 for r < rows (row list as above): one split
+// GEMM over both reductions, then its split sum (partial as for launch_down).
+hipError_t launch_down_pair(const uint16_t *h, const uint16_t *wd, const uint16_t *h2,
+                            const uint16_t *wd2, int K, int N, const int32_t *rowlist,
+                            const int32_t *count, int R_cap, float *y, float *partial,
+                            hipStream_t s);
 
 // Hybrid storage of the training forward (hybrid.hip).
 hipError_t launch_hybrid_pack(const float *tw_val, const int32_t *tw_idx, const int32_t *tw_cnt,

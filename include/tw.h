@@ -189,10 +189,11 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
 /*
  * Dense gated FFN over all M rows (section 1-1 equation): the gate and up
  * projections in one MFMA GEMM whose epilogue forms h = ReLU(g) * u rounded
- * to bf16, then the down projection into fp32 y [M][K] (for M <= 64 split
- * over N and summed by a second kernel; events[2] follows both).
- * The workspace holds h [M][N] bf16 (and for M <= 64 the split partial
- * sums): ws_bytes >= tw_ffn_workspace_bytes.
+ * to bf16, then the down projection into fp32 y [M][K] (when M is too small
+ * for its output tiles to fill the chip, split over N and summed by a
+ * second kernel; events[2] follows both).  The workspace holds h [M][N]
+ * bf16 and, when the down projection splits, the partial sums:
+ * ws_bytes >= tw_ffn_workspace_bytes.
  * Shapes: M >= 0, K and N positive multiples of 128, N * K < 2^31 (each
  * weight matrix under 4 GiB: 32-bit buffer offsets).
  */
