@@ -48,8 +48,11 @@ hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const u
                                 hipStream_t s);
 
 // Row-list gate+up GEMMs with a capacity of at most this many rows take
-// 64 x 64 tiles (measured faster up to 2048 at every shape here).
-constexpr int kSmallRows = 2048;
+// 64 x 64 tiles.  The row count itself is known only on the device; with the
+// usual capacity of an eighth of the batch, 64 x 64 tiles measured faster
+// below about 400 listed rows and 128 x 128 tiles above (at 360-1000 rows
+// the larger tiles took 25-40% less time).
+constexpr int kSmallRows = 512;
 // Whether the all-rows down GEMM of M rows splits its reduction (too few
 // output tiles to fill the chip); it then needs split_partial_bytes().
 bool dense_down_split(int M, int K);

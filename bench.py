@@ -369,6 +369,9 @@ def main():
     ap.add_argument("--density", type=float, default=None, help="override the target density")
     ap.add_argument("--M", type=int, default=None,
                     help="override the token count (decode-like batches)")
+    ap.add_argument("--r-max", type=int, default=None,
+                    help="overflow-row capacity (default: an eighth of the batch, grown by "
+                         "the retry rule before timing)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -405,7 +408,10 @@ def main():
     if args.M is not None:
         w = w.with_(M=args.M)
     M, K, N, T, C = w.M, w.K, w.N, w.T, w.C
-    R_max = M  # room for every row: timing never needs the retry
+    # overflow capacity: the static backup capacity of the review §4-3 (an
+    # eighth of the batch); if the batch overflows it, the retry rule there
+    # (read the true count on the host, allocate more) runs before timing
+    R_max = min(M, args.r_max) if args.r_max is not None else max(1, M // 8)
     d = synth.make_inputs(w)
 
     def dev(bits):
@@ -431,6 +437,18 @@ def main():
 
     def dense(ev=None):
         tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd, stream=stream, events=ev)
+
+    retries = 0
+    while True:
+        tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"],
+                        bufs["ovf_rows"], bufs["ovf_count"], R_max, ws, stream=stream)
+        n_ovf = int(bufs["ovf_count"].cpu()[0])
+        if n_ovf <= R_max:
+            break
+        R_max = min(M, max(2 * R_max, n_ovf))
+        bufs = tw.alloc_pack(M, N, T, C, R_max)
+        ws = tw.workspace(M, K, N, T, C, R_max)
+        retries += 1
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
@@ -697,7 +715,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": M, "K": K, "N": N, "T": T, "C": C,
-                   "density": w.density, "sigma_s": w.sigma_s, "seed": w.seed, "R_max": R_max},
+                   "density": w.density, "sigma_s": w.sigma_s, "seed": w.seed, "R_max": R_max,
+                   "capacity_retries": retries},
         "roofline": roof(dominant, kern[dominant]),
         "speedup_vs_dense": t_dense / t_sparse,
         "ms_per_step_p10_p50_p90": [float(np.percentile(per_sparse, q)) * 1e3 for q in (10, 50, 90)],
