@@ -31,11 +31,19 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 class HipEvents:
-    """hipEvent_t handles through the HIP runtime torch already loaded."""
+    """hipEvent_t handles through the HIP runtime torch already loaded.
+
+    The events are created with hipEventDisableSystemFence: they only time
+    work, so recording one needs no system-scope release, whose cache
+    write-back and invalidation would otherwise fall between every bracketed
+    kernel and the next and add to the measured durations."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                     ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -44,9 +52,9 @@ class HipEvents:
         out = []
         for _ in range(n):
             e = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
             if rc != 0:
-                raise RuntimeError(f"hipEventCreate failed: {rc}")
+                raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
             out.append(e.value)
         return out
 
