@@ -19,15 +19,18 @@
 //   gfx950 LDS read that transposes 16-bit elements across a 16-lane group.
 // - With few rows (the overflow path) the down GEMM also splits the
 //   reduction over N so that every CU has work; each split writes a partial
-//   tile and a small kernel sums the partials in split order (the result
-//   does not depend on timing).  A device-scope fence per workgroup instead
-//   would write back the whole L2 of its XCD each time.
+//   tile and the partials are summed in split order (the result does not
+//   depend on timing) by a small kernel, or, for the inference path's
+//   overflow rows, by the sparse kernel that runs next (tw_split.hpp).  A
+//   device-scope fence per workgroup instead would write back the whole L2
+//   of its XCD each time.
 // - Rows come either directly or through a row list with a device-side
 //   count (the overflow list): x rows are gathered and y rows scattered
 //   through it.
 #include "tw_device.hpp"
 #include "tw_gemm.hpp"
 #include "tw_internal.hpp"
+#include "tw_split.hpp"
 
 namespace tw {
 namespace {
@@ -224,18 +227,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     }
 }
 
-// Number of reduction splits of the overflow-path down GEMM: enough for
-// `grid` work items over `tiles` output tiles, at most 16, dividing the
-// NS stages of the reduction.  Both the GEMM and the reduction of its
-// partial tiles evaluate it from the same device-side row count.
-__device__ __forceinline__ int split_count(int tiles, int grid, int NS) {
-    if (tiles <= 0) return 1;
-    int S = grid / tiles;
-    S = S < 1 ? 1 : (S > 16 ? 16 : S);
-    while (NS % S) --S;
-    return S;
-}
-
 // --------------------------------- down -----------------------------------
 template <int BM, int BN, int WM, int WN, int S>
 struct DN {
@@ -412,39 +403,18 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
 
 // y[row_r] = sum over splits s = 0, 1, ... of the partial tiles (fixed
 // order), when the down GEMM split its reduction.  Each thread owns four
-// consecutive outputs; the loads of all its partials are issued before the
-// first add, so the kernel pays one memory latency instead of S.
-template <int BM, int BN>
+// consecutive outputs (split_sum4).
 __global__ __launch_bounds__(256) void split_reduce_kernel(
     const float *__restrict__ partial, const int32_t *__restrict__ rowlist,
-    const int32_t *__restrict__ count, int R_cap, int K, int N, int grid_down,
-    float *__restrict__ y) {
-    constexpr int kMaxSplit = 16;
+    const int32_t *__restrict__ count, int R_cap, int K, int N, float *__restrict__ y) {
     const int rows = rows_of(count, R_cap);
-    const int nrb = (rows + BM - 1) / BM;
-    const int tiles = nrb * (K / BN);
-    const int S = split_count(tiles, grid_down, N / kPK);
+    const int S = split_factor(rows, K, N);
     if (S == 1) return;
     const int K4 = K / 4;
-    const size_t split_stride = (size_t)tiles * (BM * BN);
     for (int q = blockIdx.x * 256 + threadIdx.x; q < rows * K4; q += gridDim.x * 256) {
         const int r = q / K4, col = 4 * (q % K4);
-        const int tile = (col / BN) * nrb + r / BM;  // as the split down GEMM numbers them
-        const float *src = partial + (size_t)tile * (BM * BN) + (r % BM) * BN + col % BN;
-        float4 v[kMaxSplit];
-#pragma unroll
-        for (int s2 = 0; s2 < kMaxSplit; ++s2)
-            if (s2 < S) v[s2] = *reinterpret_cast<const float4 *>(src + s2 * split_stride);
-        float4 sum = v[0];
-#pragma unroll
-        for (int s2 = 1; s2 < kMaxSplit; ++s2)
-            if (s2 < S) {
-                sum.x += v[s2].x;
-                sum.y += v[s2].y;
-                sum.z += v[s2].z;
-                sum.w += v[s2].w;
-            }
-        *reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col) = sum;
+        *reinterpret_cast<float4 *>(y + (size_t)(rowlist ? rowlist[r] : r) * K + col) =
+            split_sum4(partial, r, col, rows, K, S);
     }
 }
 
@@ -647,7 +617,9 @@ using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
 using DnDense = DnCfg<128, 128, 2, 2, 4>;
 using DnRows = DnCfg<128, 128, 2, 4, 6>;
 using DnRowsPair = DnCfg<128, 128, 2, 4, 6, 2>;
-constexpr int kSplitGrid = 256;  // work items of the split down GEMM
+static_assert(DnRows::BM_ == kSplitBM && DnRows::BN_ == kSplitBN &&
+                  DnRowsPair::BM_ == kSplitBM && DnRowsPair::BN_ == kSplitBN,
+              "the split layout of tw_split.hpp");
 constexpr int kFillTiles = 256;  // output tiles that fill the chip (one per CU)
 
 using WgCfg = WGR<256, 256, 2, 4, 4>;
@@ -817,8 +789,8 @@ hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
     // enough workgroups for the largest split case: at most kSplitGrid tiles
     int grid = (int)(((size_t)R_cap * K / 4 + 255) / 256);
     grid = grid < 1024 ? grid : 1024;
-    hipLaunchKernelGGL((split_reduce_kernel<DnRows::BM_, DnRows::BN_>), dim3(grid), dim3(256), 0, s, partial,
-                       rowlist, count, R_cap, K, N, kSplitGrid, y);
+    hipLaunchKernelGGL(split_reduce_kernel, dim3(grid), dim3(256), 0, s, partial, rowlist, count,
+                       R_cap, K, N, y);
     return hipGetLastError();
 }
 

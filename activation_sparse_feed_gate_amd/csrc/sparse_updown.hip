@@ -29,8 +29,14 @@
 // - The four partial y rows are summed in LDS in a fixed order (the result
 //   does not depend on timing) and written once; the staging is laid out so
 //   that neither its stores nor its loads have bank conflicts.
+// - The overflow rows' dense path runs first.  When its down GEMM split the
+//   reduction, workgroup m also sums the partial tiles of overflow-list
+//   position m (in split order) into that row of y, so no separate
+//   reduction kernel runs: the rows this kernel computes and the overflow
+//   rows it finishes are disjoint.
 #include "tw_device.hpp"
 #include "tw_internal.hpp"
+#include "tw_split.hpp"
 
 namespace tw {
 namespace {
@@ -47,7 +53,8 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const uint16_t *__restrict__ wd, int K, int N, int NT, int C,
     const float *__restrict__ tw_val,
     const int32_t *__restrict__ tw_idx, const int32_t *__restrict__ tw_cnt,
-    float *__restrict__ y) {
+    float *__restrict__ y, const float *__restrict__ partial,
+    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ ovf_count, int R_max) {
     constexpr int kThreads = NWV * 64, kWaves = NWV;
     constexpr int kBatch = NWV >= 8 ? 1 : 2;  // active neurons gathered together per wave
     extern __shared__ __attribute__((aligned(16))) char smem[];  // y staging, fp32
@@ -59,6 +66,20 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const int lane = tid & 63, wave = tid >> 6;
 
     const int c = tid < NT ? tw_cnt[(size_t)m * NT + tid] : 0;
+    if (partial) {
+        // overflow-list position m: its split partial tiles, summed in split
+        // order into its row of y (S = 1: the down GEMM stored the row)
+        const int rows = __builtin_amdgcn_readfirstlane(min(*ovf_count, R_max));
+        if (m < rows) {
+            const int S = split_factor(rows, K, N);
+            if (S > 1) {
+                const unsigned row = min((unsigned)ovf_rows[m], gridDim.x - 1);
+                float *yo = y + (size_t)row * K;
+                for (int col = 4 * tid; col < K; col += 4 * kThreads)
+                    *reinterpret_cast<float4 *>(yo + col) = split_sum4<8>(partial, m, col, rows, K, S);
+            }
+        }
+    }
     if (__syncthreads_or(c > C)) return;  // overflow row: dense backup
 
     // exclusive scan of the tile counts -> flat entry offsets
@@ -204,14 +225,17 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
 template <int KCH, int NWV>
 hipError_t launch_kw(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
                      int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
-                     const int32_t *tw_cnt, float *y, hipStream_t s) {
+                     const int32_t *tw_cnt, float *y, const float *partial,
+                     const int32_t *ovf_rows, const int32_t *ovf_count, int R_max,
+                     hipStream_t s) {
     const size_t lds = (size_t)NWV * KCH * 512 * sizeof(float);  // y staging
     {
         const hipError_t e = lds_limit_once<&sparse_updown_kernel<KCH, NWV>>((int)lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL((sparse_updown_kernel<KCH, NWV>), dim3(M), dim3(NWV * 64), lds, s, x,
-                       wu_t, wd, K, N, NT, C, tw_val, tw_idx, tw_cnt, y);
+                       wu_t, wd, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial, ovf_rows,
+                       ovf_count, R_max);
     return hipGetLastError();
 }
 
@@ -220,14 +244,17 @@ hipError_t launch_kw(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd
 template <int KCH>
 hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
                     int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
-                    const int32_t *tw_cnt, float *y, hipStream_t s) {
+                    const int32_t *tw_cnt, float *y, const float *partial,
+                    const int32_t *ovf_rows, const int32_t *ovf_count, int R_max,
+                    hipStream_t s) {
     // 16 waves cap a lane at 128 registers and the y staging at 16 KCH KB:
     // wide rows take 8
     constexpr int kSmallWaves = KCH <= 4 ? 16 : 8;
     if (M <= kSmallBatchRows)
         return launch_kw<KCH, kSmallWaves>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt,
-                                           y, s);
-    return launch_kw<KCH, 4>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+                                           y, partial, ovf_rows, ovf_count, R_max, s);
+    return launch_kw<KCH, 4>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial,
+                             ovf_rows, ovf_count, R_max, s);
 }
 
 }  // namespace
@@ -235,19 +262,23 @@ hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
 hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
                                 int M, int K, int N, int T, int C, const float *tw_val,
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
-                                hipStream_t s) {
+                                const float *partial, const int32_t *ovf_rows,
+                                const int32_t *ovf_count, int R_max, hipStream_t s) {
     if (M == 0) return hipSuccess;
     const int NT = N / T;
+#define TW_SPARSE_ARGS x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial, ovf_rows, \
+                       ovf_count, R_max, s
     switch ((K + 511) / 512) {
-    case 1: return launch_k<1>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
-    case 2: return launch_k<2>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
-    case 3: return launch_k<3>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
-    case 4: return launch_k<4>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
-    case 5: return launch_k<5>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
-    case 6: return launch_k<6>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
-    case 7: return launch_k<7>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
-    default: return launch_k<8>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, s);
+    case 1: return launch_k<1>(TW_SPARSE_ARGS);
+    case 2: return launch_k<2>(TW_SPARSE_ARGS);
+    case 3: return launch_k<3>(TW_SPARSE_ARGS);
+    case 4: return launch_k<4>(TW_SPARSE_ARGS);
+    case 5: return launch_k<5>(TW_SPARSE_ARGS);
+    case 6: return launch_k<6>(TW_SPARSE_ARGS);
+    case 7: return launch_k<7>(TW_SPARSE_ARGS);
+    default: return launch_k<8>(TW_SPARSE_ARGS);
     }
+#undef TW_SPARSE_ARGS
 }
 
 }  // namespace tw

@@ -244,30 +244,30 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     char *w = static_cast<char *>(ws);
     uint16_t *h = reinterpret_cast<uint16_t *>(w);
     float *partial = reinterpret_cast<float *>(w + round_up((size_t)R_max * N * 2, 256));
-    // All on the caller's stream: the sparse kernel, then the overflow
-    // rows' dense path (which writes the rows the sparse kernel skips).
-    // Running the two concurrently on a second stream was measured slower
-    // at the smaller shapes: the dense kernels' large LDS tiles cannot sit
-    // beside the sparse kernel's workgroups, and the cross-stream edges
-    // cost several microseconds each.
+    // All on the caller's stream: the overflow rows' dense path first (its
+    // down GEMM leaves split partial tiles when the rows are few), then the
+    // sparse kernel, which computes the other rows and sums those partials
+    // into the overflow rows.  Running the two paths concurrently on a
+    // second stream was measured slower at the smaller shapes: the dense
+    // kernels' large LDS tiles cannot sit beside the sparse kernel's
+    // workgroups, and the cross-stream edges cost several microseconds each.
     TW_TRY(record(events, 0, s));
-    TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx, tw_cnt,
-                                             y, s),
-                    "sparse_updown launch"));
-    TW_TRY(record(events, 1, s));
     if (R_max > 0) {
         TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, s),
                         "fallback gate+up launch"));
-        TW_TRY(record(events, 2, s));
+        TW_TRY(record(events, 1, s));
         TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, partial, s),
                         "fallback down launch"));
-        TW_TRY(record(events, 3, s));
-        TW_TRY(launched(tw::launch_split_reduce(partial, ovf_rows, ovf_count, R_max, K, N, y, s),
-                        "fallback split-reduce launch"));
-        TW_TRY(record(events, 4, s));
+        TW_TRY(record(events, 2, s));
     } else {
-        for (int i = 2; i <= 4; ++i) TW_TRY(record(events, i, s));
+        for (int i = 1; i <= 2; ++i) TW_TRY(record(events, i, s));
     }
+    TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx, tw_cnt,
+                                             y, R_max > 0 ? partial : nullptr, ovf_rows,
+                                             ovf_count, R_max, s),
+                    "sparse_updown launch"));
+    TW_TRY(record(events, 3, s));
+    TW_TRY(record(events, 4, s));
     return TW_OK;
 }
 

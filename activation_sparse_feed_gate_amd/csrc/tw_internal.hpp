@@ -42,10 +42,15 @@ hipError_t launch_pack_dense(const float *z, int M, int N, int T, int C, float *
 hipError_t launch_ovf_compact(const uint32_t *oflag, int NB, int MW, int R_max,
                               int32_t *ovf_rows, int32_t *ovf_count, hipStream_t s);
 
+// Sparse up + down of every non-overflow row into y.  With `partial` (the
+// split partial tiles launch_down left for the overflow list ovf_rows,
+// ovf_count, R_max), it also sums those into the listed rows of y, in place
+// of launch_split_reduce; partial null: overflow rows are left alone.
 hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
                                 int M, int K, int N, int T, int C, const float *tw_val,
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
-                                hipStream_t s);
+                                const float *partial, const int32_t *ovf_rows,
+                                const int32_t *ovf_count, int R_max, hipStream_t s);
 
 // Row-list gate+up GEMMs with a capacity of at most this many rows take
 // 64 x 64 tiles.  The row count itself is known only on the device; with the

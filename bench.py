@@ -71,7 +71,7 @@ class HipEvents:
 
 
 # headers every kernel source includes: a change there changes the kernels too
-_SHARED_HEADERS = ("tw_device.hpp", "tw_gemm.hpp", "tw_internal.hpp")
+_SHARED_HEADERS = ("tw_device.hpp", "tw_gemm.hpp", "tw_internal.hpp", "tw_split.hpp")
 
 
 def _src_sha(name: str) -> str:
@@ -660,14 +660,14 @@ def main():
     def span(evl, i, j):
         return sum(hev.ms(e[i], e[j]) for e in evl) / len(evl) * 1e-3
 
-    # the overflow path follows the sparse kernel on the same stream
+    # the overflow path runs first; the sparse kernel follows on the same
+    # stream and also sums the overflow rows' split partials
     kern = {
         "gate_twell": avg(evp, 0),
         "ovf_compact": avg(evp, 1),
-        "sparse_updown": span(evs, 0, 1),
-        "fallback_gateup": span(evs, 1, 2),
-        "fallback_down": span(evs, 2, 3),
-        "fallback_reduce": span(evs, 3, 4),
+        "fallback_gateup": span(evs, 0, 1),
+        "fallback_down": span(evs, 1, 2),
+        "sparse_updown": span(evs, 2, 3),
     }
     kern_dense = {"dense_gateup": avg(evd, 0), "dense_down": avg(evd, 1)}
     for l in (evp, evs, evd):
@@ -675,8 +675,11 @@ def main():
             hev.destroy(e)
 
     NT = N // T
+    # per non-overflow row: its entries (two weight rows, index and value),
+    # x, the y row and the counts; per overflow row: the counts and the y row
+    # it finishes (the split partials it reads are not counted)
     sparse_bytes = (sparse_nnz * (4 * K + 8) + int((~ovf).sum()) * (2 * K + 4 * K + 4 * NT)
-                    + R * 4 * NT)
+                    + R * (4 * NT + 4 * K))
     work = {  # algorithmic work per launch: (amount, bound, unit)
         "gate_twell": (2.0 * M * K * N, "mfma"),
         "sparse_updown": (float(sparse_bytes), "hbm"),

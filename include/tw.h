@@ -46,11 +46,12 @@
  *   with one more entry than the call launches kernels, for per-kernel
  *   durations with hipEventElapsedTime.  tw_pack_gate (2 kernels) and
  *   tw_ffn_fwd (2 kernels) record events[0] on `stream` before the first
- *   kernel and events[i+1] after kernel i.  tw_sparse_ffn_fwd launches 4:
- *   events[0] is recorded before any of them, events[1] after the sparse
- *   up+down kernel, events[2..4] after the overflow rows' gate+up, down and
- *   split-sum kernels, which follow it on the same stream (with R_max == 0
- *   only the sparse kernel runs and events[1..4] are recorded together).
+ *   kernel and events[i+1] after kernel i.  tw_sparse_ffn_fwd takes 5
+ *   events for 3 kernels: events[0] before any of them, events[1] and [2]
+ *   after the overflow rows' gate+up and down GEMMs, events[3] after the
+ *   sparse up+down kernel (which also finishes the overflow rows' split
+ *   sums), events[4] together with events[3] (with R_max == 0 only the
+ *   sparse kernel runs and events[0..2] are recorded together).
  *
  * Weight layout (one layout serves every path): wg_t, wu_t and wd are all
  * [N][K] row-major bf16.  wg_t and wu_t hold W_g and W_u transposed, so the
@@ -174,8 +175,12 @@ tw_status tw_pack_dense(const float *z, int M, int N, int T, int C,
  *   ovf_rows, ovf_count     the routing written by tw_pack_gate (device)
  *   y        [M][K]         fp32 out
  *
- * The overflow rows' dense path follows the sparse kernel on `stream`; it
- * writes exactly the listed rows of y, which the sparse kernel leaves alone.
+ * On `stream`, the overflow rows' dense path runs first: gate+up, then the
+ * down GEMM, which for few rows splits its reduction over N into partial
+ * tiles in the workspace.  The sparse kernel follows; it computes the rows
+ * that fit and sums those partials (in split order, so the result does not
+ * depend on timing) into the listed rows.  The two sets of rows are
+ * disjoint.
  */
 tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
                             const uint16_t *wu_t, const uint16_t *wd,
