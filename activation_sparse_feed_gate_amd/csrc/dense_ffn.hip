@@ -777,9 +777,7 @@ hipError_t launch_down_pair(const uint16_t *h, const uint16_t *wd, const uint16_
     hipLaunchKernelGGL(DnRowsPair::kernel, dim3(kSplitGrid), dim3(DnRowsPair::NTH),
                        DnRowsPair::LDS, s, h, wd, K, N, rowlist, count, R_cap, y, partial, h2,
                        wd2);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // the split count follows the whole reduction: 2 N / kPK stages
-    return launch_split_reduce(partial, rowlist, count, R_cap, K, 2 * N, y, s);
+    return hipGetLastError();
 }
 
 hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,

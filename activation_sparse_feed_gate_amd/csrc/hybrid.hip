@@ -29,6 +29,7 @@
 // Backup rows go through the dense MFMA kernels of dense_ffn.hip.
 #include "tw_device.hpp"
 #include "tw_internal.hpp"
+#include "tw_split.hpp"
 
 namespace tw {
 namespace {
@@ -229,11 +230,27 @@ __global__ __launch_bounds__(kThreads) void hybrid_down_kernel(
     const uint16_t *__restrict__ wd, const uint16_t *__restrict__ w2, int K, int N, int P,
     const float *__restrict__ hy_h, const float *__restrict__ v2,
     const int32_t *__restrict__ hy_idx, const int32_t *__restrict__ hy_cnt,
-    const uint8_t *__restrict__ route, float *__restrict__ y) {
+    const uint8_t *__restrict__ route, float *__restrict__ y, const float *__restrict__ partial,
+    const int32_t *__restrict__ bk_rows, const int32_t *__restrict__ bk_count, int R_max,
+    int NR) {
     constexpr int kDnBatch = TWO ? 2 : 4;
     extern __shared__ __attribute__((aligned(16))) char smem[];  // y staging, fp32
     const int m = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (partial) {
+        // backup-list position m: the backup GEMM's split partial tiles
+        // (reduction depth NR), summed in split order into its row of y
+        const int rows = __builtin_amdgcn_readfirstlane(min(*bk_count, R_max));
+        if (m < rows) {
+            const int S = split_factor(rows, K, NR);
+            if (S > 1) {
+                const unsigned r = min((unsigned)bk_rows[m], gridDim.x - 1);
+                float *yo = y + (size_t)r * K;
+                for (int col = 4 * tid; col < K; col += 4 * kThreads)
+                    *reinterpret_cast<float4 *>(yo + col) = split_sum4<8>(partial, m, col, rows, K, S);
+            }
+        }
+    }
     if (route[m]) return;  // block-uniform: the backup path writes this row
     const int n = min(hy_cnt[m], P);
     const int KC = K >> 3;
@@ -541,14 +558,18 @@ hipError_t launch_up_k(const uint16_t *x, const uint16_t *wu_t, int M, int K, in
 template <int KCH, bool TWO>
 hipError_t launch_down_k(const uint16_t *wd, const uint16_t *w2, int M, int K, int N, int P,
                          const float *hy_h, const float *v2, const int32_t *hy_idx,
-                         const int32_t *hy_cnt, const uint8_t *route, float *y, hipStream_t s) {
+                         const int32_t *hy_cnt, const uint8_t *route, float *y,
+                         const float *partial, const int32_t *bk_rows, const int32_t *bk_count,
+                         int R_max, hipStream_t s) {
     const size_t lds = (size_t)kWaves * KCH * 512 * sizeof(float);
     {
         const hipError_t e = lds_limit_once<&hybrid_down_kernel<KCH, TWO>>((int)lds);
         if (e != hipSuccess) return e;
     }
+    // the backup GEMM's reduction: N deep, or 2 N for the two products of dx
     hipLaunchKernelGGL((hybrid_down_kernel<KCH, TWO>), dim3(M), dim3(kThreads), lds, s, wd, w2,
-                       K, N, P, hy_h, v2, hy_idx, hy_cnt, route, y);
+                       K, N, P, hy_h, v2, hy_idx, hy_cnt, route, y, partial, bk_rows, bk_count,
+                       R_max, TWO ? 2 * N : N);
     return hipGetLastError();
 }
 
@@ -607,10 +628,12 @@ hipError_t launch_hybrid_dh(const uint16_t *dy, const uint16_t *wd, int M, int K
 
 hipError_t launch_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const float *hy_h,
                               const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
-                              float *y, hipStream_t s) {
+                              float *y, const float *partial, const int32_t *bk_rows,
+                              const int32_t *bk_count, int R_max, hipStream_t s) {
     if (M == 0) return hipSuccess;
 #define TW_DN(k) \
-    launch_down_k<k, false>(wd, nullptr, M, K, N, P, hy_h, nullptr, hy_idx, hy_cnt, route, y, s)
+    launch_down_k<k, false>(wd, nullptr, M, K, N, P, hy_h, nullptr, hy_idx, hy_cnt, route, y, \
+                            partial, bk_rows, bk_count, R_max, s)
     TW_KCH_SWITCH(K, TW_DN)
 #undef TW_DN
 }
@@ -618,10 +641,12 @@ hipError_t launch_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, co
 hipError_t launch_hybrid_dx(const uint16_t *wu_t, const uint16_t *wg_t, int M, int K, int N,
                             int P, const float *hy_du, const float *hy_dz,
                             const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
-                            float *dx, hipStream_t s) {
+                            float *dx, const float *partial, const int32_t *bk_rows,
+                            const int32_t *bk_count, int R_max, hipStream_t s) {
     if (M == 0) return hipSuccess;
 #define TW_DX(k) \
-    launch_down_k<k, true>(wu_t, wg_t, M, K, N, P, hy_du, hy_dz, hy_idx, hy_cnt, route, dx, s)
+    launch_down_k<k, true>(wu_t, wg_t, M, K, N, P, hy_du, hy_dz, hy_idx, hy_cnt, route, dx, \
+                           partial, bk_rows, bk_count, R_max, s)
     TW_KCH_SWITCH(K, TW_DX)
 #undef TW_DX
 }

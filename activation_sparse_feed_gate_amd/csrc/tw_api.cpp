@@ -400,22 +400,19 @@ tw_status tw_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const f
     if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // the backup GEMM first (split partial tiles for few rows), then the
+    // sparse-row kernel, which also sums those partials into the backup rows
+    float *partial = R_max > 0 ? static_cast<float *>(ws) : nullptr;
     TW_TRY(record(events, 0, s));
-    TW_TRY(launched(tw::launch_hybrid_down(wd, M, K, N, P, hy_h, hy_idx, hy_cnt, route, y, s),
-                    "hybrid down launch"));
-    TW_TRY(record(events, 1, s));
-    if (R_max > 0) {
-        float *partial = static_cast<float *>(ws);
+    if (R_max > 0)
         TW_TRY(launched(tw::launch_down(bk_h, wd, K, N, bk_rows, bk_count, R_max, y, partial, s),
                         "backup down launch"));
-        TW_TRY(record(events, 2, s));
-        TW_TRY(launched(tw::launch_split_reduce(partial, bk_rows, bk_count, R_max, K, N, y, s),
-                        "backup split-reduce launch"));
-        TW_TRY(record(events, 3, s));
-    } else {
-        TW_TRY(record(events, 2, s));
-        TW_TRY(record(events, 3, s));
-    }
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_hybrid_down(wd, M, K, N, P, hy_h, hy_idx, hy_cnt, route, y, partial,
+                                           bk_rows, bk_count, R_max, s),
+                    "hybrid down launch"));
+    TW_TRY(record(events, 2, s));
+    TW_TRY(record(events, 3, s));
     return TW_OK;
 }
 
@@ -485,19 +482,19 @@ tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, in
     if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    // backup rows first: dx = du W_u^T + dz W_g^T as one split GEMM whose
+    // reduction runs over both products; the sparse-row kernel follows and
+    // sums its partial tiles (split order) into the backup rows
+    float *partial = R_max > 0 ? static_cast<float *>(ws) : nullptr;
     TW_TRY(record(events, 0, s));
-    TW_TRY(launched(tw::launch_hybrid_dx(wu_t, wg_t, M, K, N, P, hy_du, hy_dz, hy_idx, hy_cnt,
-                                         route, dx, s),
-                    "hybrid dx launch"));
-    TW_TRY(record(events, 1, s));
-    if (R_max > 0) {
-        // dx = du W_u^T + dz W_g^T: one split GEMM whose reduction runs over
-        // both products, summed in split order
-        float *partial = static_cast<float *>(ws);
+    if (R_max > 0)
         TW_TRY(launched(tw::launch_down_pair(bk_du, wu_t, bk_dz, wg_t, K, N, bk_rows, bk_count,
                                              R_max, dx, partial, s),
                         "backup dx launch"));
-    }
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_hybrid_dx(wu_t, wg_t, M, K, N, P, hy_du, hy_dz, hy_idx, hy_cnt,
+                                         route, dx, partial, bk_rows, bk_count, R_max, s),
+                    "hybrid dx launch"));
     TW_TRY(record(events, 2, s));
     return TW_OK;
 }

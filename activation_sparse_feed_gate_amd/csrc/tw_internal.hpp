@@ -97,8 +97,10 @@ hipError_t launch_split_reduce(const float *partial, const int32_t *rowlist,
                                const int32_t *count, int R_cap, int K, int N, float *y,
                                hipStream_t s);
 size_t split_partial_bytes();
-// y[row_r] = h[r] W_d + h2[r] W_d2 for r < rows (row list as above): one split
-// GEMM over both reductions, then its split sum (partial as for launch_down).
+// y[row_r] = h[r] W_d + h2[r] W_d2 for r < rows (row list as above): one
+// GEMM whose reduction runs over both products (2 N deep), split as
+// launch_down splits; launch_split_reduce with 2 N, or launch_hybrid_dx,
+// sums the partial tiles.
 hipError_t launch_down_pair(const uint16_t *h, const uint16_t *wd, const uint16_t *h2,
                             const uint16_t *wd2, int K, int N, const int32_t *rowlist,
                             const int32_t *count, int R_cap, float *y, float *partial,
@@ -113,9 +115,13 @@ hipError_t launch_route_compact(const uint8_t *route, int M, int R_max, int32_t 
 hipError_t launch_hybrid_up(const uint16_t *x, const uint16_t *wu_t, int M, int K, int N, int P,
                             const float *hy_g, const int32_t *hy_idx, const int32_t *hy_cnt,
                             const uint8_t *route, float *hy_u, float *hy_h, hipStream_t s);
+// With `partial` (the split partial tiles launch_down or launch_down_pair
+// left for the backup list bk_rows, bk_count, R_max), the kernel also sums
+// those into the listed rows, in place of launch_split_reduce.
 hipError_t launch_hybrid_down(const uint16_t *wd, int M, int K, int N, int P, const float *hy_h,
                               const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
-                              float *y, hipStream_t s);
+                              float *y, const float *partial, const int32_t *bk_rows,
+                              const int32_t *bk_count, int R_max, hipStream_t s);
 // Backward over hybrid storage: du, dz at the stored entries of sparse rows;
 // dx of sparse rows; the transpose and weight gradients (all rows).
 hipError_t launch_hybrid_dh(const uint16_t *dy, const uint16_t *wd, int M, int K, int N, int P,
@@ -125,7 +131,8 @@ hipError_t launch_hybrid_dh(const uint16_t *dy, const uint16_t *wd, int M, int K
 hipError_t launch_hybrid_dx(const uint16_t *wu_t, const uint16_t *wg_t, int M, int K, int N,
                             int P, const float *hy_du, const float *hy_dz,
                             const int32_t *hy_idx, const int32_t *hy_cnt, const uint8_t *route,
-                            float *dx, hipStream_t s);
+                            float *dx, const float *partial, const int32_t *bk_rows,
+                            const int32_t *bk_count, int R_max, hipStream_t s);
 size_t hybrid_dw_bytes(int M, int K, int N, int P, int R_max);
 hipError_t launch_hybrid_dw(const uint16_t *x, const uint16_t *dy, int M, int K, int N, int P,
                             const float *hy_h, const float *hy_du, const float *hy_dz,

@@ -221,7 +221,7 @@ def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, st
 
     kern = {"gate_twell": avg(0, 0), "ovf_compact": avg(0, 1), "hybrid_pack": avg(1, 0),
             "route_compact": avg(1, 1), "hybrid_up": avg(2, 0), "backup_gateup": avg(2, 1),
-            "hybrid_down": avg(3, 0), "backup_down": avg(3, 1), "backup_reduce": avg(3, 2)}
+            "backup_down": avg(3, 0), "hybrid_down": avg(3, 1)}
     for e in evl:
         for q in e:
             hev.destroy(q)
@@ -230,7 +230,9 @@ def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, st
     bytes_ = {
         "hybrid_pack": M * (4 * NT + 4 + 1) + nnz_sp * 16,
         "hybrid_up": nnz_sp * (2 * K + 4 + 4 + 8) + rows_sp_act * 2 * K + M * 5,
-        "hybrid_down": nnz_sp * (2 * K + 8) + rows_sp * 4 * K + M * 5,
+        # (+ the backup rows of y it finishes; the split partials it reads
+        # are not counted)
+        "hybrid_down": nnz_sp * (2 * K + 8) + rows_sp * 4 * K + M * 5 + bk_count * 4 * K,
     }
     roof = {k: {"bound": "hbm", "achieved": b / kern[k] / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": b / kern[k] / 1e9 / PEAK_HBM_GBS, "bytes": b,
@@ -355,8 +357,8 @@ def hybrid_backward_bench(args, tw, torch, w, x, wg, wu, wdn, hy, Rh, P, hev):
     def avg(j, i):
         return sum(hev.ms(e[j][i], e[j][i + 1]) for e in evl) / len(evl) * 1e-3
 
-    kern = {"hybrid_dh": avg(0, 0), "backup_dh": avg(0, 1), "hybrid_dx": avg(1, 0),
-            "backup_dx": avg(1, 1), "transpose": avg(2, 0), "weight_grads": avg(2, 1),
+    kern = {"hybrid_dh": avg(0, 0), "backup_dh": avg(0, 1), "backup_dx": avg(1, 0),
+            "hybrid_dx": avg(1, 1), "transpose": avg(2, 0), "weight_grads": avg(2, 1),
             "backup_weight_grads": avg(2, 2)}
     for e in evl:
         for q in e:

@@ -285,8 +285,10 @@ tw_status tw_hybrid_up(const uint16_t *x, const uint16_t *wg_t, const uint16_t *
  * row bk_rows[r] of y gets bk_h[r] W_d on the matrix cores.  The workspace
  * holds the backup GEMM's partial tiles: ws_bytes >=
  * tw_hybrid_down_workspace_bytes(R_max) (ws may be NULL when that is 0).
- * events: [0] before, [1] after the sparse-row kernel, [2], [3] after the
- * backup GEMM and the sum of its partial tiles.
+ * The backup GEMM runs first; the sparse-row kernel follows and also sums
+ * the GEMM's partial tiles into the backup rows (in split order).
+ * events: [0] before, [1] after the backup GEMM, [2] and [3] after the
+ * sparse-row kernel.
  */
 size_t tw_hybrid_down_workspace_bytes(int R_max);
 tw_status tw_hybrid_down(const uint16_t *wd, int M, int K, int N, int P,
@@ -327,10 +329,12 @@ tw_status tw_hybrid_bwd_dh(const uint16_t *dy, const uint16_t *wd, int M, int K,
 
 /*
  * tw_hybrid_bwd_dx (hybrid-to-dense): dx [M][K] fp32 for sparse rows and the
- * listed backup rows (the latter on the matrix cores: dx = du W_u^T, then
- * dx += dz W_g^T).  ws_bytes >= tw_hybrid_bwd_dx_workspace_bytes(R_max) (ws
- * may be NULL when that is 0).  events: [0] before, [1] after the sparse-row
- * kernel, [2] after the backup rows' kernels.
+ * listed backup rows (the latter on the matrix cores: one GEMM whose
+ * reduction runs over both products, du W_u^T then dz W_g^T, split into
+ * partial tiles that the sparse-row kernel, which runs after it, sums in
+ * split order).  ws_bytes >= tw_hybrid_bwd_dx_workspace_bytes(R_max) (ws
+ * may be NULL when that is 0).  events: [0] before, [1] after the backup
+ * GEMM, [2] after the sparse-row kernel.
  */
 size_t tw_hybrid_bwd_dx_workspace_bytes(int R_max);
 tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, int K, int N, int P,
