@@ -23,7 +23,8 @@
 // - Batches of at most 256 rows cannot fill the chip with 4 waves per row,
 //   and the heaviest row's serial chain of gathers sets the kernel time, so
 //   such rows are spread over 16 waves (8 when K > 2048) that take one
-//   entry at a time.
+//   entry at a time; 32 to 128 rows, over G = 256 / M workgroups, each
+//   writing a partial row that row_sum_kernel adds up in a fixed order.
 // - The dot product is reduced across the wave with DPP (no LDS), its
 //   product with g is the scalar h_j, and h_j * W_d[j] is added lane-wise.
 // - The four partial y rows are summed in LDS in a fixed order (the result
@@ -54,29 +55,33 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const float *__restrict__ tw_val,
     const int32_t *__restrict__ tw_idx, const int32_t *__restrict__ tw_cnt,
     float *__restrict__ y, const float *__restrict__ partial,
-    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ ovf_count, int R_max) {
+    const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ ovf_count, int R_max,
+    int G, float *__restrict__ rowpart) {
     constexpr int kThreads = NWV * 64, kWaves = NWV;
     constexpr int kBatch = NWV >= 8 ? 1 : 2;  // active neurons gathered together per wave
     extern __shared__ __attribute__((aligned(16))) char smem[];  // y staging, fp32
     __shared__ int s_off[kThreads + 1];
     __shared__ int s_wtot[kWaves];
 
-    const int m = blockIdx.x;
+    // G workgroups per row (G = 1: one); part gs of row m
+    const int M = gridDim.x / G;
+    const int m = blockIdx.x / G, gs = blockIdx.x % G;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
 
     const int c = tid < NT ? tw_cnt[(size_t)m * NT + tid] : 0;
     if (partial) {
-        // overflow-list position m: its split partial tiles, summed in split
+        // overflow-list position p: its split partial tiles, summed in split
         // order into its row of y (S = 1: the down GEMM stored the row)
+        const int p = blockIdx.x;
         const int rows = __builtin_amdgcn_readfirstlane(min(*ovf_count, R_max));
-        if (m < rows) {
+        if (p < rows) {
             const int S = split_factor(rows, K, N);
             if (S > 1) {
-                const unsigned row = min((unsigned)ovf_rows[m], gridDim.x - 1);
+                const unsigned row = min((unsigned)ovf_rows[p], (unsigned)(M - 1));
                 float *yo = y + (size_t)row * K;
                 for (int col = 4 * tid; col < K; col += 4 * kThreads)
-                    *reinterpret_cast<float4 *>(yo + col) = split_sum4<8>(partial, m, col, rows, K, S);
+                    *reinterpret_cast<float4 *>(yo + col) = split_sum4<8>(partial, p, col, rows, K, S);
             }
         }
     }
@@ -101,7 +106,8 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const int nnz = s_off[kThreads];
 
     const int KC = K >> 3;  // 16-byte chunks per K-row
-    float *yrow = y + (size_t)m * K;
+    // this workgroup's output: the row of y, or its partial row
+    float *yrow = G > 1 ? rowpart + ((size_t)gs * M + m) * K : y + (size_t)m * K;
     if (nnz == 0) {
         for (int q = tid; q < 2 * KC; q += kThreads)
             st16(yrow + 4 * q, u32x4{0u, 0u, 0u, 0u});
@@ -120,14 +126,16 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) yacc[ch][e] = 0.0f;
 
-    // entries of this wave: f = wave + 4 * e, e < ne
-    const int ne = (nnz - wave + kWaves - 1) / kWaves;
+    // entries of this wave: f = gw + GW e, e < ne (gw: the wave's index
+    // among the GW = G NWV waves of the row)
+    const int gw = gs * kWaves + wave, GW = G * kWaves;
+    const int ne = (nnz - gw + GW - 1) / GW;
     for (int e0 = 0; e0 < ne; e0 += 64) {
         // lane resolves entry e0 + lane: tile by binary search over s_off
         int jl = 0;
         float gl = 0.0f;
         if (e0 + lane < ne) {
-            const int f = wave + kWaves * (e0 + lane);
+            const int f = gw + GW * (e0 + lane);
             int lo = 0, hi = NT;
             while (hi - lo > 1) {
                 const int mid = (lo + hi) >> 1;
@@ -222,20 +230,46 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     }
 }
 
+// y[m] = sum over parts g = 0 .. G-1 (in that order) of the partial rows
+// the split sparse kernel wrote, for every row with no tile over capacity
+// (the overflow rows hold the dense path's result).
+__global__ __launch_bounds__(256) void row_sum_kernel(const float *__restrict__ rowpart, int G,
+                                                      int K, int NT, int C,
+                                                      const int32_t *__restrict__ tw_cnt,
+                                                      float *__restrict__ y) {
+    const int m = blockIdx.x, M = gridDim.x, tid = threadIdx.x;
+    const int c = tid < NT ? tw_cnt[(size_t)m * NT + tid] : 0;
+    if (__syncthreads_or(c > C)) return;
+    for (int col = 4 * tid; col < K; col += 4 * 256) {
+        float4 v = *reinterpret_cast<const float4 *>(rowpart + (size_t)m * K + col);
+        for (int g = 1; g < G; ++g) {
+            const float4 u = *reinterpret_cast<const float4 *>(rowpart + ((size_t)g * M + m) * K + col);
+            v.x += u.x;
+            v.y += u.y;
+            v.z += u.z;
+            v.w += u.w;
+        }
+        *reinterpret_cast<float4 *>(y + (size_t)m * K + col) = v;
+    }
+}
+
 template <int KCH, int NWV>
 hipError_t launch_kw(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd, int M, int K,
                      int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
                      const int32_t *tw_cnt, float *y, const float *partial,
-                     const int32_t *ovf_rows, const int32_t *ovf_count, int R_max,
-                     hipStream_t s) {
+                     const int32_t *ovf_rows, const int32_t *ovf_count, int R_max, int G,
+                     float *rowpart, hipStream_t s) {
     const size_t lds = (size_t)NWV * KCH * 512 * sizeof(float);  // y staging
     {
         const hipError_t e = lds_limit_once<&sparse_updown_kernel<KCH, NWV>>((int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((sparse_updown_kernel<KCH, NWV>), dim3(M), dim3(NWV * 64), lds, s, x,
+    hipLaunchKernelGGL((sparse_updown_kernel<KCH, NWV>), dim3(M * G), dim3(NWV * 64), lds, s, x,
                        wu_t, wd, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial, ovf_rows,
-                       ovf_count, R_max);
+                       ovf_count, R_max, G, rowpart);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || G == 1) return e;
+    hipLaunchKernelGGL(row_sum_kernel, dim3(M), dim3(256), 0, s, rowpart, G, K, NT, C, tw_cnt, y);
     return hipGetLastError();
 }
 
@@ -246,15 +280,16 @@ hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
                     int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
                     const int32_t *tw_cnt, float *y, const float *partial,
                     const int32_t *ovf_rows, const int32_t *ovf_count, int R_max,
-                    hipStream_t s) {
+                    float *rowpart, hipStream_t s) {
     // 16 waves cap a lane at 128 registers and the y staging at 16 KCH KB:
     // wide rows take 8
     constexpr int kSmallWaves = KCH <= 4 ? 16 : 8;
     if (M <= kSmallBatchRows)
         return launch_kw<KCH, kSmallWaves>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt,
-                                           y, partial, ovf_rows, ovf_count, R_max, s);
+                                           y, partial, ovf_rows, ovf_count, R_max,
+                                           sparse_row_parts(M), rowpart, s);
     return launch_kw<KCH, 4>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial,
-                             ovf_rows, ovf_count, R_max, s);
+                             ovf_rows, ovf_count, R_max, 1, rowpart, s);
 }
 
 }  // namespace
@@ -263,11 +298,12 @@ hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const u
                                 int M, int K, int N, int T, int C, const float *tw_val,
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
                                 const float *partial, const int32_t *ovf_rows,
-                                const int32_t *ovf_count, int R_max, hipStream_t s) {
+                                const int32_t *ovf_count, int R_max, float *rowpart,
+                                hipStream_t s) {
     if (M == 0) return hipSuccess;
     const int NT = N / T;
 #define TW_SPARSE_ARGS x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial, ovf_rows, \
-                       ovf_count, R_max, s
+                       ovf_count, R_max, rowpart, s
     switch ((K + 511) / 512) {
     case 1: return launch_k<1>(TW_SPARSE_ARGS);
     case 2: return launch_k<2>(TW_SPARSE_ARGS);

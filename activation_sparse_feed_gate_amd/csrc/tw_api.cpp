@@ -66,10 +66,14 @@ tw_status check_hybrid(int M, int K, int N, int T, int C, int P, int R_max) {
 size_t pack_ws(int M, int N) {
     return round_up((size_t)((N + 127) / 128) * tw::row_words(M) * 4, 256);
 }
-// overflow path: h rows [R_max][N] bf16, then the split partial tiles
-size_t sparse_ws(int R_max, int N) {
+// overflow path: h rows [R_max][N] bf16, then the split partial tiles;
+// then the sparse kernel's partial rows (small batches)
+size_t overflow_ws(int R_max, int N) {
     if (R_max == 0) return 0;
     return round_up((size_t)R_max * N * 2, 256) + tw::split_partial_bytes();
+}
+size_t sparse_ws(int M, int K, int R_max, int N) {
+    return overflow_ws(R_max, N) + round_up(tw::sparse_rowpart_bytes(M, K), 256);
 }
 
 tw_status record(void *const *events, int i, hipStream_t s) {
@@ -124,7 +128,7 @@ size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max) {
     const tw_status st = check_shape(M, K, N, T, C, R_max);
     std::snprintf(g_err, sizeof g_err, "%s", saved);
     if (st != TW_OK) return 0;
-    size_t a = pack_ws(M, N), b = sparse_ws(R_max, N);
+    size_t a = pack_ws(M, N), b = sparse_ws(M, K, R_max, N);
     return (a > b ? a : b) + 256;
 }
 
@@ -244,6 +248,7 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     char *w = static_cast<char *>(ws);
     uint16_t *h = reinterpret_cast<uint16_t *>(w);
     float *partial = reinterpret_cast<float *>(w + round_up((size_t)R_max * N * 2, 256));
+    float *rowpart = reinterpret_cast<float *>(w + overflow_ws(R_max, N));
     // All on the caller's stream: the overflow rows' dense path first (its
     // down GEMM leaves split partial tiles when the rows are few), then the
     // sparse kernel, which computes the other rows and sums those partials
@@ -264,7 +269,7 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     }
     TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx, tw_cnt,
                                              y, R_max > 0 ? partial : nullptr, ovf_rows,
-                                             ovf_count, R_max, s),
+                                             ovf_count, R_max, rowpart, s),
                     "sparse_updown launch"));
     TW_TRY(record(events, 3, s));
     TW_TRY(record(events, 4, s));

@@ -42,15 +42,31 @@ hipError_t launch_pack_dense(const float *z, int M, int N, int T, int C, float *
 hipError_t launch_ovf_compact(const uint32_t *oflag, int NB, int MW, int R_max,
                               int32_t *ovf_rows, int32_t *ovf_count, hipStream_t s);
 
+// Workgroups per row of the sparse kernel: batches of 32 to 128 rows are
+// spread over G = 256 / M per row, which write partial rows
+// (sparse_rowpart_bytes of them) that a second kernel sums; else 1.
+// Measured: below 32 rows the second kernel costs more than the split
+// gains, and 512 / M parts were slower at the 0.5B block shape.
+inline int sparse_row_parts(int M) {
+    if (M < 32 || M > 128) return 1;
+    return 256 / M;
+}
+inline size_t sparse_rowpart_bytes(int M, int K) {
+    const int g = sparse_row_parts(M);
+    return g > 1 ? (size_t)g * M * K * 4 : 0;
+}
+
 // Sparse up + down of every non-overflow row into y.  With `partial` (the
 // split partial tiles launch_down left for the overflow list ovf_rows,
 // ovf_count, R_max), it also sums those into the listed rows of y, in place
 // of launch_split_reduce; partial null: overflow rows are left alone.
+// rowpart: sparse_rowpart_bytes(M, K) bytes (unused when that is 0).
 hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
                                 int M, int K, int N, int T, int C, const float *tw_val,
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
                                 const float *partial, const int32_t *ovf_rows,
-                                const int32_t *ovf_count, int R_max, hipStream_t s);
+                                const int32_t *ovf_count, int R_max, float *rowpart,
+                                hipStream_t s);
 
 // Row-list gate+up GEMMs with a capacity of at most this many rows take
 // 64 x 64 tiles.  The row count itself is known only on the device; with the

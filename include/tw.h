@@ -50,8 +50,9 @@
  *   events for 3 kernels: events[0] before any of them, events[1] and [2]
  *   after the overflow rows' gate+up and down GEMMs, events[3] after the
  *   sparse up+down kernel (which also finishes the overflow rows' split
- *   sums), events[4] together with events[3] (with R_max == 0 only the
- *   sparse kernel runs and events[0..2] are recorded together).
+ *   sums; for batches of 32 to 128 rows it is followed by the sum of its
+ *   partial rows), events[4] together with events[3] (with R_max == 0 only
+ *   the sparse kernel runs and events[0..2] are recorded together).
  *
  * Weight layout (one layout serves every path): wg_t, wu_t and wd are all
  * [N][K] row-major bf16.  wg_t and wu_t hold W_g and W_u transposed, so the
@@ -180,7 +181,9 @@ tw_status tw_pack_dense(const float *z, int M, int N, int T, int C,
  * tiles in the workspace.  The sparse kernel follows; it computes the rows
  * that fit and sums those partials (in split order, so the result does not
  * depend on timing) into the listed rows.  The two sets of rows are
- * disjoint.
+ * disjoint.  Batches of 32 to 128 rows spread each row over several
+ * workgroups, whose partial rows (in the workspace) a last small kernel
+ * sums in a fixed order.
  */
 tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
                             const uint16_t *wu_t, const uint16_t *wd,

@@ -64,6 +64,11 @@ def _full_check(tw, w, R_max=None, dense=True):
     # small-batch one): a half-empty last column block, and T = 256
     dict(M=4096, K=256, N=1152, T=128, C=8, density=0.02, sigma_s=0.5),
     dict(M=2048, K=256, N=2048, T=256, C=12, density=0.01, sigma_s=0.7, seed=5),
+    # batches of 32 to 128 rows: each row over 256 / M workgroups whose
+    # partial rows a second kernel sums (2B and 0.5B block shapes)
+    dict(M=32, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5),
+    dict(M=100, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=2),
+    dict(M=128, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=4),
 ])
 def test_tiny_all_rows(tw, kw):
     _full_check(tw, W["tiny"].with_(**kw))
@@ -110,8 +115,10 @@ def test_empty_batch(tw):
     assert int(p["ovf_count"].cpu()[0]) == 0 and y.numel() == 0
 
 
-def test_deterministic(tw):
-    w = W["tiny"].with_(M=512, C=6, sigma_s=0.5, density=0.03)
+@pytest.mark.parametrize("M", [512, 48])  # one workgroup per row; several per row
+def test_deterministic(tw, M):
+    w = W["tiny"].with_(M=M, C=6, sigma_s=0.5, density=0.03)
+    print(f"case {w}", flush=True)
     d = synth.make_inputs(w)
     dev = parity.upload(d)
     a = parity.run_path(tw, dev, w.T, w.C, w.M)
