@@ -751,7 +751,13 @@ def main():
         "stages": stages,
         "realized": {"density": float(nnz.sum()) / (M * N), "overflow_rows": R,
                      "nnz_per_sparse_row": sparse_nnz / max(1, int((~ovf).sum())),
-                     "max_nnz_sparse_row": int(nnz[~ovf].max(initial=0))},
+                     "max_nnz_sparse_row": int(nnz[~ovf].max(initial=0)),
+                     # active neurons per token over all rows (the true counts,
+                     # overflow rows included): the tail the capacities face
+                     "nnz_per_row_mean_p50_p95_p99_max": [
+                         float(nnz.mean()) if M else 0.0,
+                         *[float(np.percentile(nnz, q)) if M else 0.0 for q in (50, 95, 99)],
+                         int(nnz.max(initial=0))]},
         "device": torch.cuda.get_device_properties(0).name,
     }
     if not args.no_cpu_baseline:
