@@ -235,33 +235,49 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
 // wave (lane l holds T / 64 consecutive columns; a wave-wide scan of the
 // lanes' counts gives the slots in ascending column order).  The row
 // overflow bits go to oflag[tile][row word]: N / T column blocks.
+// While such workgroups number fewer than the CUs, each holds KS = 2 groups
+// of 4 waves that take the two halves of the reduction, each through its
+// own ring: the serial k-loop of a workgroup is half as long.  The second group adds its accumulators into
+// the first's staged tile before the packing, which all 8 waves share.
 constexpr int kSmallBM = 64;
-constexpr int kSmallThreads = 256;
 
-template <int T>
+// Whether the small-batch kernel splits the reduction in two: while its
+// workgroups (64-row blocks x 128-column tiles, counted at T = 128 for every
+// T so that the packing and the dense gate sum in the same order) number
+// fewer than the CUs.
+inline bool gate_small_split(int M, int N) {
+    return (long long)((M + kSmallBM - 1) / kSmallBM) * (N / 128) < 256;
+}
+
+template <int T, int KS>
 struct SmallGate {
-    static constexpr int NW = 4, WC = T / NW;          // columns per wave
+    static constexpr int NW = 4, WC = T / NW;          // waves per group, columns per wave
+    static constexpr int NTH = KS * NW * 64;            // threads
     static constexpr int FB = WC / 32;                  // 32-column blocks per wave
     static constexpr int SR = kSmallBM + T;             // stage rows: x, then W_g
     static constexpr int NI = SR / (16 * NW);           // direct loads per wave and stage
     static constexpr int STAGE = SR * kPRow;
-    static constexpr int RING = kStages * STAGE;
+    static constexpr int ST = kStages;                  // ring stages per group
+    static constexpr int RING = ST * STAGE;             // one group's ring
     static constexpr int PITCH = T + 4;                 // staged row, floats
-    static constexpr int EPI = kSmallBM * PITCH * 4;
-    static constexpr int LDS = (RING > EPI ? RING : EPI) + 16;
+    static constexpr int EPI = kSmallBM * PITCH * 4;    // staged tile, then 2 flag words
+    static constexpr int LDS = KS * RING > EPI + 16 ? KS * RING : EPI + 16;
     static_assert(SR % (16 * NW) == 0 && kSmallBM % (16 * NW) == 0, "load slots");
+    static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(NTH == 256 * KS, "launch bounds of gate_small_kernel");
 };
 
-template <int T>
-__global__ __launch_bounds__(kSmallThreads) void gate_small_kernel(
+template <int T, int KS>
+__global__ __launch_bounds__(256 * KS) void gate_small_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t, int M, int K, int N,
     int C, int NRB, float *__restrict__ tw_val, int32_t *__restrict__ tw_idx,
     int32_t *__restrict__ tw_cnt, uint32_t *__restrict__ oflag, float *__restrict__ zdbg) {
-    using P = SmallGate<T>;
+    using P = SmallGate<T, KS>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
-    uint32_t *s_flag = reinterpret_cast<uint32_t *>(smem + P::LDS - 16);
+    uint32_t *s_flag = reinterpret_cast<uint32_t *>(smem + P::EPI);  // after the k-loop only
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave_all / P::NW, wave = wave_all % P::NW;  // K half, wave in the group
     const int rb = blockIdx.x % NRB, tc = blockIdx.x / NRB;  // row block, tile
     const int m0 = rb * kSmallBM, n0 = tc * T;
     const int NT = N / T;
@@ -307,29 +323,55 @@ __global__ __launch_bounds__(kSmallThreads) void gate_small_kernel(
             for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
     };
     settle_scalars(tw_val, tw_idx, tw_cnt, oflag, zdbg);
-    kloop_pipelined<kStages, P::NI>(0, K / kPK, smem, P::STAGE, issue, load, mma);
-    __syncthreads();  // the ring becomes the tile staging
+    // group g reduces stages [g KT / KS, (g + 1) KT / KS) through its own
+    // ring; both groups run the same number of stages, so the ring's
+    // workgroup-wide barriers pair up
+    const int kth = K / kPK / KS;
+    kloop_pipelined<P::ST, P::NI>(grp * kth, (grp + 1) * kth, smem + grp * P::RING, P::STAGE,
+                                  issue, load, mma);
+    __syncthreads();  // the rings become the tile staging
 
     float *zs = reinterpret_cast<float *>(smem);
+    auto zo = [&](int a, int b, int i) {
+        return (a * 32 + mfma32_row(i, lane)) * P::PITCH + wave * P::WC + b * 32 + (lane & 31);
+    };
+    if (grp == 0) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < P::FB; ++b)
+            for (int b = 0; b < P::FB; ++b)
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                zs[(a * 32 + mfma32_row(i, lane)) * P::PITCH + wave * P::WC + b * 32 + (lane & 31)] =
-                    acc[a][b][i];
+                for (int i = 0; i < 16; ++i) zs[zo(a, b, i)] = acc[a][b][i];
+    }
     if (tid < 2) s_flag[tid] = 0u;
     __syncthreads();
+    if constexpr (KS == 2) {
+        // z = (first half) + (second half), added by the lane that holds
+        // the same element in the second group
+        if (grp == 1) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) zs[zo(a, b, i)] += acc[a][b][i];
+        }
+        __syncthreads();
+    }
 
     constexpr int CPL = T / 64;  // columns per lane
     uint64_t over = 0;           // bit r: row r of the block overflows (wave-uniform)
-    for (int r = wave; r < kSmallBM; r += P::NW) {
+    for (int r = wave_all; r < kSmallBM; r += KS * P::NW) {
         const int m = m0 + r;
         if (m >= M) break;  // wave-uniform
         float v[CPL];
 #pragma unroll
         for (int k = 0; k < CPL; ++k) v[k] = zs[r * P::PITCH + lane * CPL + k];
+        if (zdbg) {
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) zdbg[(size_t)m * N + n0 + lane * CPL + k] = v[k];
+        }
+        if (!tw_cnt) continue;  // the dense gate only (the unfused path's first half)
         uint32_t bits = 0;
 #pragma unroll
         for (int k = 0; k < CPL; ++k) bits |= (v[k] > 0.0f ? 1u : 0u) << k;
@@ -353,10 +395,6 @@ __global__ __launch_bounds__(kSmallThreads) void gate_small_kernel(
                 ++slot;
             }
         if (lane == 0) tw_cnt[(size_t)m * NT + tc] = total;
-        if (zdbg) {
-#pragma unroll
-            for (int k = 0; k < CPL; ++k) zdbg[(size_t)m * N + n0 + lane * CPL + k] = v[k];
-        }
         if (total > C) over |= 1ull << r;
     }
     if (lane == 0 && over) {
@@ -365,20 +403,21 @@ __global__ __launch_bounds__(kSmallThreads) void gate_small_kernel(
     }
     __syncthreads();
     const int MW = (M + 31) >> 5;
-    if (tid < 2 && m0 + 32 * tid < M) oflag[(size_t)tc * MW + (m0 >> 5) + tid] = s_flag[tid];
+    if (oflag && tid < 2 && m0 + 32 * tid < M)
+        oflag[(size_t)tc * MW + (m0 >> 5) + tid] = s_flag[tid];
 }
 
-template <int T>
-hipError_t launch_gate_small(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int C,
-                             float *tw_val, int32_t *tw_idx, int32_t *tw_cnt, uint32_t *oflag,
-                             float *z_debug, hipStream_t s) {
-    using P = SmallGate<T>;
+template <int T, int KS>
+hipError_t launch_gate_small_k(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
+                               int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                               uint32_t *oflag, float *z_debug, hipStream_t s) {
+    using P = SmallGate<T, KS>;
     {
-        const hipError_t e = lds_limit_once<&gate_small_kernel<T>>(P::LDS);
+        const hipError_t e = lds_limit_once<&gate_small_kernel<T, KS>>(P::LDS);
         if (e != hipSuccess) return e;
     }
     const int NRB = (M + kSmallBM - 1) / kSmallBM;
-    hipLaunchKernelGGL(gate_small_kernel<T>, dim3(NRB * (N / T)), dim3(kSmallThreads), P::LDS, s,
+    hipLaunchKernelGGL((gate_small_kernel<T, KS>), dim3(NRB * (N / T)), dim3(P::NTH), P::LDS, s,
                        x, wg_t, M, K, N, C, NRB, tw_val, tw_idx, tw_cnt, oflag, z_debug);
     return hipGetLastError();
 }
@@ -473,11 +512,12 @@ hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int
                              uint32_t *oflag, float *z_debug, hipStream_t s) {
     if (M == 0) return hipSuccess;
     if (gate_small(M, N)) {
-        if (T == 128)
-            return launch_gate_small<128>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
-                                          z_debug, s);
-        return launch_gate_small<256>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug,
-                                      s);
+        const bool split = gate_small_split(M, N);
+#define TW_SMALL(t, ks) \
+    launch_gate_small_k<t, ks>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug, s)
+        if (T == 128) return split ? TW_SMALL(128, 2) : TW_SMALL(128, 1);
+        return split ? TW_SMALL(256, 2) : TW_SMALL(256, 1);
+#undef TW_SMALL
     }
     if (T == 128)
         return launch_gate_t<128, true>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
@@ -489,6 +529,14 @@ hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int
 hipError_t launch_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
                              float *z, hipStream_t s) {
     if (M == 0) return hipSuccess;
+    // the kernel tw_pack_gate would take, so that z is the same to the bit
+    // (the small-batch kernel's two K halves sum in another order)
+    if (gate_small(M, N))
+        return gate_small_split(M, N)
+                   ? launch_gate_small_k<128, 2>(x, wg_t, M, K, N, 1, nullptr, nullptr, nullptr,
+                                                 nullptr, z, s)
+                   : launch_gate_small_k<128, 1>(x, wg_t, M, K, N, 1, nullptr, nullptr, nullptr,
+                                                 nullptr, z, s);
     return launch_gate_t<128, false>(x, wg_t, M, K, N, 1, nullptr, nullptr, nullptr, nullptr, z,
                                      s);
 }
