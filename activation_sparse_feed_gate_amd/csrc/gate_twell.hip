@@ -235,18 +235,41 @@ __global__ __launch_bounds__(kThreads) void gate_twell_kernel(
 // wave (lane l holds T / 64 consecutive columns; a wave-wide scan of the
 // lanes' counts gives the slots in ascending column order).  The row
 // overflow bits go to oflag[tile][row word]: N / T column blocks.
-// While such workgroups number fewer than the CUs, each holds KS = 2 groups
-// of 4 waves that take the two halves of the reduction, each through its
-// own ring: the serial k-loop of a workgroup is half as long.  The second group adds its accumulators into
-// the first's staged tile before the packing, which all 8 waves share.
+// Such workgroups number NRB N / T (NRB 64-row blocks); each streams its
+// slice of W_g through one CU.  By how many there are (counted at T = 128
+// for every T, so that the fused gate and the unfused dense gate take the
+// same route and sum z in the same order):
+// - under 128, and few rows (the partial gates small next to W_g): the
+//   reduction is split over S workgroups (S = 2, 4 or 8 K-slices) that write
+//   fp32 partial tiles to the workspace, and a second kernel sums them in
+//   slice order and packs (the whole chip streams W_g);
+// - under 256: each workgroup holds KS = 2 groups of 4 waves that take the
+//   two halves of the reduction through their own rings and add in LDS;
+// - else one group, the whole reduction.
 constexpr int kSmallBM = 64;
 
-// Whether the small-batch kernel splits the reduction in two: while its
-// workgroups (64-row blocks x 128-column tiles, counted at T = 128 for every
-// T so that the packing and the dense gate sum in the same order) number
-// fewer than the CUs.
-inline bool gate_small_split(int M, int N) {
-    return (long long)((M + kSmallBM - 1) / kSmallBM) * (N / 128) < 256;
+// Workgroups of the small-batch gate, counted at T = 128.
+inline long long gate_small_wg(int M, int N) {
+    return (long long)((M + kSmallBM - 1) / kSmallBM) * (N / 128);
+}
+// K-slices of the split reduction (1: none): enough for 256 to 512
+// workgroups, at most 8, dividing the K / 32 stages; taken only while the
+// partial gates (S M N fp32, written and read back) stay within an eighth of
+// W_g's bytes (S M 16 <= K).  Measured: at M = 1 and 16 of the 2B block the
+// gate took 10.8 and 16.5 us split against 21.5 and 23.9 whole; past that
+// bound (M = 16 and 64 at the 0.5B block, 64 at the 2B) the partials cost more.
+inline int gate_small_parts(int M, int N, int K) {
+    if (!gate_small(M, N)) return 1;
+    const long long wg = gate_small_wg(M, N);
+    if (wg >= 128) return 1;
+    int S = 8;
+    while (S > 2 && (wg * S > 256 * 2 || (K / kPK) % S)) S >>= 1;
+    if ((K / kPK) % S || (long long)S * M * 16 > K) return 1;
+    return S;
+}
+// Whether the workgroups of the unsplit small-batch gate take two K halves.
+inline bool gate_small_split(int M, int N, int K) {
+    return gate_small_parts(M, N, K) == 1 && gate_small_wg(M, N) < 256;
 }
 
 template <int T, int KS>
@@ -267,106 +290,28 @@ struct SmallGate {
     static_assert(NTH == 256 * KS, "launch bounds of gate_small_kernel");
 };
 
-template <int T, int KS>
-__global__ __launch_bounds__(256 * KS) void gate_small_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t, int M, int K, int N,
-    int C, int NRB, float *__restrict__ tw_val, int32_t *__restrict__ tw_idx,
-    int32_t *__restrict__ tw_cnt, uint32_t *__restrict__ oflag, float *__restrict__ zdbg) {
-    using P = SmallGate<T, KS>;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
-    uint32_t *s_flag = reinterpret_cast<uint32_t *>(smem + P::EPI);  // after the k-loop only
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = wave_all / P::NW, wave = wave_all % P::NW;  // K half, wave in the group
-    const int rb = blockIdx.x % NRB, tc = blockIdx.x / NRB;  // row block, tile
-    const int m0 = rb * kSmallBM, n0 = tc * T;
-    const int NT = N / T;
-
-    // load slot j of a wave: stage rows [16 (4 j + wave), +16); slot 0 is x
-    const rsrc_t ra = make_rsrc(x + (size_t)m0 * K, (uint64_t)(M - m0) * K * 2);
-    const rsrc_t rw = make_rsrc(wg_t + (size_t)n0 * K, (uint64_t)T * K * 2);
-    uint32_t voff[P::NI];
-#pragma unroll
-    for (int j = 0; j < P::NI; ++j) {
-        const int row0 = (j * P::NW + wave) * 16;
-        const int sr = row0 + (lane >> 2);
-        const uint32_t row_off = j == 0 ? (uint32_t)(min(m0 + sr, M - 1) - m0) * K * 2
-                                        : (uint32_t)(sr - kSmallBM) * K * 2;
-        voff[j] = rows16_voff(row_off, lane, row0);
-    }
-    auto issue = [&](int kt, char *st) {
-        const uint32_t soff = kt * kPK * 2;
-#pragma unroll
-        for (int j = 0; j < P::NI; ++j) {
-            const int row0 = (j * P::NW + wave) * 16;
-            if (j == 0) dma16(ra, voff[j], soff, st + row0 * kPRow);
-            else dma16(rw, voff[j], soff, st + row0 * kPRow);
-        }
-    };
-    f32x16 acc[2][P::FB];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < P::FB; ++b) acc[a][b] = f32x16{};
-    u32x4 fa[2][2], fb[2][P::FB];
-    auto load = [&](const char *st, int s, int buf) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a) fa[buf][a] = frag(st, a * 32, s, lane);
-#pragma unroll
-        for (int b = 0; b < P::FB; ++b)
-            fb[buf][b] = frag(st, kSmallBM + wave * P::WC + b * 32, s, lane);
-    };
-    auto mma = [&](int buf) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
-    };
-    settle_scalars(tw_val, tw_idx, tw_cnt, oflag, zdbg);
-    // group g reduces stages [g KT / KS, (g + 1) KT / KS) through its own
-    // ring; both groups run the same number of stages, so the ring's
-    // workgroup-wide barriers pair up
-    const int kth = K / kPK / KS;
-    kloop_pipelined<P::ST, P::NI>(grp * kth, (grp + 1) * kth, smem + grp * P::RING, P::STAGE,
-                                  issue, load, mma);
-    __syncthreads();  // the rings become the tile staging
-
-    float *zs = reinterpret_cast<float *>(smem);
-    auto zo = [&](int a, int b, int i) {
-        return (a * 32 + mfma32_row(i, lane)) * P::PITCH + wave * P::WC + b * 32 + (lane & 31);
-    };
-    if (grp == 0) {
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-            for (int b = 0; b < P::FB; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) zs[zo(a, b, i)] = acc[a][b][i];
-    }
-    if (tid < 2) s_flag[tid] = 0u;
-    __syncthreads();
-    if constexpr (KS == 2) {
-        // z = (first half) + (second half), added by the lane that holds
-        // the same element in the second group
-        if (grp == 1) {
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int b = 0; b < P::FB; ++b)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) zs[zo(a, b, i)] += acc[a][b][i];
-        }
-        __syncthreads();
-    }
-
+// Pack the staged 64 x T tile zs (rows of PITCH floats) of row block m0 and
+// tile tc: TwELL slots, counts and row overflow bits (and the dense copy
+// zdbg when given; tw_cnt null: only that copy).  NWAVES waves share the
+// rows; s_flag (2 words, zero) collects the block's overflow bits.  Ends
+// with the block's oflag words written.
+template <int T, int NWAVES>
+__device__ __forceinline__ void pack_tile(const float *zs, int pitch, uint32_t *s_flag,
+                                          int wave, int lane, int tid, int m0, int n0, int tc,
+                                          int M, int N, int C, float *__restrict__ tw_val,
+                                          int32_t *__restrict__ tw_idx,
+                                          int32_t *__restrict__ tw_cnt,
+                                          uint32_t *__restrict__ oflag,
+                                          float *__restrict__ zdbg) {
     constexpr int CPL = T / 64;  // columns per lane
+    const int NT = N / T;
     uint64_t over = 0;           // bit r: row r of the block overflows (wave-uniform)
-    for (int r = wave_all; r < kSmallBM; r += KS * P::NW) {
+    for (int r = wave; r < kSmallBM; r += NWAVES) {
         const int m = m0 + r;
         if (m >= M) break;  // wave-uniform
         float v[CPL];
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) v[k] = zs[r * P::PITCH + lane * CPL + k];
+        for (int k = 0; k < CPL; ++k) v[k] = zs[r * pitch + lane * CPL + k];
         if (zdbg) {
 #pragma unroll
             for (int k = 0; k < CPL; ++k) zdbg[(size_t)m * N + n0 + lane * CPL + k] = v[k];
@@ -407,19 +352,220 @@ __global__ __launch_bounds__(256 * KS) void gate_small_kernel(
         oflag[(size_t)tc * MW + (m0 >> 5) + tid] = s_flag[tid];
 }
 
-template <int T, int KS>
-hipError_t launch_gate_small_k(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
-                               int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
-                               uint32_t *oflag, float *z_debug, hipStream_t s) {
+// PART = false: the fused gate (or, with tw_cnt null, the dense gate into
+// zdbg).  The reduction runs as `nseq` consecutive K-slices, each from zero,
+// added in slice order (the order the split path sums its partial tiles in;
+// nseq = 1 otherwise), by KS groups of waves (two halves when KS = 2).
+// PART = true: workgroup (tile, slice) reduces K-slice `slice` of `nseq` and
+// stores the fp32 partial tile to part[slice][M][N].
+template <int T, int KS, bool PART>
+__global__ __launch_bounds__(256 * KS) void gate_small_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wg_t, int M, int K, int N,
+    int C, int NRB, int nseq, float *__restrict__ tw_val, int32_t *__restrict__ tw_idx,
+    int32_t *__restrict__ tw_cnt, uint32_t *__restrict__ oflag, float *__restrict__ zdbg,
+    float *__restrict__ part) {
+    using P = SmallGate<T, KS>;
+    static_assert(!PART || KS == 1, "one group per K-slice");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint32_t *s_flag = reinterpret_cast<uint32_t *>(smem + P::EPI);  // after the k-loop only
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave_all / P::NW, wave = wave_all % P::NW;  // K half, wave in the group
+    const int NT = N / T;
+    const int tile = PART ? blockIdx.x % (NRB * NT) : blockIdx.x;
+    const int slice = PART ? blockIdx.x / (NRB * NT) : 0;
+    const int rb = tile % NRB, tc = tile / NRB;  // row block, tile
+    const int m0 = rb * kSmallBM, n0 = tc * T;
+
+    // load slot j of a wave: stage rows [16 (4 j + wave), +16); slot 0 is x
+    const rsrc_t ra = make_rsrc(x + (size_t)m0 * K, (uint64_t)(M - m0) * K * 2);
+    const rsrc_t rw = make_rsrc(wg_t + (size_t)n0 * K, (uint64_t)T * K * 2);
+    uint32_t voff[P::NI];
+#pragma unroll
+    for (int j = 0; j < P::NI; ++j) {
+        const int row0 = (j * P::NW + wave) * 16;
+        const int sr = row0 + (lane >> 2);
+        const uint32_t row_off = j == 0 ? (uint32_t)(min(m0 + sr, M - 1) - m0) * K * 2
+                                        : (uint32_t)(sr - kSmallBM) * K * 2;
+        voff[j] = rows16_voff(row_off, lane, row0);
+    }
+    auto issue = [&](int kt, char *st) {
+        const uint32_t soff = kt * kPK * 2;
+#pragma unroll
+        for (int j = 0; j < P::NI; ++j) {
+            const int row0 = (j * P::NW + wave) * 16;
+            if (j == 0) dma16(ra, voff[j], soff, st + row0 * kPRow);
+            else dma16(rw, voff[j], soff, st + row0 * kPRow);
+        }
+    };
+    f32x16 acc[2][P::FB], tot[2][P::FB];
+    u32x4 fa[2][2], fb[2][P::FB];
+    auto load = [&](const char *st, int s, int buf) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a) fa[buf][a] = frag(st, a * 32, s, lane);
+#pragma unroll
+        for (int b = 0; b < P::FB; ++b)
+            fb[buf][b] = frag(st, kSmallBM + wave * P::WC + b * 32, s, lane);
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) acc[a][b] = mfma32(fa[buf][a], fb[buf][b], acc[a][b]);
+    };
+    settle_scalars(tw_val, tw_idx, tw_cnt, oflag, zdbg, part);
+    // K-slices of kts stages; with KS = 2, group g takes half g of each
+    // (both groups run the same number of stages, so the ring's
+    // workgroup-wide barriers pair up)
+    const int kts = K / kPK / nseq, kth = kts / KS;
+    const int q0 = PART ? slice : 0, q1 = PART ? slice + 1 : nseq;
+    for (int q = q0; q < q1; ++q) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) acc[a][b] = f32x16{};
+        const int k0 = q * kts + grp * kth;
+        kloop_pipelined<P::ST, P::NI>(k0, k0 + kth, smem + grp * P::RING, P::STAGE, issue, load,
+                                      mma);
+        __syncthreads();  // the ring is free again
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b) {
+                if (q == q0) tot[a][b] = acc[a][b];
+                else
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) tot[a][b][i] += acc[a][b][i];
+            }
+    }
+    if constexpr (PART) {
+        // the partial tile, one 32-column block per store instruction
+        float *pt = part + (size_t)slice * M * N;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + a * 32 + mfma32_row(i, lane);
+                    if (m < M) pt[(size_t)m * N + n0 + wave * P::WC + b * 32 + (lane & 31)] = tot[a][b][i];
+                }
+        return;
+    }
+
+    float *zs = reinterpret_cast<float *>(smem);
+    auto zo = [&](int a, int b, int i) {
+        return (a * 32 + mfma32_row(i, lane)) * P::PITCH + wave * P::WC + b * 32 + (lane & 31);
+    };
+    if (grp == 0) {
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < P::FB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) zs[zo(a, b, i)] = tot[a][b][i];
+    }
+    if (tid < 2) s_flag[tid] = 0u;
+    __syncthreads();
+    if constexpr (KS == 2) {
+        // z = (first half) + (second half), added by the lane that holds
+        // the same element in the second group
+        if (grp == 1) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < P::FB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) zs[zo(a, b, i)] += tot[a][b][i];
+        }
+        __syncthreads();
+    }
+    pack_tile<T, KS * P::NW>(zs, P::PITCH, s_flag, wave_all, lane, tid, m0, n0, tc, M, N, C,
+                             tw_val, tw_idx, tw_cnt, oflag, zdbg);
+}
+
+// The split path's second pass: workgroup (row block, tile) sums the S
+// partial tiles in slice order into the LDS staging and packs the tile.
+template <int T>
+__global__ __launch_bounds__(256) void gate_sumpack_kernel(
+    const float *__restrict__ part, int S, int M, int N, int C, int NRB,
+    float *__restrict__ tw_val, int32_t *__restrict__ tw_idx, int32_t *__restrict__ tw_cnt,
+    uint32_t *__restrict__ oflag, float *__restrict__ zdbg) {
+    using P = SmallGate<T, 1>;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    float *zs = reinterpret_cast<float *>(smem);
+    uint32_t *s_flag = reinterpret_cast<uint32_t *>(smem + P::EPI);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rb = blockIdx.x % NRB, tc = blockIdx.x / NRB;
+    const int m0 = rb * kSmallBM, n0 = tc * T;
+    const int rows = min(kSmallBM, M - m0);
+    constexpr int C4 = T / 4;  // float4 per tile row
+    constexpr int kMaxS = 8;   // gate_small_parts takes at most 8 slices
+    for (int q = tid; q < rows * C4; q += 256) {
+        const int r = q / C4, c = 4 * (q % C4);
+        const float *src = part + (size_t)(m0 + r) * N + n0 + c;
+        // every slice's load issued before the first add (one latency)
+        float4 u[kMaxS];
+#pragma unroll
+        for (int s = 0; s < kMaxS; ++s)
+            if (s < S) u[s] = *reinterpret_cast<const float4 *>(src + (size_t)s * M * N);
+        float4 v = u[0];
+#pragma unroll
+        for (int s = 1; s < kMaxS; ++s)
+            if (s < S) {
+                v.x += u[s].x;
+                v.y += u[s].y;
+                v.z += u[s].z;
+                v.w += u[s].w;
+            }
+        *reinterpret_cast<float4 *>(zs + r * P::PITCH + c) = v;
+    }
+    if (tid < 2) s_flag[tid] = 0u;
+    __syncthreads();
+    pack_tile<T, 4>(zs, P::PITCH, s_flag, wave, lane, tid, m0, n0, tc, M, N, C, tw_val, tw_idx,
+                    tw_cnt, oflag, zdbg);
+}
+
+template <int T, int KS, bool PART>
+hipError_t launch_small(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int C,
+                        int nseq, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                        uint32_t *oflag, float *z_debug, float *part, hipStream_t s) {
     using P = SmallGate<T, KS>;
     {
-        const hipError_t e = lds_limit_once<&gate_small_kernel<T, KS>>(P::LDS);
+        const hipError_t e = lds_limit_once<&gate_small_kernel<T, KS, PART>>(P::LDS);
         if (e != hipSuccess) return e;
     }
     const int NRB = (M + kSmallBM - 1) / kSmallBM;
-    hipLaunchKernelGGL((gate_small_kernel<T, KS>), dim3(NRB * (N / T)), dim3(P::NTH), P::LDS, s,
-                       x, wg_t, M, K, N, C, NRB, tw_val, tw_idx, tw_cnt, oflag, z_debug);
+    const int grid = NRB * (N / T) * (PART ? nseq : 1);
+    hipLaunchKernelGGL((gate_small_kernel<T, KS, PART>), dim3(grid), dim3(P::NTH), P::LDS, s, x,
+                       wg_t, M, K, N, C, NRB, nseq, tw_val, tw_idx, tw_cnt, oflag, z_debug, part);
     return hipGetLastError();
+}
+
+// The fused small-batch gate: split path (partials, then sum + pack), two K
+// halves per workgroup, or one.  `part`: gate_part_bytes(M, K, N) bytes.
+template <int T>
+hipError_t launch_gate_small(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int C,
+                             float *tw_val, int32_t *tw_idx, int32_t *tw_cnt, uint32_t *oflag,
+                             float *z_debug, float *part, hipStream_t s) {
+    const int S = gate_small_parts(M, N, K);
+    if (S > 1) {
+        hipError_t e = launch_small<T, 1, true>(x, wg_t, M, K, N, C, S, nullptr, nullptr, nullptr,
+                                                nullptr, nullptr, part, s);
+        if (e != hipSuccess) return e;
+        using P = SmallGate<T, 1>;
+        e = lds_limit_once<&gate_sumpack_kernel<T>>(P::EPI + 16);
+        if (e != hipSuccess) return e;
+        const int NRB = (M + kSmallBM - 1) / kSmallBM;
+        hipLaunchKernelGGL(gate_sumpack_kernel<T>, dim3(NRB * (N / T)), dim3(256), P::EPI + 16, s,
+                           part, S, M, N, C, NRB, tw_val, tw_idx, tw_cnt, oflag, z_debug);
+        return hipGetLastError();
+    }
+    if (gate_small_split(M, N, K))
+        return launch_small<T, 2, false>(x, wg_t, M, K, N, C, 1, tw_val, tw_idx, tw_cnt, oflag,
+                                         z_debug, nullptr, s);
+    return launch_small<T, 1, false>(x, wg_t, M, K, N, C, 1, tw_val, tw_idx, tw_cnt, oflag,
+                                     z_debug, nullptr, s);
 }
 
 // Ascending list of the rows whose bit is set in any column block.  One
@@ -507,17 +653,21 @@ int gate_flag_blocks(int M, int N, int T) {
     return gate_small(M, N) ? N / T : gate_col_blocks(N);
 }
 
+size_t gate_part_bytes(int M, int K, int N) {
+    const int S = gate_small_parts(M, N, K);
+    return S > 1 ? (size_t)S * M * N * sizeof(float) : 0;
+}
+
 hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
                              int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
-                             uint32_t *oflag, float *z_debug, hipStream_t s) {
+                             uint32_t *oflag, float *z_debug, float *part, hipStream_t s) {
     if (M == 0) return hipSuccess;
     if (gate_small(M, N)) {
-        const bool split = gate_small_split(M, N);
-#define TW_SMALL(t, ks) \
-    launch_gate_small_k<t, ks>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug, s)
-        if (T == 128) return split ? TW_SMALL(128, 2) : TW_SMALL(128, 1);
-        return split ? TW_SMALL(256, 2) : TW_SMALL(256, 1);
-#undef TW_SMALL
+        if (T == 128)
+            return launch_gate_small<128>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
+                                          z_debug, part, s);
+        return launch_gate_small<256>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag, z_debug,
+                                      part, s);
     }
     if (T == 128)
         return launch_gate_t<128, true>(x, wg_t, M, K, N, C, tw_val, tw_idx, tw_cnt, oflag,
@@ -529,14 +679,20 @@ hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int
 hipError_t launch_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
                              float *z, hipStream_t s) {
     if (M == 0) return hipSuccess;
-    // the kernel tw_pack_gate would take, so that z is the same to the bit
-    // (the small-batch kernel's two K halves sum in another order)
-    if (gate_small(M, N))
-        return gate_small_split(M, N)
-                   ? launch_gate_small_k<128, 2>(x, wg_t, M, K, N, 1, nullptr, nullptr, nullptr,
-                                                 nullptr, z, s)
-                   : launch_gate_small_k<128, 1>(x, wg_t, M, K, N, 1, nullptr, nullptr, nullptr,
-                                                 nullptr, z, s);
+    // the summation order tw_pack_gate would take, so that z is the same to
+    // the bit: its K-slices (added in slice order, here within each
+    // workgroup, so no workspace is needed) or its two K halves
+    if (gate_small(M, N)) {
+        const int S = gate_small_parts(M, N, K);
+        if (S > 1)
+            return launch_small<128, 1, false>(x, wg_t, M, K, N, 1, S, nullptr, nullptr, nullptr,
+                                               nullptr, z, nullptr, s);
+        if (gate_small_split(M, N, K))
+            return launch_small<128, 2, false>(x, wg_t, M, K, N, 1, 1, nullptr, nullptr, nullptr,
+                                               nullptr, z, nullptr, s);
+        return launch_small<128, 1, false>(x, wg_t, M, K, N, 1, 1, nullptr, nullptr, nullptr,
+                                           nullptr, z, nullptr, s);
+    }
     return launch_gate_t<128, false>(x, wg_t, M, K, N, 1, nullptr, nullptr, nullptr, nullptr, z,
                                      s);
 }

@@ -66,6 +66,10 @@ tw_status check_hybrid(int M, int K, int N, int T, int C, int P, int R_max) {
 size_t pack_ws(int M, int N) {
     return round_up((size_t)((N + 127) / 128) * tw::row_words(M) * 4, 256);
 }
+// tw_pack_gate: the overflow bits, then the small-batch gate's partial gates
+size_t gate_ws(int M, int K, int N) {
+    return pack_ws(M, N) + round_up(tw::gate_part_bytes(M, K, N), 256);
+}
 // overflow path: h rows [R_max][N] bf16, then the split partial tiles;
 // then the sparse kernel's partial rows (small batches)
 size_t overflow_ws(int R_max, int N) {
@@ -128,7 +132,7 @@ size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max) {
     const tw_status st = check_shape(M, K, N, T, C, R_max);
     std::snprintf(g_err, sizeof g_err, "%s", saved);
     if (st != TW_OK) return 0;
-    size_t a = pack_ws(M, N), b = sparse_ws(M, K, R_max, N);
+    size_t a = gate_ws(M, K, N), b = sparse_ws(M, K, R_max, N);
     return (a > b ? a : b) + 256;
 }
 
@@ -158,9 +162,10 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t, int M, int K, in
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t *oflag = static_cast<uint32_t *>(ws);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + pack_ws(M, N));
     TW_TRY(record(events, 0, s));
     TW_TRY(launched(tw::launch_gate_twell(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, oflag,
-                                          z_debug, s),
+                                          z_debug, part, s),
                     "gate_twell launch"));
     TW_TRY(record(events, 1, s));
     TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_flag_blocks(M, N, T), tw::row_words(M),

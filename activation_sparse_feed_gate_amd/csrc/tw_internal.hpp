@@ -25,9 +25,13 @@ inline bool gate_small(int M, int N) {
 // Column blocks of the row-overflow bits launch_gate_twell writes.
 int gate_flag_blocks(int M, int N, int T);
 
+// Workspace of the small-batch gate's split reduction (fp32 partial gates;
+// 0 when the batch does not take it).
+size_t gate_part_bytes(int M, int K, int N);
+
 hipError_t launch_gate_twell(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
                              int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
-                             uint32_t *oflag, float *z_debug, hipStream_t s);
+                             uint32_t *oflag, float *z_debug, float *part, hipStream_t s);
 
 // The dense gate z = x W_g as fp32 [M][N] (the gate kernel without its
 // packing epilogue).

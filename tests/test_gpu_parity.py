@@ -67,6 +67,9 @@ def _full_check(tw, w, R_max=None, dense=True):
     # batches of 32 to 128 rows: each row over 256 / M workgroups whose
     # partial rows a second kernel sums (2B and 0.5B block shapes)
     dict(M=32, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5),
+    # few rows at the 2B block: the gate's reduction split into 8 K-slices
+    dict(M=16, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=6),
+    dict(M=3, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=7),
     dict(M=100, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=2),
     dict(M=128, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=4),
 ])

@@ -46,6 +46,9 @@ def _host(p):
     ("tiny", dict(M=513, K=512, N=2048, T=256, C=12, density=0.01, sigma_s=0.7, seed=3)),
     ("tiny", dict(M=1, K=128, N=128, C=3, density=0.1)),
     ("tiny", dict(density=1.0, C=128)),                           # every entry active
+    # few rows: the gate's reduction split into K-slices over workgroups
+    # (fused: partial tiles summed by a second pass; dense: summed in place)
+    ("tiny", dict(M=8, K=1024, N=2048, T=256, C=8, density=0.01, sigma_s=0.5)),
     ("ffn-0.5b", dict()),                                         # the full 0.5B block
 ])
 def test_unfused_equals_fused(tw, name, kw):
