@@ -385,7 +385,8 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
                 }
             }
         } else {
-            // partial tile of split sp, summed by split_reduce_kernel
+            // partial tile of split sp, summed in split order later (split_reduce_kernel,
+            // or the sparse kernels that take the listed rows; tw_split.hpp)
             float *pt = partial + ((size_t)sp * tiles + tile) * (BM * BN);
 #pragma unroll
             for (int a = 0; a < P::FA; ++a)
