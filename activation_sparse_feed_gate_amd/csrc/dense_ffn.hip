@@ -615,6 +615,25 @@ using GuRows = GuCfg<128, 128, 2, 4, 4>;
 using GuSmall = GuCfg<64, 64, 2, 2, 4>;
 using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
 using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
+using GuSmallKeep = GuCfg<64, 64, 2, 2, 4, kKeep>;
+using GuSmallDh = GuCfg<64, 64, 2, 2, 4, kDh>;
+
+// A row-list gate+up configuration G over a grid of at most grid_cap
+// persistent workgroups (sized for the capacity; the rows are counted on the
+// device).
+template <typename G>
+hipError_t launch_gu(int grid_cap, const uint16_t *x, const uint16_t *w1, const uint16_t *w2,
+                     int K, int N, const int32_t *rowlist, const int32_t *count, int R_cap,
+                     int xrows, uint16_t *o1, uint16_t *o2, uint16_t *o3, const uint16_t *g_in,
+                     const uint16_t *u_in, float l1, hipStream_t s) {
+    hipError_t e = lds_limit_once<G::kernel>(G::LDS);
+    if (e != hipSuccess) return e;
+    const int tiles = (R_cap + G::BM_ - 1) / G::BM_ * (N / G::BN_);
+    hipLaunchKernelGGL(G::kernel, dim3(tiles < grid_cap ? tiles : grid_cap), dim3(G::NTH), G::LDS,
+                       s, x, w1, w2, K, N, rowlist, count, R_cap, xrows, o1, o2, o3, g_in, u_in,
+                       l1);
+    return hipGetLastError();
+}
 using DnDense = DnCfg<128, 128, 2, 2, 4>;
 using DnRows = DnCfg<128, 128, 2, 4, 6>;
 using DnRowsPair = DnCfg<128, 128, 2, 4, 6, 2>;
@@ -724,14 +743,12 @@ hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,
                               uint16_t *u_out, hipStream_t s) {
     if (!g_out && !u_out) return launch_gateup(x, M, wg_t, wu_t, K, N, rowlist, count, R_cap, h, s);
     if (R_cap <= 0) return hipSuccess;
-    hipError_t e = lds_limit_once<GuRowsKeep::kernel>(GuRowsKeep::LDS);
-    if (e != hipSuccess) return e;
-    const int tiles = (R_cap + GuRowsKeep::BM_ - 1) / GuRowsKeep::BM_ * (N / GuRowsKeep::BN_);
-    const int grid = tiles < 256 ? tiles : 256;
-    hipLaunchKernelGGL(GuRowsKeep::kernel, dim3(grid), dim3(GuRowsKeep::NTH), GuRowsKeep::LDS, s,
-                       x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, g_out, u_out, nullptr,
-                       nullptr, 0.0f);
-    return hipGetLastError();
+    // the tiles of launch_gateup's row-list path
+    if (R_cap <= kSmallRows)
+        return launch_gu<GuSmallKeep>(1024, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h,
+                                      g_out, u_out, nullptr, nullptr, 0.0f, s);
+    return launch_gu<GuRowsKeep>(256, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, g_out,
+                                 u_out, nullptr, nullptr, 0.0f, s);
 }
 
 hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K, int N,
@@ -739,14 +756,11 @@ hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K
                             const uint16_t *g_in, const uint16_t *u_in, float l1,
                             uint16_t *du, uint16_t *dz, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
-    hipError_t e = lds_limit_once<GuRowsDh::kernel>(GuRowsDh::LDS);
-    if (e != hipSuccess) return e;
-    const int tiles = (R_cap + GuRowsDh::BM_ - 1) / GuRowsDh::BM_ * (N / GuRowsDh::BN_);
-    const int grid = tiles < 256 ? tiles : 256;
-    hipLaunchKernelGGL(GuRowsDh::kernel, dim3(grid), dim3(GuRowsDh::NTH), GuRowsDh::LDS, s, dy,
-                       wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz, nullptr, g_in, u_in,
-                       l1);
-    return hipGetLastError();
+    if (R_cap <= kSmallRows)
+        return launch_gu<GuSmallDh>(1024, dy, wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz,
+                                    nullptr, g_in, u_in, l1, s);
+    return launch_gu<GuRowsDh>(256, dy, wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz,
+                               nullptr, g_in, u_in, l1, s);
 }
 
 hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
