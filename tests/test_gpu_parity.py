@@ -91,6 +91,18 @@ def test_density_extremes(tw, kw):
         assert g["ovf_count"] == 64
 
 
+@pytest.mark.parametrize("kw,R_max", [
+    (dict(C=12), 8),                                     # ~7 listed rows of 8
+    (dict(M=64, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5), 8),  # 0.5B block
+    (dict(M=16, K=2048, N=8192, T=256, C=16, density=0.01, sigma_s=0.5, seed=9), 2),
+])
+def test_few_overflow_rows(tw, kw, R_max):
+    """A backup capacity of a handful of rows (decode-size batches): the
+    backup's split partials for one row block, summed by the sparse kernel."""
+    g, _ = _full_check(tw, W["tiny"].with_(**kw), R_max=R_max)
+    print(f"overflow rows {g['ovf_count']} of capacity {R_max}", flush=True)
+
+
 def test_capacity_retry(tw):
     """Too small a dense backup: the true count comes back, and a retry with
     enough room gives the full result (the retry of the static-capacity
