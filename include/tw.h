@@ -44,9 +44,12 @@
  *   size is a multiple of M may be NULL.
  * - Optional `events`: NULL, or an array of hipEvent_t (passed as void*)
  *   with one more entry than the call launches kernels, for per-kernel
- *   durations with hipEventElapsedTime.  tw_pack_gate (2 kernels) and
- *   tw_ffn_fwd (2 kernels) record events[0] on `stream` before the first
- *   kernel and events[i+1] after kernel i.  tw_sparse_ffn_fwd takes 5
+ *   durations with hipEventElapsedTime.  tw_pack_gate records events[0]
+ *   on `stream` before the gate, events[1] after it (one kernel; for a few
+ *   token rows two: the K-sliced partial gates, then their sum and the
+ *   packing) and events[2] after the overflow-list compaction.  tw_ffn_fwd
+ *   (2 kernels) records events[0] before the first kernel and events[i+1]
+ *   after kernel i.  tw_sparse_ffn_fwd takes 5
  *   events for 3 kernels: events[0] before any of them, events[1] and [2]
  *   after the overflow rows' gate+up and down GEMMs, events[3] after the
  *   sparse up+down kernel (which also finishes the overflow rows' split
