@@ -61,6 +61,21 @@ def test_workspace_bytes(tw):
     assert tw.tw_ffn_workspace_bytes(64, 256, 1024) >= 64 * 1024 * 2
 
 
+def test_workspace_covers_small_batch_buffers(tw):
+    """The workspace also holds the small-batch gate's partial gates (a few
+    rows: 8 K-slices of M x N fp32), the sparse kernel's partial rows (32 to
+    128 rows: 256 / M per row, M x K fp32 each) and the backup's split
+    partial tiles (16 MB)."""
+    # 16 rows of the 2B block: the gate's reduction in 8 slices
+    assert tw.tw_workspace_bytes(16, 2048, 8192, 256, 16, 2) >= 8 * 16 * 8192 * 4
+    # 64 rows of the 0.5B block: 4 partial rows per row, after the backup's
+    # h rows and split partials
+    need = 8 * 4096 * 2 + (16 << 20) + 4 * 64 * 1024 * 4
+    assert tw.tw_workspace_bytes(64, 1024, 4096, 128, 8, 8) >= need
+    # no backup room: the partial rows alone still fit
+    assert tw.tw_workspace_bytes(64, 1024, 4096, 128, 8, 0) >= 4 * 64 * 1024 * 4
+
+
 # Fake, 16-byte-aligned device addresses: every case below must be rejected
 # on the host before any of them is dereferenced or any HIP call is made.
 P = 0x100000
