@@ -78,6 +78,17 @@ def test_tiny_all_rows(tw, kw):
 
 
 @pytest.mark.parametrize("kw", [
+    # the largest shapes the library accepts: K = 4096 and 256 tiles per row
+    # (here with the 256 x 256 gate kernel and several workgroups per row) ...
+    dict(M=40, K=4096, N=32768, T=128, C=8, density=0.003, sigma_s=0.5, seed=11),
+    # ... and K = 4096 in the few-row gate whose reduction is split into K-slices
+    dict(M=8, K=4096, N=1024, T=128, C=8, density=0.02, sigma_s=0.5, seed=12),
+])
+def test_maximum_sizes(tw, kw):
+    _full_check(tw, W["tiny"].with_(**kw))
+
+
+@pytest.mark.parametrize("kw", [
     dict(density=0.0), dict(density=1.0, C=128), dict(density=1.0, C=16),
     dict(density=1.0, T=256, C=256),
 ])
