@@ -10,14 +10,21 @@ from activation_sparse_feed_gate_amd import synth
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("kw", [
+    dict(M=700, C=6, sigma_s=0.5, density=0.03),  # one workgroup per row
+    # 2B block: 48 rows (each over several workgroups, partial rows summed by
+    # a second kernel) and 8 rows (the gate's reduction split into K-slices)
+    dict(M=48, K=2048, N=8192, T=256, C=8, density=0.01, sigma_s=0.5, seed=21),
+    dict(M=8, K=2048, N=8192, T=256, C=8, density=0.01, sigma_s=0.5, seed=22),
+])
+def test_graph_replay_matches_eager(kw):
     import torch
 
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from activation_sparse_feed_gate_amd import tw
 
-    w = synth.WORKLOADS["tiny"].with_(M=700, C=6, sigma_s=0.5, density=0.03)
+    w = synth.WORKLOADS["tiny"].with_(**kw)
     print(f"case {w}", flush=True)
     dev = parity.upload(synth.make_inputs(w))
     x, wg, wu, wd = dev["x"], dev["wg_t"], dev["wu_t"], dev["wd"]
