@@ -16,6 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libtw.so")
+PEAK_PROBE = os.path.join(HERE, "peak_probe")  # achievable-peak program (csrc/peak_probe.hip)
 
 SOURCES = ["gate_twell.hip", "pack_dense.hip", "sparse_updown.hip", "dense_ffn.hip", "hybrid.hip",
            "tw_api.cpp"]
@@ -56,7 +57,17 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIBRARY)
+    build_peak_probe(verbose)
     return LIBRARY
+
+
+def build_peak_probe(verbose: bool = False) -> str:
+    """Compile the standalone achievable-peak program; returns its path."""
+    cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "peak_probe.hip"), "-o", PEAK_PROBE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return PEAK_PROBE
 
 
 if __name__ == "__main__":
