@@ -191,7 +191,7 @@ def test_hybrid_parity(tw, name, kw, P, R_max):
         assert not g["y"].any() and g["bk_count"] == 0
 
 
-@pytest.mark.parametrize("name", ["ffn-0.5b", "ffn-2b"])
+@pytest.mark.parametrize("name", ["ffn-0.5b", "ffn-1b", "ffn-2b", "ffn-ovf", "ffn-paper"])
 def test_hybrid_full_size(tw, name):
     """Full shapes at the static capacities (P = 128, backup room M / 8):
     the whole conversion bit-exact, values and y on sampled rows (every
