@@ -119,7 +119,7 @@ def _dense(hy, vals_sp, vals_bk, N):
     return out
 
 
-def _check(g, acts, r, d, dy_bits, w, l1):
+def _check(g, acts, r, d, dy_bits, w, l1, weights=True):
     orc = oracle.default()
     ref = orc.hybrid_bwd(d["x"], d["wg_t"], d["wu_t"], d["wd"], dy_bits, g, acts, l1)
     N, K = w.N, w.K
@@ -170,6 +170,8 @@ def _check(g, acts, r, d, dy_bits, w, l1):
     assert np.all(np.abs(r["dx"][stored] - ref["dx"][stored]) <= bdx[stored]), "dx"
     parity.check_y(r["dx"][stored], ref["dx"][stored], "dx")
     assert np.all(np.isnan(r["dx"][~stored])), "a row with nothing stored got a dx"
+    if not weights:
+        return int(stored.sum())
     # weight gradients
     gm = _gamma(w.M)
     xs, dys = x * stored[:, None], dy * stored[:, None]
@@ -236,3 +238,49 @@ def test_hybrid_bwd_full_size_and_determinism(tw):
         assert np.array_equal(a.view(np.uint64), b.view(np.uint64)), f"{k} not repeatable"
     assert g["bk_count"] <= R_max
     _check(g, acts, r1, d, dy_bits, w, l1)
+
+
+def _rows(g, acts, r, d, dy_bits, rows):
+    """The storage, activations, GPU gradients and inputs of a subset of
+    token rows (ascending): every quantity but the weight gradients is per
+    row, so the oracle's backward on the subset is the full one's rows."""
+    pos = {int(m): i for i, m in enumerate(rows)}
+    sel = [k for k, m in enumerate(g["bk_rows"]) if int(m) in pos]
+    gs = {"hy_cnt": g["hy_cnt"][rows], "hy_idx": g["hy_idx"][rows], "hy_val": g["hy_val"][rows],
+          "route": g["route"][rows], "bk_count": len(sel),
+          "bk_rows": np.array([pos[int(g["bk_rows"][k])] for k in sel], dtype=g["bk_rows"].dtype)}
+    acs = {"hy_u": acts["hy_u"][rows], "hy_h": acts["hy_h"][rows]}
+    rs = {"hy_du": r["hy_du"][rows], "hy_dz": r["hy_dz"][rows], "dx": r["dx"][rows]}
+    for k in ("bk_g", "bk_u", "bk_h"):
+        acs[k] = acts[k][sel]
+    for k in ("bk_du", "bk_dz"):
+        rs[k] = r[k][sel]
+    ds = dict(d, x=d["x"][rows])
+    return gs, acs, rs, ds, dy_bits[rows]
+
+
+def test_hybrid_bwd_2b_sampled_rows(tw):
+    """The full 2B block at the static capacities: the whole backward runs on
+    the GPU; du, dz and dx are checked on sampled rows (backup rows, sparse
+    rows, the first and the last) against the oracle's backward of those
+    rows."""
+    w = W["ffn-2b"]
+    P, R_max, l1 = 128, w.M // 8, 2e-5 * 1000
+    print(f"case {w} P={P} R_max={R_max} l1={l1}", flush=True)
+    d = synth.make_inputs(w)
+    dev = parity.upload(d)
+    dy_bits = _dy(w)
+    g, acts, (r,) = _run(tw, dev, w, P, R_max, l1, parity.to_dev(dy_bits))
+    assert 0 < g["bk_count"] <= R_max
+    rng = np.random.default_rng(5)
+    bk = g["bk_rows"]
+    sparse_rows = np.nonzero(g["route"] == 0)[0]
+    rows = np.unique(np.concatenate([
+        rng.choice(bk, size=min(16, len(bk)), replace=False),
+        rng.choice(sparse_rows, size=min(32, len(sparse_rows)), replace=False),
+        [0, w.M - 1]]).astype(np.int64))
+    gs, acs, rs, ds, dys = _rows(g, acts, r, d, dy_bits, rows)
+    assert gs["bk_count"] > 0
+    n = _check(gs, acs, rs, ds, dys, w.with_(M=len(rows)), l1, weights=False)
+    print(f"checked {len(rows)} rows ({gs['bk_count']} backup), {n} with stored activations",
+          flush=True)
