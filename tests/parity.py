@@ -117,3 +117,22 @@ def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what="y") -> float:
     tol = 1e-2 * float(np.abs(y_ref).max(initial=0.0)) + 1e-3
     assert err <= tol, f"{what}: max error {err} > tolerance {tol}"
     return err
+
+
+def hybrid_row_subset(g: dict, acts: dict, r: dict, d: dict, dy_bits, rows):
+    """The storage, activations, GPU gradients and inputs of a subset of
+    token rows (ascending): every quantity but the weight gradients is per
+    row, so the oracle's backward on the subset is the full one's rows."""
+    pos = {int(m): i for i, m in enumerate(rows)}
+    sel = [k for k, m in enumerate(g["bk_rows"]) if int(m) in pos]
+    gs = {"hy_cnt": g["hy_cnt"][rows], "hy_idx": g["hy_idx"][rows], "hy_val": g["hy_val"][rows],
+          "route": g["route"][rows], "bk_count": len(sel),
+          "bk_rows": np.array([pos[int(g["bk_rows"][k])] for k in sel], dtype=g["bk_rows"].dtype)}
+    acs = {"hy_u": acts["hy_u"][rows], "hy_h": acts["hy_h"][rows]}
+    rs = {"hy_du": r["hy_du"][rows], "hy_dz": r["hy_dz"][rows], "dx": r["dx"][rows]}
+    for k in ("bk_g", "bk_u", "bk_h"):
+        acs[k] = acts[k][sel]
+    for k in ("bk_du", "bk_dz"):
+        rs[k] = r[k][sel]
+    ds = dict(d, x=d["x"][rows])
+    return gs, acs, rs, ds, dy_bits[rows]

@@ -240,25 +240,6 @@ def test_hybrid_bwd_full_size_and_determinism(tw):
     _check(g, acts, r1, d, dy_bits, w, l1)
 
 
-def _rows(g, acts, r, d, dy_bits, rows):
-    """The storage, activations, GPU gradients and inputs of a subset of
-    token rows (ascending): every quantity but the weight gradients is per
-    row, so the oracle's backward on the subset is the full one's rows."""
-    pos = {int(m): i for i, m in enumerate(rows)}
-    sel = [k for k, m in enumerate(g["bk_rows"]) if int(m) in pos]
-    gs = {"hy_cnt": g["hy_cnt"][rows], "hy_idx": g["hy_idx"][rows], "hy_val": g["hy_val"][rows],
-          "route": g["route"][rows], "bk_count": len(sel),
-          "bk_rows": np.array([pos[int(g["bk_rows"][k])] for k in sel], dtype=g["bk_rows"].dtype)}
-    acs = {"hy_u": acts["hy_u"][rows], "hy_h": acts["hy_h"][rows]}
-    rs = {"hy_du": r["hy_du"][rows], "hy_dz": r["hy_dz"][rows], "dx": r["dx"][rows]}
-    for k in ("bk_g", "bk_u", "bk_h"):
-        acs[k] = acts[k][sel]
-    for k in ("bk_du", "bk_dz"):
-        rs[k] = r[k][sel]
-    ds = dict(d, x=d["x"][rows])
-    return gs, acs, rs, ds, dy_bits[rows]
-
-
 def test_hybrid_bwd_2b_sampled_rows(tw):
     """The full 2B block at the static capacities: the whole backward runs on
     the GPU; du, dz and dx are checked on sampled rows (backup rows, sparse
@@ -279,7 +260,7 @@ def test_hybrid_bwd_2b_sampled_rows(tw):
         rng.choice(bk, size=min(16, len(bk)), replace=False),
         rng.choice(sparse_rows, size=min(32, len(sparse_rows)), replace=False),
         [0, w.M - 1]]).astype(np.int64))
-    gs, acs, rs, ds, dys = _rows(g, acts, r, d, dy_bits, rows)
+    gs, acs, rs, ds, dys = parity.hybrid_row_subset(g, acts, r, d, dy_bits, rows)
     assert gs["bk_count"] > 0
     n = _check(gs, acs, rs, ds, dys, w.with_(M=len(rows)), l1, weights=False)
     print(f"checked {len(rows)} rows ({gs['bk_count']} backup), {n} with stored activations",
