@@ -50,6 +50,8 @@ def _host(p):
     # (fused: partial tiles summed by a second pass; dense: summed in place)
     ("tiny", dict(M=8, K=1024, N=2048, T=256, C=8, density=0.01, sigma_s=0.5)),
     ("ffn-0.5b", dict()),                                         # the full 0.5B block
+    ("ffn-2b", dict()),                                           # full 2B block, T = 256
+    ("ffn-ovf", dict()),                                          # full overflow-stress block
 ])
 def test_unfused_equals_fused(tw, name, kw):
     w = W[name].with_(**kw)
