@@ -78,6 +78,22 @@ def test_tiny_all_rows(tw, kw):
 
 
 @pytest.mark.parametrize("kw", [
+    # both sides of each batch-size route change, every row checked: at the
+    # 0.5B block the 256 x 256 gate kernel takes over above 768 rows, at the
+    # 2B block above 256; the sparse kernel drops from 16 to 4 waves per row
+    # above 256 rows
+    dict(M=256, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=31),
+    dict(M=257, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=32),
+    dict(M=768, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=33),
+    dict(M=769, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=34),
+    dict(M=256, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=35),
+    dict(M=257, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=36),
+])
+def test_route_boundaries(tw, kw):
+    _full_check(tw, W["tiny"].with_(**kw))
+
+
+@pytest.mark.parametrize("kw", [
     # the largest shapes the library accepts: K = 4096 and 256 tiles per row
     # (here with the 256 x 256 gate kernel and several workgroups per row) ...
     dict(M=40, K=4096, N=32768, T=128, C=8, density=0.003, sigma_s=0.5, seed=11),
