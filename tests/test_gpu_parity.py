@@ -88,6 +88,19 @@ def test_tiny_all_rows(tw, kw):
     dict(M=769, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=34),
     dict(M=256, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=35),
     dict(M=257, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=36),
+    # inside the small-batch gate: its reduction split into K-slices up to 8
+    # rows (0.5B block) or 16 (2B), two K halves per workgroup up to 448 rows
+    # (0.5B) or 192 (2B), one beyond
+    dict(M=8, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=37),
+    dict(M=9, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=38),
+    dict(M=448, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=39),
+    dict(M=449, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=40),
+    dict(M=17, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=41),
+    dict(M=192, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=42),
+    dict(M=193, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=43),
+    # the sparse kernel spreads a row over 256 / M workgroups for 32 to 128 rows
+    dict(M=31, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=44),
+    dict(M=129, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=45),
 ])
 def test_route_boundaries(tw, kw):
     _full_check(tw, W["tiny"].with_(**kw))
