@@ -178,10 +178,30 @@ def test_deterministic(tw, M):
     dev = parity.upload(d)
     a = parity.run_path(tw, dev, w.T, w.C, w.M)
     b = parity.run_path(tw, dev, w.T, w.C, w.M)
-    for k in ("tw_cnt", "ovf_rows", "y", "y_dense", "z"):
+    assert a["ovf_count"] == b["ovf_count"]
+    n = a["ovf_count"]  # list entries past the count are unspecified
+    assert np.array_equal(a["ovf_rows"][:n], b["ovf_rows"][:n])
+    for k in ("tw_cnt", "y", "y_dense", "z"):
         assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
     used = np.arange(w.C)[None, None, :] < np.minimum(a["tw_cnt"], w.C)[:, :, None]
     assert np.array_equal(np.where(used, a["tw_idx"], 0), np.where(used, b["tw_idx"], 0))
+
+
+@pytest.mark.parametrize("name", ["ffn-0.5b", "ffn-2b"])
+def test_deterministic_full_size(tw, name):
+    """The benchmark's configuration (full block, backup room M / 8) gives
+    the same bits run after run: counts, overflow list, y and the dense y."""
+    w = W[name]
+    R_max = w.M // 8
+    print(f"case {w} R_max={R_max}", flush=True)
+    dev = parity.upload(synth.make_inputs(w))
+    a = parity.run_path(tw, dev, w.T, w.C, R_max, z_debug=False)
+    b = parity.run_path(tw, dev, w.T, w.C, R_max, z_debug=False)
+    assert 0 < a["ovf_count"] <= R_max and a["ovf_count"] == b["ovf_count"]
+    n = a["ovf_count"]  # list entries past the count are unspecified
+    assert np.array_equal(a["ovf_rows"][:n], b["ovf_rows"][:n])
+    for k in ("tw_cnt", "y", "y_dense"):
+        assert np.array_equal(a[k].view(np.uint8), b[k].view(np.uint8)), k
 
 
 def _sample_rows(g, M, C, n_even=32, n_ovf=16, n_heavy=16):
