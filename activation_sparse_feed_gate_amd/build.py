@@ -57,12 +57,14 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIBRARY)
-    build_peak_probe(verbose)
     return LIBRARY
 
 
 def build_peak_probe(verbose: bool = False) -> str:
-    """Compile the standalone achievable-peak program; returns its path."""
+    """Compile the standalone achievable-peak program (a measurement tool,
+    not part of the library: built only on request, with
+    ``python -m activation_sparse_feed_gate_amd.build --peak-probe``);
+    returns its path."""
     cmd = [HIPCC, *FLAGS, os.path.join(CSRC, "peak_probe.hip"), "-o", PEAK_PROBE]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -71,4 +73,7 @@ def build_peak_probe(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--peak-probe" in sys.argv:
+        print(build_peak_probe(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

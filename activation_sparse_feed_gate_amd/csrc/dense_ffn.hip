@@ -734,7 +734,7 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
 }
 
 bool dense_down_split(int M, int K) {
-    return (size_t)((M + DnDense::BM_ - 1) / DnDense::BM_) * (K / DnDense::BN_) < kFillTiles;
+    return ((size_t)M + DnDense::BM_ - 1) / DnDense::BM_ * (size_t)(K / DnDense::BN_) < kFillTiles;
 }
 
 hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,

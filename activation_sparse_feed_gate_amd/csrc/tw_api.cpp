@@ -58,13 +58,17 @@ tw_status check_hybrid(int M, int K, int N, int T, int C, int P, int R_max) {
         return fail(TW_EUNSUPPORTED, "R_max*N=%lld: backup rows must stay under 4 GiB",
                     (long long)R_max * N);
     if (P < 1 || P > N) return fail(TW_EINVAL, "sparse row capacity P=%d outside [1, N=%d]", P, N);
+    // the kernels name a stored slot by the 32-bit id m * P + s
+    if ((int64_t)M * P >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "M*P = %lld stored slots: at most 2^31 - 1",
+                    (long long)M * P);
     return TW_OK;
 }
 
 // row-overflow bits: at most N / 128 column blocks (the small-batch gate
 // kernel with T = 128) by ceil(M / 32) words
 size_t pack_ws(int M, int N) {
-    return round_up((size_t)((N + 127) / 128) * tw::row_words(M) * 4, 256);
+    return round_up(((size_t)N + 127) / 128 * (((size_t)M + 31) / 32) * 4, 256);
 }
 // tw_pack_gate: the overflow bits, then the small-batch gate's partial gates
 size_t gate_ws(int M, int K, int N) {
@@ -138,7 +142,8 @@ size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max) {
 
 // h [M][N] bf16, and when the down GEMM splits its reduction its partials
 size_t tw_ffn_workspace_bytes(int M, int K, int N) {
-    if (M < 0 || K <= 0 || N <= 0) return 0;
+    if (M < 0 || K <= 0 || N <= 0 || N % 128 || K % 128) return 0;
+    if ((int64_t)N * K >= (int64_t(1) << 31)) return 0;
     const size_t split = tw::dense_down_split(M, K) ? tw::split_partial_bytes() : 0;
     return round_up((size_t)M * N * 2, 256) + split + 256;
 }
@@ -180,6 +185,10 @@ tw_status tw_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, i
     if (M < 0 || K <= 0 || N <= 0) return fail(TW_EINVAL, "M=%d K=%d N=%d: need M >= 0, K, N > 0", M, K, N);
     if (K % 128) return fail(TW_EUNSUPPORTED, "K=%d: must be a multiple of 128", K);
     if (N % 128) return fail(TW_EUNSUPPORTED, "N=%d: must be a multiple of 128", N);
+    // tw_pack_gate's kernels, so tw_pack_gate's limits on K and on x
+    if (K > 4096) return fail(TW_EUNSUPPORTED, "K=%d: at most 4096", K);
+    if ((int64_t)M * K >= (int64_t(1) << 31))
+        return fail(TW_EUNSUPPORTED, "M*K=%lld: x must stay under 4 GiB", (long long)M * K);
     TW_NEED_M(x);
     TW_NEED(wg_t);
     TW_NEED_M(z);
@@ -510,7 +519,13 @@ tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, in
 }
 
 size_t tw_hybrid_bwd_dw_workspace_bytes(int M, int K, int N, int P, int R_max) {
-    if (M < 0 || K <= 0 || N <= 0 || P < 1 || R_max < 0) return 0;
+    // a shape tw_hybrid_bwd_dw rejects needs no workspace (and its sizes
+    // might not be representable); the check's message is not kept
+    char saved[sizeof g_err];
+    std::snprintf(saved, sizeof saved, "%s", g_err);
+    const tw_status st = check_hybrid(M, K, N, 128, 1, P, R_max);
+    std::snprintf(g_err, sizeof g_err, "%s", saved);
+    if (st != TW_OK) return 0;
     return tw::hybrid_dw_bytes(M, K, N, P, R_max) + 256;
 }
 
@@ -522,9 +537,6 @@ tw_status tw_hybrid_bwd_dw(const uint16_t *x, const uint16_t *dy, int M, int K, 
                            float *dwg_t, float *dwu_t, float *dwd, void *ws, size_t ws_bytes,
                            void *stream, void *const *events) {
     TW_TRY(check_hybrid(M, K, N, 128, 1, P, R_max));
-    if ((int64_t)M * P >= (int64_t(1) << 31))
-        return fail(TW_EUNSUPPORTED, "M*P = %lld stored slots: at most 2^31 - 1",
-                    (long long)M * P);
     TW_NEED_M(x);
     TW_NEED_M(dy);
     TW_NEED_M(hy_h);

@@ -107,9 +107,71 @@ def _ptr(t):
     return t.data_ptr()
 
 
-def _dtype(t, dt, name):
-    if t.dtype != dt:
-        raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+_F32, _I32, _BF16, _U8T = torch.float32, torch.int32, torch.bfloat16, torch.uint8
+
+
+class _Args:
+    """Checks every tensor of one call against the shape, dtype and device
+    the kernels assume.  The C ABI receives bare pointers and cannot see a
+    buffer's size, so a tensor of the wrong shape (say a packing made for
+    another T or C) would be read or written out of bounds on the device:
+    such calls raise here, before the library is called."""
+
+    def __init__(self, where, ref):
+        self.where = where
+        self.device = ref.device
+
+    def _common(self, t, name, dtype):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.where}: {name} must be a tensor, got {type(t).__name__}")
+        if t.dtype != dtype:
+            raise TypeError(f"{self.where}: {name} must be {dtype}, got {t.dtype}")
+        if t.device != self.device:
+            raise ValueError(f"{self.where}: {name} is on {t.device}, the inputs on {self.device}")
+
+    def shape(self, t, name, dtype, shape):
+        """t must have exactly this shape (None: t may be None)."""
+        if t is None:
+            raise ValueError(f"{self.where}: {name} is required")
+        self._common(t, name, dtype)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{self.where}: {name} has shape {tuple(t.shape)}, "
+                             f"expected {tuple(shape)}")
+
+    def opt(self, t, name, dtype, shape):
+        if t is not None:
+            self.shape(t, name, dtype, shape)
+
+    def room(self, t, name, dtype, n):
+        """t must be one-dimensional with at least n elements."""
+        if t is None:
+            raise ValueError(f"{self.where}: {name} is required")
+        self._common(t, name, dtype)
+        if t.dim() != 1 or t.numel() < n:
+            raise ValueError(f"{self.where}: {name} has shape {tuple(t.shape)}, expected "
+                             f"one dimension of at least {n} elements")
+
+    def bytes(self, t, name):
+        """A workspace: any dtype, on the inputs' device (its size is checked
+        by the library against the bytes it needs)."""
+        if t is None:
+            return
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.where}: {name} must be a tensor")
+        if t.device != self.device:
+            raise ValueError(f"{self.where}: {name} is on {t.device}, the inputs on {self.device}")
+
+
+def _dims2(t, name, where):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{where}: {name} must be a two-dimensional tensor")
+    return t.shape
+
+
+def _tiles(N, T, where):
+    if T <= 0 or N % T:
+        raise ValueError(f"{where}: N={N} is not a multiple of the tile width T={T}")
+    return N // T
 
 
 def _stream(stream):
@@ -135,10 +197,19 @@ def tw_ffn_workspace_bytes(M, K, N) -> int:
 
 def tw_pack_gate(x, wg_t, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_max, ws,
                  z_debug=None, stream=None, events=None) -> None:
-    M, K = x.shape
-    N = wg_t.shape[0]
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(wg_t, torch.bfloat16, "wg_t")
+    M, K = _dims2(x, "x", "tw_pack_gate")
+    N = _dims2(wg_t, "wg_t", "tw_pack_gate")[0]
+    NT = _tiles(N, T, "tw_pack_gate")
+    a = _Args("tw_pack_gate", x)
+    a.shape(x, "x", _BF16, (M, K))
+    a.shape(wg_t, "wg_t", _BF16, (N, K))
+    a.shape(tw_val, "tw_val", _F32, (M, NT, C))
+    a.shape(tw_idx, "tw_idx", _I32, (M, NT, C))
+    a.shape(tw_cnt, "tw_cnt", _I32, (M, NT))
+    a.room(ovf_rows, "ovf_rows", _I32, max(R_max, 1))
+    a.room(ovf_count, "ovf_count", _I32, 1)
+    a.opt(z_debug, "z_debug", _F32, (M, N))
+    a.bytes(ws, "ws")
     ev = _events(events)
     st = _lib.tw_pack_gate(_ptr(x), _ptr(wg_t), M, K, N, T, C, _ptr(tw_val), _ptr(tw_idx),
                            _ptr(tw_cnt), _ptr(ovf_rows), _ptr(ovf_count), R_max, _ptr(z_debug),
@@ -149,11 +220,20 @@ def tw_pack_gate(x, wg_t, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_m
 
 def tw_sparse_ffn_fwd(x, wg_t, wu_t, wd, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count,
                       R_max, y, ws, stream=None, events=None) -> None:
-    M, K = x.shape
-    N = wg_t.shape[0]
-    for t, n in ((x, "x"), (wg_t, "wg_t"), (wu_t, "wu_t"), (wd, "wd")):
-        _dtype(t, torch.bfloat16, n)
-    _dtype(y, torch.float32, "y")
+    M, K = _dims2(x, "x", "tw_sparse_ffn_fwd")
+    N = _dims2(wg_t, "wg_t", "tw_sparse_ffn_fwd")[0]
+    NT = _tiles(N, T, "tw_sparse_ffn_fwd")
+    a = _Args("tw_sparse_ffn_fwd", x)
+    a.shape(x, "x", _BF16, (M, K))
+    for t, n in ((wg_t, "wg_t"), (wu_t, "wu_t"), (wd, "wd")):
+        a.shape(t, n, _BF16, (N, K))
+    a.shape(tw_val, "tw_val", _F32, (M, NT, C))
+    a.shape(tw_idx, "tw_idx", _I32, (M, NT, C))
+    a.shape(tw_cnt, "tw_cnt", _I32, (M, NT))
+    a.room(ovf_rows, "ovf_rows", _I32, max(R_max, 1))
+    a.room(ovf_count, "ovf_count", _I32, 1)
+    a.shape(y, "y", _F32, (M, K))
+    a.bytes(ws, "ws")
     ev = _events(events)
     st = _lib.tw_sparse_ffn_fwd(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), M, K, N, T, C,
                                 _ptr(tw_val), _ptr(tw_idx), _ptr(tw_cnt), _ptr(ovf_rows),
@@ -164,11 +244,14 @@ def tw_sparse_ffn_fwd(x, wg_t, wu_t, wd, T, C, tw_val, tw_idx, tw_cnt, ovf_rows,
 
 
 def tw_ffn_fwd(x, wg_t, wu_t, wd, y, ws, stream=None, events=None) -> None:
-    M, K = x.shape
-    N = wg_t.shape[0]
-    for t, n in ((x, "x"), (wg_t, "wg_t"), (wu_t, "wu_t"), (wd, "wd")):
-        _dtype(t, torch.bfloat16, n)
-    _dtype(y, torch.float32, "y")
+    M, K = _dims2(x, "x", "tw_ffn_fwd")
+    N = _dims2(wg_t, "wg_t", "tw_ffn_fwd")[0]
+    a = _Args("tw_ffn_fwd", x)
+    a.shape(x, "x", _BF16, (M, K))
+    for t, n in ((wg_t, "wg_t"), (wu_t, "wu_t"), (wd, "wd")):
+        a.shape(t, n, _BF16, (N, K))
+    a.shape(y, "y", _F32, (M, K))
+    a.bytes(ws, "ws")
     ev = _events(events)
     st = _lib.tw_ffn_fwd(_ptr(x), _ptr(wg_t), _ptr(wu_t), _ptr(wd), M, K, N, _ptr(y), _ptr(ws),
                          ws.numel() * ws.element_size(), _stream(stream), ev[0] if ev else None)
@@ -176,11 +259,12 @@ def tw_ffn_fwd(x, wg_t, wu_t, wd, y, ws, stream=None, events=None) -> None:
 
 
 def tw_gate_dense(x, wg_t, z, stream=None, events=None) -> None:
-    M, K = x.shape
-    N = wg_t.shape[0]
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(wg_t, torch.bfloat16, "wg_t")
-    _dtype(z, torch.float32, "z")
+    M, K = _dims2(x, "x", "tw_gate_dense")
+    N = _dims2(wg_t, "wg_t", "tw_gate_dense")[0]
+    a = _Args("tw_gate_dense", x)
+    a.shape(x, "x", _BF16, (M, K))
+    a.shape(wg_t, "wg_t", _BF16, (N, K))
+    a.shape(z, "z", _F32, (M, N))
     ev = _events(events)
     st = _lib.tw_gate_dense(_ptr(x), _ptr(wg_t), M, K, N, _ptr(z), _stream(stream),
                             ev[0] if ev else None)
@@ -193,8 +277,16 @@ def tw_pack_dense_workspace_bytes(M, N) -> int:
 
 def tw_pack_dense(z, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_max, ws, stream=None,
                   events=None) -> None:
-    M, N = z.shape
-    _dtype(z, torch.float32, "z")
+    M, N = _dims2(z, "z", "tw_pack_dense")
+    NT = _tiles(N, T, "tw_pack_dense")
+    a = _Args("tw_pack_dense", z)
+    a.shape(z, "z", _F32, (M, N))
+    a.shape(tw_val, "tw_val", _F32, (M, NT, C))
+    a.shape(tw_idx, "tw_idx", _I32, (M, NT, C))
+    a.shape(tw_cnt, "tw_cnt", _I32, (M, NT))
+    a.room(ovf_rows, "ovf_rows", _I32, max(R_max, 1))
+    a.room(ovf_count, "ovf_count", _I32, 1)
+    a.bytes(ws, "ws")
     ev = _events(events)
     st = _lib.tw_pack_dense(_ptr(z), M, N, T, C, _ptr(tw_val), _ptr(tw_idx), _ptr(tw_cnt),
                             _ptr(ovf_rows), _ptr(ovf_count), R_max, _ptr(ws),
@@ -205,7 +297,17 @@ def tw_pack_dense(z, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_max, w
 
 def tw_hybrid_pack(T, C, tw_val, tw_idx, tw_cnt, P, hy_val, hy_idx, hy_cnt, route, bk_rows,
                    bk_count, R_max, stream=None, events=None) -> None:
-    M, NT = tw_cnt.shape
+    M, NT = _dims2(tw_cnt, "tw_cnt", "tw_hybrid_pack")
+    a = _Args("tw_hybrid_pack", tw_cnt)
+    a.shape(tw_cnt, "tw_cnt", _I32, (M, NT))
+    a.shape(tw_val, "tw_val", _F32, (M, NT, C))
+    a.shape(tw_idx, "tw_idx", _I32, (M, NT, C))
+    a.shape(hy_val, "hy_val", _F32, (M, P))
+    a.shape(hy_idx, "hy_idx", _I32, (M, P))
+    a.shape(hy_cnt, "hy_cnt", _I32, (M,))
+    a.shape(route, "route", _U8T, (M,))
+    a.room(bk_rows, "bk_rows", _I32, max(R_max, 1))
+    a.room(bk_count, "bk_count", _I32, 1)
     ev = _events(events)
     st = _lib.tw_hybrid_pack(M, NT * T, T, C, _ptr(tw_val), _ptr(tw_idx), _ptr(tw_cnt), P,
                              _ptr(hy_val), _ptr(hy_idx), _ptr(hy_cnt), _ptr(route), _ptr(bk_rows),
@@ -215,10 +317,24 @@ def tw_hybrid_pack(T, C, tw_val, tw_idx, tw_cnt, P, hy_val, hy_idx, hy_cnt, rout
 
 def tw_hybrid_up(x, wg_t, wu_t, P, hy_g, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max,
                  hy_u, hy_h, bk_g, bk_u, bk_h, stream=None, events=None) -> None:
-    M, K = x.shape
-    N = wg_t.shape[0]
-    for t, n in ((x, "x"), (wg_t, "wg_t"), (wu_t, "wu_t")):
-        _dtype(t, torch.bfloat16, n)
+    M, K = _dims2(x, "x", "tw_hybrid_up")
+    N = _dims2(wg_t, "wg_t", "tw_hybrid_up")[0]
+    R1 = max(R_max, 1)
+    a = _Args("tw_hybrid_up", x)
+    a.shape(x, "x", _BF16, (M, K))
+    a.shape(wg_t, "wg_t", _BF16, (N, K))
+    a.shape(wu_t, "wu_t", _BF16, (N, K))
+    a.shape(hy_g, "hy_g", _F32, (M, P))
+    a.shape(hy_idx, "hy_idx", _I32, (M, P))
+    a.shape(hy_cnt, "hy_cnt", _I32, (M,))
+    a.shape(route, "route", _U8T, (M,))
+    a.room(bk_rows, "bk_rows", _I32, R1)
+    a.room(bk_count, "bk_count", _I32, 1)
+    a.opt(hy_u, "hy_u", _F32, (M, P))
+    a.shape(hy_h, "hy_h", _F32, (M, P))
+    a.opt(bk_g, "bk_g", _BF16, (R1, N))
+    a.opt(bk_u, "bk_u", _BF16, (R1, N))
+    a.shape(bk_h, "bk_h", _BF16, (R1, N))
     ev = _events(events)
     st = _lib.tw_hybrid_up(_ptr(x), _ptr(wg_t), _ptr(wu_t), M, K, N, P, _ptr(hy_g), _ptr(hy_idx),
                            _ptr(hy_cnt), _ptr(route), _ptr(bk_rows), _ptr(bk_count), R_max,
@@ -233,9 +349,19 @@ def tw_hybrid_down_workspace_bytes(R_max) -> int:
 
 def tw_hybrid_down(wd, M, P, hy_h, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max, bk_h, y,
                    ws, stream=None, events=None) -> None:
-    N, K = wd.shape
-    _dtype(wd, torch.bfloat16, "wd")
-    _dtype(y, torch.float32, "y")
+    N, K = _dims2(wd, "wd", "tw_hybrid_down")
+    R1 = max(R_max, 1)
+    a = _Args("tw_hybrid_down", wd)
+    a.shape(wd, "wd", _BF16, (N, K))
+    a.shape(hy_h, "hy_h", _F32, (M, P))
+    a.shape(hy_idx, "hy_idx", _I32, (M, P))
+    a.shape(hy_cnt, "hy_cnt", _I32, (M,))
+    a.shape(route, "route", _U8T, (M,))
+    a.room(bk_rows, "bk_rows", _I32, R1)
+    a.room(bk_count, "bk_count", _I32, 1)
+    a.shape(bk_h, "bk_h", _BF16, (R1, N))
+    a.shape(y, "y", _F32, (M, K))
+    a.bytes(ws, "ws")
     ev = _events(events)
     nws = 0 if ws is None else ws.numel() * ws.element_size()
     st = _lib.tw_hybrid_down(_ptr(wd), M, K, N, P, _ptr(hy_h), _ptr(hy_idx), _ptr(hy_cnt),
@@ -250,10 +376,21 @@ def _nbytes(t):
 
 def tw_hybrid_bwd_dh(dy, wd, P, l1, hy_g, hy_u, hy_idx, hy_cnt, route, bk_rows, bk_count, R_max,
                      bk_g, bk_u, hy_du, hy_dz, bk_du, bk_dz, stream=None, events=None) -> None:
-    M, K = dy.shape
-    N = wd.shape[0]
-    _dtype(dy, torch.bfloat16, "dy")
-    _dtype(wd, torch.bfloat16, "wd")
+    M, K = _dims2(dy, "dy", "tw_hybrid_bwd_dh")
+    N = _dims2(wd, "wd", "tw_hybrid_bwd_dh")[0]
+    R1 = max(R_max, 1)
+    a = _Args("tw_hybrid_bwd_dh", dy)
+    a.shape(dy, "dy", _BF16, (M, K))
+    a.shape(wd, "wd", _BF16, (N, K))
+    for t, n in ((hy_g, "hy_g"), (hy_u, "hy_u"), (hy_du, "hy_du"), (hy_dz, "hy_dz")):
+        a.shape(t, n, _F32, (M, P))
+    a.shape(hy_idx, "hy_idx", _I32, (M, P))
+    a.shape(hy_cnt, "hy_cnt", _I32, (M,))
+    a.shape(route, "route", _U8T, (M,))
+    a.room(bk_rows, "bk_rows", _I32, R1)
+    a.room(bk_count, "bk_count", _I32, 1)
+    for t, n in ((bk_g, "bk_g"), (bk_u, "bk_u"), (bk_du, "bk_du"), (bk_dz, "bk_dz")):
+        a.shape(t, n, _BF16, (R1, N))
     ev = _events(events)
     st = _lib.tw_hybrid_bwd_dh(_ptr(dy), _ptr(wd), M, K, N, P, float(l1), _ptr(hy_g), _ptr(hy_u),
                                _ptr(hy_idx), _ptr(hy_cnt), _ptr(route), _ptr(bk_rows),
@@ -269,8 +406,22 @@ def tw_hybrid_bwd_dx_workspace_bytes(R_max) -> int:
 
 def tw_hybrid_bwd_dx(wg_t, wu_t, M, P, hy_du, hy_dz, hy_idx, hy_cnt, route, bk_rows, bk_count,
                      R_max, bk_du, bk_dz, dx, ws, stream=None, events=None) -> None:
-    N, K = wg_t.shape
-    _dtype(dx, torch.float32, "dx")
+    N, K = _dims2(wg_t, "wg_t", "tw_hybrid_bwd_dx")
+    R1 = max(R_max, 1)
+    a = _Args("tw_hybrid_bwd_dx", wg_t)
+    a.shape(wg_t, "wg_t", _BF16, (N, K))
+    a.shape(wu_t, "wu_t", _BF16, (N, K))
+    a.shape(hy_du, "hy_du", _F32, (M, P))
+    a.shape(hy_dz, "hy_dz", _F32, (M, P))
+    a.shape(hy_idx, "hy_idx", _I32, (M, P))
+    a.shape(hy_cnt, "hy_cnt", _I32, (M,))
+    a.shape(route, "route", _U8T, (M,))
+    a.room(bk_rows, "bk_rows", _I32, R1)
+    a.room(bk_count, "bk_count", _I32, 1)
+    a.shape(bk_du, "bk_du", _BF16, (R1, N))
+    a.shape(bk_dz, "bk_dz", _BF16, (R1, N))
+    a.shape(dx, "dx", _F32, (M, K))
+    a.bytes(ws, "ws")
     ev = _events(events)
     st = _lib.tw_hybrid_bwd_dx(_ptr(wg_t), _ptr(wu_t), M, K, N, P, _ptr(hy_du), _ptr(hy_dz),
                                _ptr(hy_idx), _ptr(hy_cnt), _ptr(route), _ptr(bk_rows),
@@ -286,10 +437,24 @@ def tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max) -> int:
 def tw_hybrid_bwd_dw(x, dy, P, hy_h, hy_du, hy_dz, hy_idx, hy_cnt, route, bk_rows, bk_count,
                      R_max, bk_h, bk_du, bk_dz, dwg_t, dwu_t, dwd, ws, stream=None,
                      events=None) -> None:
-    M, K = x.shape
-    N = dwd.shape[0]
-    _dtype(x, torch.bfloat16, "x")
-    _dtype(dy, torch.bfloat16, "dy")
+    M, K = _dims2(x, "x", "tw_hybrid_bwd_dw")
+    N = _dims2(dwd, "dwd", "tw_hybrid_bwd_dw")[0]
+    R1 = max(R_max, 1)
+    a = _Args("tw_hybrid_bwd_dw", x)
+    a.shape(x, "x", _BF16, (M, K))
+    a.shape(dy, "dy", _BF16, (M, K))
+    for t, n in ((hy_h, "hy_h"), (hy_du, "hy_du"), (hy_dz, "hy_dz")):
+        a.shape(t, n, _F32, (M, P))
+    a.shape(hy_idx, "hy_idx", _I32, (M, P))
+    a.shape(hy_cnt, "hy_cnt", _I32, (M,))
+    a.shape(route, "route", _U8T, (M,))
+    a.room(bk_rows, "bk_rows", _I32, R1)
+    a.room(bk_count, "bk_count", _I32, 1)
+    for t, n in ((bk_h, "bk_h"), (bk_du, "bk_du"), (bk_dz, "bk_dz")):
+        a.shape(t, n, _BF16, (R1, N))
+    for t, n in ((dwg_t, "dwg_t"), (dwu_t, "dwu_t"), (dwd, "dwd")):
+        a.shape(t, n, _F32, (N, K))
+    a.bytes(ws, "ws")
     ev = _events(events)
     st = _lib.tw_hybrid_bwd_dw(_ptr(x), _ptr(dy), M, K, N, P, _ptr(hy_h), _ptr(hy_du),
                                _ptr(hy_dz), _ptr(hy_idx), _ptr(hy_cnt), _ptr(route),

@@ -145,7 +145,8 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t,
  *
  * tw_gate_dense: z = x W_g as fp32 [M][N] (the same kernel and arithmetic
  * as tw_pack_gate, so z is bitwise tw_pack_gate's z_debug).  K and N
- * multiples of 128.  events: [0] before, [1] after the kernel.
+ * multiples of 128, K <= 4096, M * K < 2^31 (tw_pack_gate's limits; other
+ * shapes return TW_EUNSUPPORTED).  events: [0] before, [1] after the kernel.
  *
  * tw_pack_dense: TwELL packing and overflow routing of any fp32 gate z
  * [M][N] (active means z > 0), with exactly the outputs and conventions of
@@ -206,7 +207,8 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
  * bf16 and, when the down projection splits, the partial sums:
  * ws_bytes >= tw_ffn_workspace_bytes.
  * Shapes: M >= 0, K and N positive multiples of 128, N * K < 2^31 (each
- * weight matrix under 4 GiB: 32-bit buffer offsets).
+ * weight matrix under 4 GiB: 32-bit buffer offsets).  The workspace query
+ * returns 0 for any other shape.
  */
 size_t tw_ffn_workspace_bytes(int M, int K, int N);
 tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
@@ -247,7 +249,8 @@ tw_status tw_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
  * Shapes: as for tw_pack_gate (T in {128, 256}, N a multiple of T, N/T <=
  * 256, 1 <= C <= T, K a multiple of 128 and at most 4096, M*K < 2^31), and
  * N a multiple of 128, 1 <= P <= N, 0 <= R_max <= M, N*K < 2^31,
- * R_max*N < 2^31.
+ * R_max*N < 2^31, and M*P < 2^31 (the kernels name a stored slot by the
+ * 32-bit id m*P + s); other shapes return TW_EUNSUPPORTED.
  */
 
 /*
@@ -359,7 +362,8 @@ tw_status tw_hybrid_bwd_dx(const uint16_t *wg_t, const uint16_t *wu_t, int M, in
  * (dwd += bk_h^T dy, dwu_t += bk_du^T x, dwg_t += bk_dz^T x over the backup
  * slots).  Results are bit-identical run to run.  ws_bytes >=
  * tw_hybrid_bwd_dw_workspace_bytes(M, K, N, P, R_max) (about 16 M P +
- * 4 R_max K bytes); M P < 2^31.  events: [0] before, [1] after the
+ * 4 R_max K bytes; 0 for a shape this call rejects).  events: [0] before,
+ * [1] after the
  * transpose, [2] after the sparse rows' gradients, [3] after the backup
  * rows' products.
  */

@@ -121,6 +121,8 @@ def test_unfused_entry_points_reject(tw):
     assert L.tw_gate_dense(P, P, 64, 256, 1000, P, None, None) == 2   # N not a multiple of 128
     assert L.tw_gate_dense(None, P, 64, 256, 1024, P, None, None) == 1
     assert L.tw_gate_dense(P, P, 64, 256, 1024, P + 4, None, None) == 1
+    assert L.tw_gate_dense(P, P, 64, 8192, 1024, P, None, None) == 2      # K above 4096
+    assert L.tw_gate_dense(P, P, 1 << 20, 4096, 1024, P, None, None) == 2  # x of 4 GiB or more
     assert L.tw_pack_dense_workspace_bytes(64, 1024) >= 4 * 4
     ws = L.tw_pack_dense_workspace_bytes(64, 1024)
     # z, M, N, T, C, val, idx, cnt, ovf_rows, ovf_count, R_max, ws, ws_bytes, stream, events
@@ -143,11 +145,15 @@ def test_hybrid_entry_points_reject(tw):
     assert H(route=None) == 1 and H(route=P + 1) == 1 and H(bk=None) == 1 and H(hv=None) == 1
     # backup rows of 4 GiB or more are outside the 32-bit buffer offsets
     assert H(M=1 << 17, N=1 << 15, R=1 << 17) == 2
+    # more stored slots than the kernels' 32-bit slot ids m * P + s can name
+    assert H(M=1 << 20, N=4096, cap=4096, R=0) == 2
 
     def U(K=256, cap=128, R=8, hy_h=P, bk_h=P, hy_u=None):
         return L.tw_hybrid_up(P, P, P, 64, K, 1024, cap, P, P, P, P, P, P, R, hy_u, hy_h, None,
                               None, bk_h, None, None)
     assert U(K=100) == 2 and U(cap=0) == 1 and U(hy_h=None) == 1
+    assert L.tw_hybrid_up(P, P, P, 1 << 20, 256, 4096, 4096, P, P, P, P, P, P, 0, None, P, None,
+                          None, P, None, None) == 2  # M * P >= 2^31 slot ids
     assert U(bk_h=None) == 1 and U(hy_u=P + 4) == 1
 
     nws = L.tw_hybrid_down_workspace_bytes(8)
