@@ -81,7 +81,7 @@ def check_gate_bound(z_gpu_rows: np.ndarray, z_ref_rows: np.ndarray, x_rows, wg_
 
 
 def check_index_parity(g: dict, rows: np.ndarray, z_ref_rows: np.ndarray, T: int, C: int) -> None:
-    """GPU packing vs the oracle's own gate on sampled rows, outside the band."""
+    """GPU packing vs the oracle's own gate on the given rows, outside the band."""
     M_s, N = z_ref_rows.shape
     NT = N // T
     zt = z_ref_rows.reshape(M_s, NT, T)
@@ -89,27 +89,58 @@ def check_index_parity(g: dict, rows: np.ndarray, z_ref_rows: np.ndarray, T: int
     hi = (zt > -BAND).sum(axis=2)
     cnt = g["tw_cnt"][rows]
     assert np.all((cnt >= lo) & (cnt <= hi)), "count outside the band's range"
+    ids = g["tw_idx"][rows]                                    # [M_s][NT][C]
+    used = np.arange(C)[None, None, :] < np.minimum(cnt, C)[:, :, None]
+    if C > 1:
+        assert np.all(np.diff(ids, axis=2)[used[:, :, 1:]] > 0), "indices not ascending"
+    t0 = (np.arange(NT) * T)[None, :, None]
+    assert np.all(((ids >= t0) & (ids < t0 + T))[used]), "index outside its tile"
+    # tiles whose whole active set was stored (at most C even at the band's
+    # top): the stored set equals the firmly active columns, up to columns
+    # inside the band
+    stored = np.zeros((M_s, N), dtype=bool)
+    r_i, t_i, s_i = np.nonzero(used)
+    stored[r_i, ids[r_i, t_i, s_i]] = True
+    whole = np.repeat(hi <= C, T, axis=1)                      # [M_s][N]
     firm = np.abs(z_ref_rows) >= BAND
-    for r_i, m in enumerate(rows):
-        for t in range(NT):
-            n = min(int(cnt[r_i, t]), C)
-            ids = g["tw_idx"][m, t, :n]
-            assert np.all(np.diff(ids) > 0), "indices not ascending"
-            assert np.all((ids >= t * T) & (ids < (t + 1) * T)), "index outside its tile"
-            if hi[r_i, t] <= C:  # the whole tile's active set was stored
-                cols = np.arange(t * T, (t + 1) * T)
-                want = set(cols[(z_ref_rows[r_i, t * T:(t + 1) * T] > 0) & firm[r_i, t * T:(t + 1) * T]])
-                got = set(ids.tolist())
-                assert want <= got, "a firmly active column is missing"
-                extra = got - want
-                assert all(abs(z_ref_rows[r_i, j]) < BAND for j in extra), "a firmly inactive column was packed"
+    want = (z_ref_rows > 0) & firm
+    assert not np.any(want & ~stored & whole), "a firmly active column is missing"
+    assert not np.any(stored & ~want & firm & whole), "a firmly inactive column was packed"
     # overflow status on determined rows
     over_gpu = np.isin(rows, g["ovf_rows"][: min(g["ovf_count"], len(g["ovf_rows"]))]) | \
-        (g["tw_cnt"][rows] > C).any(axis=1)
+        (cnt > C).any(axis=1)
     surely_over = (lo > C).any(axis=1)
     surely_not = (hi <= C).all(axis=1)
     assert np.all(over_gpu[surely_over]), "row that must overflow did not"
     assert not np.any(over_gpu[surely_not]), "row that cannot overflow did"
+
+
+def check_gate_rows(g: dict, d: dict, T: int, C: int, chunk: int = 2048) -> int:
+    """The GPU gate of every row against the oracle's float64 gate (the
+    2 gamma_K bound) and the GPU packing against it (index parity), in
+    blocks of rows so that the float64 gate of a large batch is never held
+    whole.  Returns the number of rows checked."""
+    orc = oracle.default()
+    M = g["z"].shape[0]
+    for r0 in range(0, M, chunk):
+        rows = np.arange(r0, min(r0 + chunk, M))
+        z_ref = orc.gate(d["x"][rows], d["wg_t"])
+        check_gate_bound(g["z"][rows], z_ref, d["x"][rows], d["wg_t"])
+        check_index_parity(g, rows, z_ref, T, C)
+    return M
+
+
+_DENSE_REF = {}
+
+
+def dense_reference(w, d: dict) -> np.ndarray:
+    """The oracle's dense block output y_ref [M][K] (float64) for workload
+    ``w`` (inputs ``d`` = synth.make_inputs(w)), computed once per test
+    session: several full-size tests compare against the same block."""
+    key = w.with_(T=0, C=0)  # the inputs do not depend on the tile shape
+    if key not in _DENSE_REF:
+        _DENSE_REF[key] = oracle.default().dense_ffn(d["x"], d["wg_t"], d["wu_t"], d["wd"])
+    return _DENSE_REF[key]
 
 
 def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what="y") -> float:

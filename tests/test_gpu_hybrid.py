@@ -104,8 +104,9 @@ def _sub_hybrid(g, rows):
     return hy, listed, gslots
 
 
-def _check_values(g, d, rows, w):
-    """Up values, backup rows and y on `rows` against the oracle."""
+def _check_values(g, d, rows, w, y_ref=None):
+    """Up values, backup rows and y on `rows` against the oracle (y_ref: the
+    oracle's dense output of those rows, if already computed)."""
     orc = oracle.default()
     x = d["x"][rows]
     hy, listed, gslots = _sub_hybrid(g, rows)
@@ -129,18 +130,16 @@ def _check_values(g, d, rows, w):
         assert np.all(np.abs(g["hy_u"][m, :n] - u_ref) <= bu), f"hy_u row {m}"
         bh = gv * bu + 2 * U24 * np.abs(u_ref * gv) + 1e-30
         assert np.all(np.abs(g["hy_h"][m, :n] - u_ref * gv) <= bh), f"hy_h row {m}"
-    # backup rows: dense bf16 g, u, h
-    for i, r in zip(listed, gslots):
-        bz = 2 * gamma * (xa[i] @ wga.T)
-        bu = 2 * gamma * (xa[i] @ wua.T)
-        k = hy["bk_rows"].tolist().index(i)
-        g_ref, u_ref, h_ref = up["bk_g"][k], up["bk_u"][k], up["bk_h"][k]
-        assert np.all(np.abs(g["bk_g"][r] - g_ref) <= bz + BF * (g_ref + bz)), f"bk_g row {rows[i]}"
-        assert np.all(np.abs(g["bk_u"][r] - u_ref) <= bu + BF * (np.abs(u_ref) + bu)), \
-            f"bk_u row {rows[i]}"
+    # backup rows: dense bf16 g, u, h (the subset's backup slot k is listed[k])
+    if listed:
+        bz = 2 * gamma * (xa[listed] @ wga.T)
+        bu = 2 * gamma * (xa[listed] @ wua.T)
+        g_ref, u_ref, h_ref = up["bk_g"], up["bk_u"], up["bk_h"]
+        gg, gu, gh = g["bk_g"][gslots], g["bk_u"][gslots], g["bk_h"][gslots]
+        assert np.all(np.abs(gg - g_ref) <= bz + BF * (g_ref + bz)), "bk_g"
+        assert np.all(np.abs(gu - u_ref) <= bu + BF * (np.abs(u_ref) + bu)), "bk_u"
         dh = g_ref * bu + np.abs(u_ref) * bz + bz * bu
-        assert np.all(np.abs(g["bk_h"][r] - h_ref) <= dh + BF * (np.abs(h_ref) + dh) + 1e-30), \
-            f"bk_h row {rows[i]}"
+        assert np.all(np.abs(gh - h_ref) <= dh + BF * (np.abs(h_ref) + dh) + 1e-30), "bk_h"
     # the down product of the GPU's own h, and the block output
     bk_h = g["bk_h"][gslots] if gslots else np.zeros((0, w.N))
     y_own = orc.hybrid_down(d["wd"], hy, g["hy_h"][rows].astype(np.float64), bk_h)
@@ -156,7 +155,8 @@ def _check_values(g, d, rows, w):
         h_abs[i] = np.abs(bk_h[k])
     bound = 2 * gamma_n * (h_abs @ wda) + 1e-30
     assert np.all(np.abs(g["y"][rows][done] - y_own[done]) <= bound[done]), "down product"
-    y_ref = orc.dense_ffn(x, d["wg_t"], d["wu_t"], d["wd"])
+    if y_ref is None:
+        y_ref = orc.dense_ffn(x, d["wg_t"], d["wu_t"], d["wd"])
     parity.check_y(g["y"][rows][done], y_ref[done], "hybrid y")
     # rows routed to the backup but past its room keep the NaN prefill
     assert np.all(np.isnan(g["y"][rows][~done])), "a row past the backup room was written"
@@ -194,25 +194,25 @@ def test_hybrid_parity(tw, name, kw, P, R_max):
 @pytest.mark.parametrize("name", ["ffn-0.5b", "ffn-1b", "ffn-2b", "ffn-ovf", "ffn-paper"])
 def test_hybrid_full_size(tw, name):
     """Full shapes at the static capacities (P = 128, backup room M / 8):
-    the whole conversion bit-exact, values and y on sampled rows (every
-    backup row among them up to a cap, plus random sparse rows)."""
+    the whole conversion bit-exact, and the up values, the backup rows and
+    y of every row against the oracle (in blocks of rows)."""
     w = W[name]
     P, R_max = 128, w.M // 8
     print(f"case {w} P={P} R_max={R_max}", flush=True)
     d = synth.make_inputs(w)
     dev = parity.upload(d)
     g = _run(tw, dev, w, P, R_max)
+    del dev
     ref, _ = _check_pack(g, w.C, P, R_max)
     assert ref["bk_count"] <= R_max, "the static backup room overflowed at this workload"
-    rng = np.random.default_rng(7)
-    bk = g["bk_rows"][:min(g["bk_count"], R_max)]
-    sparse_rows = np.nonzero(g["route"] == 0)[0]
-    rows = np.union1d(rng.choice(bk, size=min(24, len(bk)), replace=False) if len(bk) else [],
-                      rng.choice(sparse_rows, size=min(64, len(sparse_rows)), replace=False))
-    rows = np.concatenate([rows, [0, w.M - 1]])
-    rows = np.unique(rows.astype(np.int64))
-    done, left = _check_values(g, d, rows, w)
-    assert left == 0
+    y_ref = parity.dense_reference(w, d)
+    done = left = 0
+    for r0 in range(0, w.M, 2048):
+        rows = np.arange(r0, min(r0 + 2048, w.M))
+        a, b = _check_values(g, d, rows, w, y_ref[rows])
+        done, left = done + a, left + b
+    assert done == w.M and left == 0
+    print(f"all {w.M} rows ({ref['bk_count']} backup rows)", flush=True)
 
 
 def test_hybrid_forward_wrapper(tw):
