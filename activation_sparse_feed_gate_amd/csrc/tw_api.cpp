@@ -6,6 +6,7 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "tw_internal.hpp"
 
@@ -114,6 +115,90 @@ tw_status launched(hipError_t e, const char *what) {
         if (M > 0 || (p)) TW_NEED(p);                                                \
     } while (0)
 
+
+// Argument checks of tw_pack_gate and tw_pack_gate_noalloc (all but the
+// workspace).
+tw_status check_pack_args(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int T,
+                          int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                          int32_t *ovf_rows, int32_t *ovf_count, int R_max, float *z_debug) {
+    TW_TRY(check_shape(M, K, N, T, C, R_max));
+    TW_NEED_M(x);
+    TW_NEED(wg_t);
+    TW_NEED_M(tw_val);
+    TW_NEED_M(tw_idx);
+    TW_NEED_M(tw_cnt);
+    TW_NEED(ovf_rows);
+    TW_NEED(ovf_count);
+    if (z_debug && !aligned16(z_debug)) return fail(TW_EINVAL, "z_debug is not 16-byte aligned");
+    return TW_OK;
+}
+
+// The gate kernel and the compaction on a workspace of at least
+// gate_ws(M, K, N) bytes: row-overflow bits, then the small-batch gate's
+// partial gates.  Every word of it that a kernel reads is written earlier in
+// the same call, so it needs no clearing.
+tw_status pack_gate_launch(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, int T,
+                           int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                           int32_t *ovf_rows, int32_t *ovf_count, int R_max, float *z_debug,
+                           void *ws, void *stream, void *const *events) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t *oflag = static_cast<uint32_t *>(ws);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + pack_ws(M, N));
+    TW_TRY(record(events, 0, s));
+    TW_TRY(launched(tw::launch_gate_twell(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, oflag,
+                                          z_debug, part, s),
+                    "gate_twell launch"));
+    TW_TRY(record(events, 1, s));
+    TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_flag_blocks(M, N, T), tw::row_words(M),
+                                           R_max, ovf_rows, ovf_count, s),
+                    "ovf_compact launch"));
+    TW_TRY(record(events, 2, s));
+    return TW_OK;
+}
+
+// ---- scratch of the entry point that allocates nothing --------------------
+// tw_pack_gate_noalloc serves callers that cannot allocate (code under HIP
+// graph capture, tight serving loops): its workspace is this file-scope
+// device array, of which every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address is taken once per device with
+// hipGetSymbolAddress (with that device current) and only that address is
+// ever handed to a kernel.  Every call on one GPU shares that GPU's copy, so
+// calls that overlap on one GPU (two streams, two threads) race.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device.
+tw_status scratch_ptr(void **out) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TW_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(TW_EUNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess)
+        return fail(TW_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                    hipGetErrorString(g_scratch_err[dev]));
+    if (!g_scratch_ptr[dev]) return fail(TW_EHIP, "no device address for scratch on device %d", dev);
+    *out = g_scratch_ptr[dev];
+    return TW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,33 +237,35 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t, int M, int K, in
                        int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
                        int32_t *ovf_rows, int32_t *ovf_count, int R_max, float *z_debug,
                        void *ws, size_t ws_bytes, void *stream, void *const *events) {
-    TW_TRY(check_shape(M, K, N, T, C, R_max));
-    TW_NEED_M(x);
-    TW_NEED(wg_t);
-    TW_NEED_M(tw_val);
-    TW_NEED_M(tw_idx);
-    TW_NEED_M(tw_cnt);
-    TW_NEED(ovf_rows);
-    TW_NEED(ovf_count);
+    TW_TRY(check_pack_args(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count,
+                           R_max, z_debug));
     TW_NEED(ws);
-    if (z_debug && !aligned16(z_debug)) return fail(TW_EINVAL, "z_debug is not 16-byte aligned");
     const size_t need = tw_workspace_bytes(M, K, N, T, C, R_max);
     if (ws_bytes < need) return fail(TW_EINVAL, "workspace %zu bytes < %zu needed", ws_bytes, need);
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    uint32_t *oflag = static_cast<uint32_t *>(ws);
-    float *part = reinterpret_cast<float *>(static_cast<char *>(ws) + pack_ws(M, N));
-    TW_TRY(record(events, 0, s));
-    TW_TRY(launched(tw::launch_gate_twell(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, oflag,
-                                          z_debug, part, s),
-                    "gate_twell launch"));
-    TW_TRY(record(events, 1, s));
-    TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_flag_blocks(M, N, T), tw::row_words(M),
-                                           R_max, ovf_rows, ovf_count, s),
-                    "ovf_compact launch"));
-    TW_TRY(record(events, 2, s));
-    return TW_OK;
+    return pack_gate_launch(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count,
+                            R_max, z_debug, ws, stream, events);
 }
+
+// The variant that allocates nothing: tw_pack_gate's kernels on the
+// per-device file-scope scratch array (see the top of this file).
+tw_status tw_pack_gate_noalloc(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N,
+                               int T, int C, float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                               int32_t *ovf_rows, int32_t *ovf_count, int R_max, float *z_debug,
+                               void *stream, void *const *events) {
+    TW_TRY(check_pack_args(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count,
+                           R_max, z_debug));
+    const size_t need = gate_ws(M, K, N);
+    if (need > kScratchBytes)
+        return fail(TW_EUNSUPPORTED,
+                    "M=%d K=%d N=%d needs %zu bytes of workspace; tw_pack_gate_noalloc's "
+                    "static scratch holds %zu (use tw_pack_gate with a workspace)",
+                    M, K, N, need, kScratchBytes);
+    void *ws = nullptr;
+    TW_TRY(scratch_ptr(&ws));
+    return pack_gate_launch(x, wg_t, M, K, N, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count,
+                            R_max, z_debug, ws, stream, events);
+}
+
 
 tw_status tw_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int K, int N, float *z,
                         void *stream, void *const *events) {

@@ -6,7 +6,8 @@ Importing this module fails loudly when the library has not been built
 (``python -m activation_sparse_feed_gate_amd.build``); there is no fallback.
 
 Low-level functions carry the C names and take preallocated tensors:
-``tw_pack_gate``, ``tw_sparse_ffn_fwd``, ``tw_ffn_fwd``, ``tw_workspace_bytes``,
+``tw_pack_gate`` (and ``tw_pack_gate_noalloc``, which takes no workspace),
+``tw_sparse_ffn_fwd``, ``tw_ffn_fwd``, ``tw_workspace_bytes``,
 ``tw_ffn_workspace_bytes``, ``tw_gate_dense``, ``tw_pack_dense`` and the
 hybrid training storage ``tw_hybrid_pack``, ``tw_hybrid_up``,
 ``tw_hybrid_down`` with its backward ``tw_hybrid_bwd_dh``, ``tw_hybrid_bwd_dx``,
@@ -45,6 +46,9 @@ _lib.tw_ffn_workspace_bytes.argtypes = [_i] * 3
 _lib.tw_pack_gate.restype = _i
 _lib.tw_pack_gate.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
                               _vp, _sz, _vp, _vp]
+_lib.tw_pack_gate_noalloc.restype = _i
+_lib.tw_pack_gate_noalloc.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i,
+                                      _vp, _vp, _vp]
 _lib.tw_sparse_ffn_fwd.restype = _i
 _lib.tw_sparse_ffn_fwd.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
                                    _vp, _i, _vp, _vp, _sz, _vp, _vp]
@@ -216,6 +220,28 @@ def tw_pack_gate(x, wg_t, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_m
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
                            ev[0] if ev else None)
     _check(st, "tw_pack_gate")
+
+
+def tw_pack_gate_noalloc(x, wg_t, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_max,
+                         z_debug=None, stream=None, events=None) -> None:
+    """tw_pack_gate on the library's static per-GPU scratch (no workspace)."""
+    M, K = _dims2(x, "x", "tw_pack_gate_noalloc")
+    N = _dims2(wg_t, "wg_t", "tw_pack_gate_noalloc")[0]
+    NT = _tiles(N, T, "tw_pack_gate_noalloc")
+    a = _Args("tw_pack_gate_noalloc", x)
+    a.shape(x, "x", _BF16, (M, K))
+    a.shape(wg_t, "wg_t", _BF16, (N, K))
+    a.shape(tw_val, "tw_val", _F32, (M, NT, C))
+    a.shape(tw_idx, "tw_idx", _I32, (M, NT, C))
+    a.shape(tw_cnt, "tw_cnt", _I32, (M, NT))
+    a.room(ovf_rows, "ovf_rows", _I32, max(R_max, 1))
+    a.room(ovf_count, "ovf_count", _I32, 1)
+    a.opt(z_debug, "z_debug", _F32, (M, N))
+    ev = _events(events)
+    st = _lib.tw_pack_gate_noalloc(_ptr(x), _ptr(wg_t), M, K, N, T, C, _ptr(tw_val),
+                                   _ptr(tw_idx), _ptr(tw_cnt), _ptr(ovf_rows), _ptr(ovf_count),
+                                   R_max, _ptr(z_debug), _stream(stream), ev[0] if ev else None)
+    _check(st, "tw_pack_gate_noalloc")
 
 
 def tw_sparse_ffn_fwd(x, wg_t, wu_t, wd, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count,

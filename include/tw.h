@@ -136,6 +136,27 @@ tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t,
                        void *stream, void *const *events);
 
 /*
+ * tw_pack_gate without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same kernels, arguments, outputs and
+ * error behaviour as tw_pack_gate; the workspace is instead a static device
+ * array inside the library of 16 MiB per GPU (held by every GPU the library
+ * runs on until the process ends; its address is looked up once per device,
+ * on the first call there).  Shapes whose tw_pack_gate workspace would
+ * exceed it (row-overflow bits of (N/128) * ceil(M/32) words, plus for a few
+ * token rows the small-batch gate's partial gates) return TW_EUNSUPPORTED
+ * with a message giving the bytes needed.  The call allocates nothing.  All
+ * calls on one GPU share that GPU's array, so calls that overlap on one GPU
+ * (on two streams, or from two host threads) race; calls in stream order do
+ * not.  Nothing in the array needs to start at zero.
+ */
+tw_status tw_pack_gate_noalloc(const uint16_t *x, const uint16_t *wg_t,
+                               int M, int K, int N, int T, int C,
+                               float *tw_val, int32_t *tw_idx, int32_t *tw_cnt,
+                               int32_t *ovf_rows, int32_t *ovf_count, int R_max,
+                               float *z_debug, void *stream, void *const *events);
+
+/*
  * The unfused alternative to tw_pack_gate, in two calls: section 3-4
  * contrasts packing in the gate's epilogue with computing the dense gate,
  * writing it to memory and packing it in a separate pass (an extra write,

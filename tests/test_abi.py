@@ -193,3 +193,17 @@ def test_hybrid_backward_entry_points_reject(tw):
     # more stored entries than 32-bit entry ids can name
     assert DW(M=1 << 20, N=1 << 15, cap=1 << 12, R=0, nb=1 << 62) == 2
     assert tw._lib.tw_last_error()
+
+
+def test_pack_gate_noalloc_rejects(tw):
+    """The entry point without a workspace: the shape checks of tw_pack_gate,
+    and shapes whose workspace would not fit its 16 MiB static scratch
+    (here 32 MiB of row-overflow bits) rejected before anything runs."""
+    L = tw._lib
+
+    def NA(M=64, K=256, N=1024, T=128, C=16, R=64, x=P):
+        return L.tw_pack_gate_noalloc(x, P, M, K, N, T, C, P, P, P, P, P, R, None, None, None)
+    assert NA(T=64) == 2 and NA(C=0) == 1 and NA(R=65) == 1 and NA(x=None) == 1
+    assert NA(x=P + 8) == 1 and NA(K=192) == 2
+    assert NA(M=524287, K=4096, N=65536, T=256, R=0) == 2
+    assert b"static scratch" in L.tw_last_error()
