@@ -194,27 +194,24 @@ def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, st
         hstep(evl[i])
     torch.cuda.synchronize()
     t_eager = (time.perf_counter() - t0) / Ks
-    if not args.no_graph:
-        G = max(1, min(args.graph_steps, Ks))
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for _ in range(G):
-                    hstep(st=None)
-        torch.cuda.current_stream().wait_stream(cap)
+    G = max(1, min(args.graph_steps, Ks))
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(G):
+                hstep(st=None)
+    torch.cuda.current_stream().wait_stream(cap)
+    g.replay()
+    n_rep = max(1, Ks // G)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_rep):
         g.replay()
-        n_rep = max(1, Ks // G)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n_rep):
-            g.replay()
-        torch.cuda.synchronize()
-        t_h = (time.perf_counter() - t0) / (n_rep * G)
-        del g
-    else:
-        t_h = t_eager
+    torch.cuda.synchronize()
+    t_h = (time.perf_counter() - t0) / (n_rep * G)
+    del g
 
     def avg(j, i):
         return sum(hev.ms(e[j][i], e[j][i + 1]) for e in evl) / len(evl) * 1e-3
@@ -327,26 +324,24 @@ def hybrid_backward_bench(args, tw, torch, w, x, wg, wu, wdn, hy, Rh, P, hev):
         bstep(evl[i])
     torch.cuda.synchronize()
     t_eager = (time.perf_counter() - t0) / Ks
-    t_b = t_eager
-    if not args.no_graph:
-        G = max(1, min(args.graph_steps, Ks))
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for _ in range(G):
-                    bstep(st=None)
-        torch.cuda.current_stream().wait_stream(cap)
+    G = max(1, min(args.graph_steps, Ks))
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for _ in range(G):
+                bstep(st=None)
+    torch.cuda.current_stream().wait_stream(cap)
+    g.replay()
+    n_rep = max(1, Ks // G)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_rep):
         g.replay()
-        n_rep = max(1, Ks // G)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n_rep):
-            g.replay()
-        torch.cuda.synchronize()
-        t_b = (time.perf_counter() - t0) / (n_rep * G)
-        del g
+    torch.cuda.synchronize()
+    t_b = (time.perf_counter() - t0) / (n_rep * G)
+    del g
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(Ks):
@@ -370,53 +365,104 @@ def hybrid_backward_bench(args, tw, torch, w, x, wg, wu, wdn, hy, Rh, P, hev):
                     "the same backward on torch.matmul from dense bf16 g and u"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ffn-0.5b")
-    ap.add_argument("--density", type=float, default=None, help="override the target density")
-    ap.add_argument("--M", type=int, default=None,
-                    help="override the token count (decode-like batches)")
-    ap.add_argument("--r-max", type=int, default=None,
-                    help="overflow-row capacity (default: an eighth of the batch, grown by "
-                         "the retry rule before timing)")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
-                    help="also run a plain elementwise copy of MB megabytes (fp32, read + "
-                         "write) so that a counter profile can scale FETCH_SIZE/WRITE_SIZE")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time eager launches instead of HIP-graph replays")
-    ap.add_argument("--no-fusion-ablation", dest="fusion_ablation", action="store_false",
-                    help="skip timing the unfused gate + pack path")
-    ap.add_argument("--no-hybrid", dest="hybrid", action="store_false",
-                    help="skip the hybrid training-forward measurement")
-    ap.add_argument("--cold-steps", type=int, default=20,
-                    help="replays for the Infinity-Cache-cold line (0: skip it)")
-    ap.add_argument("--graph-steps", type=int, default=5,
-                    help="consecutive steps captured in one HIP graph (1: a graph launch "
-                         "per step)")
-    args = ap.parse_args()
+# Workloads measured besides the headline (SURVEY's headline set: every block
+# at >= 99% sparsity, and the 2B shape at 0% and 5% density for the crossover).
+SIDE_CONFIGS = [("ffn-1b", None), ("ffn-2b", None), ("ffn-ovf", None), ("ffn-2b", 0.0),
+                ("ffn-2b", 0.05)]
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
-              f"{world}): the path is data-parallel over tokens with no exchange, so N GPUs "
-              f"run N independent copies; no multi-GPU figure is produced.", file=sys.stderr)
-        sys.exit(2)
 
+class ClockSampler:
+    """Current shader (sclk) and memory (mclk) clocks of the GPU, sampled
+    from the amdgpu driver's sysfs DPM tables (the level marked '*') on a
+    background thread while the timed loops run."""
+
+    def __init__(self, torch):
+        import glob
+        import threading
+
+        self.card = None
+        self.why = "no amdgpu DPM clock table under /sys/class/drm"
+        bus = None
+        try:
+            p = torch.cuda.get_device_properties(0)
+            bus = "%04x:%02x:%02x" % (p.pci_domain_id, p.pci_bus_id, p.pci_device_id)
+        except Exception:
+            pass
+        cards = [c for c in sorted(glob.glob("/sys/class/drm/card*/device"))
+                 if os.path.exists(os.path.join(c, "pp_dpm_sclk"))]
+        for c in cards:
+            try:
+                slot = open(os.path.join(c, "uevent")).read()
+            except OSError:
+                continue
+            if bus and bus in slot.lower():
+                self.card = c
+        if self.card is None and len(cards) == 1:
+            self.card = cards[0]
+        if self.card is None and cards:
+            self.why = f"{len(cards)} cards, none matching PCI {bus}"
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._threading = threading
+
+    @staticmethod
+    def _level(path):
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    v = line.split(":", 1)[1].strip().rstrip("*").strip().lower()
+                    return float(v.replace("mhz", "").strip())
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                self.samples.append((self._level(os.path.join(self.card, "pp_dpm_sclk")),
+                                     self._level(os.path.join(self.card, "pp_dpm_mclk"))))
+            except (OSError, ValueError, IndexError):
+                pass
+            self._stop.wait(0.005)
+
+    def __enter__(self):
+        if self.card:
+            self._stop.clear()
+            self._thread = self._threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+            self._thread = None
+
+    def summary(self):
+        import numpy as np
+
+        s = [v for v in self.samples if v[0] is not None]
+        if not s:
+            return {"unavailable": self.why if not self.card else "no readable samples"}
+        sc = np.array([v[0] for v in s])
+        mc = np.array([v[1] for v in s if v[1] is not None])
+        return {"sclk_mhz_min_median_max": [float(sc.min()), float(np.median(sc)), float(sc.max())],
+                "mclk_mhz_min_median_max": ([float(mc.min()), float(np.median(mc)), float(mc.max())]
+                                            if len(mc) else None),
+                "samples": len(s), "source": os.path.join(self.card, "pp_dpm_{sclk,mclk}"),
+                "note": "DPM level marked current, sampled every ~5 ms during the timed loops; "
+                        "fractions are against the published peaks, not these clocks"}
+
+
+def measure(args, w, torch, tw, hev, clocks, full: bool):
+    """Everything measured on one workload: the step (Infinity-Cache-cold as
+    the headline figure, warm graph replays beside it), the dense
+    comparators, per-kernel durations and rooflines, the realized sparsity;
+    with ``full`` also the fusion ablation and the hybrid training forward
+    and backward.  Returns (record, inputs)."""
     import numpy as np
-    import torch
 
-    from activation_sparse_feed_gate_amd import synth, tw
+    from activation_sparse_feed_gate_amd import synth
 
-    w = synth.WORKLOADS[args.workload]
-    if args.density is not None:
-        w = w.with_(density=args.density)
-    if args.M is not None:
-        w = w.with_(M=args.M)
     M, K, N, T, C = w.M, w.K, w.N, w.T, w.C
     # overflow capacity: the static backup capacity of the review §4-3 (an
     # eighth of the batch); if the batch overflows it, the retry rule there
@@ -435,7 +481,6 @@ def main():
     yd = torch.empty((M, K), dtype=torch.float32, device="cuda")
     wsd = torch.empty((tw.tw_ffn_workspace_bytes(M, K, N),), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    hev = HipEvents()
 
     def step(evp=None, evs=None):
         tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"],
@@ -460,7 +505,7 @@ def main():
         ws = tw.workspace(M, K, N, T, C, R_max)
         retries += 1
 
-    if args.copy_calibration:
+    if full and args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -498,152 +543,146 @@ def main():
     t_sparse_eager = timed(lambda i: step(evp[i], evs[i]))
     t_dense_eager = timed(lambda i: dense(evd[i]))
 
-    # ---- whole-step throughput: G consecutive steps of each path captured in
-    # one HIP graph (as a model forward would chain its layers), replayed so
-    # that exactly Ks steps run in the timed region ----
-    g_sparse, g_dense = None, None
-    if not args.no_graph:
-        G = max(1, min(args.graph_steps, Ks))
-        sizes = [G] * (Ks // G) + ([Ks % G] if Ks % G else [])
-        step_cap = lambda: (tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
-                                            bufs["tw_cnt"], bufs["ovf_rows"],
-                                            bufs["ovf_count"], R_max, ws),
-                            tw.tw_sparse_ffn_fwd(x, wg, wu, wdn, T, C, bufs["tw_val"],
-                                                 bufs["tw_idx"], bufs["tw_cnt"],
-                                                 bufs["ovf_rows"], bufs["ovf_count"], R_max,
-                                                 y, ws))
-        dense_cap = lambda: tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd)
-        graphs = {}
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            for n in set(sizes):
-                gs, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gs, stream=cap):
-                    for _ in range(n):
-                        step_cap()
-                with torch.cuda.graph(gd, stream=cap):
-                    for _ in range(n):
-                        dense_cap()
-                graphs[n] = (gs, gd)
-        torch.cuda.current_stream().wait_stream(cap)
-        for n in graphs:
-            graphs[n][0].replay()
-            graphs[n][1].replay()
+    # ---- G consecutive steps of each path captured in one HIP graph (as a
+    # model forward would chain its layers) ----
+    G = max(1, min(args.graph_steps, Ks))
+    sizes = [G] * (Ks // G) + ([Ks % G] if Ks % G else [])
+    step_cap = lambda: (tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
+                                        bufs["tw_cnt"], bufs["ovf_rows"],
+                                        bufs["ovf_count"], R_max, ws),
+                        tw.tw_sparse_ffn_fwd(x, wg, wu, wdn, T, C, bufs["tw_val"],
+                                             bufs["tw_idx"], bufs["tw_cnt"],
+                                             bufs["ovf_rows"], bufs["ovf_count"], R_max,
+                                             y, ws))
+    dense_cap = lambda: tw.tw_ffn_fwd(x, wg, wu, wdn, yd, wsd)
+    graphs = {}
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        for n in set(sizes):
+            gs, gd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gs, stream=cap):
+                for _ in range(n):
+                    step_cap()
+            with torch.cuda.graph(gd, stream=cap):
+                for _ in range(n):
+                    dense_cap()
+            graphs[n] = (gs, gd)
+    torch.cuda.current_stream().wait_stream(cap)
+    for n in graphs:
+        graphs[n][0].replay()
+        graphs[n][1].replay()
 
-        def timed_graphs(which):
-            """Mean step time over the Ks steps (host clock around the whole
-            loop), and per-replay step times from events between replays."""
-            evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    for _ in sizes]
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for (a, b), n in zip(evs_, sizes):
-                a.record()
-                graphs[n][which].replay()
-                b.record()
-            torch.cuda.synchronize()
-            mean = (time.perf_counter() - t0) / Ks
-            per = [a.elapsed_time(b) * 1e-3 / n for (a, b), n in zip(evs_, sizes)]
-            return mean, per
+    def timed_graphs(which):
+        """Warm steps: mean step time over the Ks steps (host clock around the
+        whole loop), and per-replay step times from events between replays."""
+        evs_ = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in sizes]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for (a, b), n in zip(evs_, sizes):
+            a.record()
+            graphs[n][which].replay()
+            b.record()
+        torch.cuda.synchronize()
+        mean = (time.perf_counter() - t0) / Ks
+        per = [a.elapsed_time(b) * 1e-3 / n for (a, b), n in zip(evs_, sizes)]
+        return mean, per
 
+    # ---- Infinity-Cache-cold steps (the headline): an in-place pass over
+    # 512 MB (twice the 256 MB cache) before each step evicts the weights, as
+    # in a deep model where the other layers' weights pass through the cache
+    # between two uses of this one.  Exactly Ks steps of each path run, one
+    # per graph replay; step time = (pass + step) - pass, each the median of
+    # Ks replays. ----
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    gf, gfs, gfd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(gf, stream=cap):
+            flush.add_(1)
+        with torch.cuda.graph(gfs, stream=cap):
+            flush.add_(1)
+            step_cap()
+        with torch.cuda.graph(gfd, stream=cap):
+            flush.add_(1)
+            dense_cap()
+    torch.cuda.current_stream().wait_stream(cap)
+
+    def replays(g):
+        ts = []
+        for _ in range(Ks):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return np.array(ts)
+
+    for g in (gf, gfs, gfd):
+        g.replay()
+    torch.cuda.synchronize()
+    with clocks:
         t_sparse, per_sparse = timed_graphs(0)
         t_dense, per_dense = timed_graphs(1)
-        g_sparse = graphs
+        f_ts = replays(gf)
+        cs_ts = replays(gfs)
+        cd_ts = replays(gfd)
+    t_f = float(np.median(f_ts))
+    per_cold = cs_ts - t_f
+    t_cs = float(np.median(cs_ts)) - t_f
+    t_cd = float(np.median(cd_ts)) - t_f
+    del flush, gf, gfs, gfd
 
-        # ---- the fusion the method turns on: packing in the gate's epilogue
-        # (tw_pack_gate) against the unfused path that writes the dense gate
-        # and packs it in a separate pass (tw_gate_dense + tw_pack_dense) ----
-        fusion = None
-        if args.fusion_ablation:
-            zbuf = torch.empty((M, N), dtype=torch.float32, device="cuda")
-            wsp = torch.empty((tw.tw_pack_dense_workspace_bytes(M, N),), dtype=torch.uint8,
-                              device="cuda")
-            bu = tw.alloc_pack(M, N, T, C, R_max)
-            fused_cap = lambda: tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
-                                                bufs["tw_cnt"], bufs["ovf_rows"],
-                                                bufs["ovf_count"], R_max, ws)
-            unfused_cap = lambda: (tw.tw_gate_dense(x, wg, zbuf),
-                                   tw.tw_pack_dense(zbuf, T, C, bu["tw_val"], bu["tw_idx"],
-                                                    bu["tw_cnt"], bu["ovf_rows"],
-                                                    bu["ovf_count"], R_max, wsp))
-            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(ga, stream=cap):
-                    for _ in range(G):
-                        fused_cap()
-                with torch.cuda.graph(gb, stream=cap):
-                    for _ in range(G):
-                        unfused_cap()
-            torch.cuda.current_stream().wait_stream(cap)
+    # ---- the fusion the method turns on: packing in the gate's epilogue
+    # (tw_pack_gate) against the unfused path that writes the dense gate and
+    # packs it in a separate pass (tw_gate_dense + tw_pack_dense) ----
+    fusion = None
+    if full and args.fusion_ablation:
+        zbuf = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        wsp = torch.empty((tw.tw_pack_dense_workspace_bytes(M, N),), dtype=torch.uint8,
+                          device="cuda")
+        bu = tw.alloc_pack(M, N, T, C, R_max)
+        fused_cap = lambda: tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"],
+                                            bufs["tw_cnt"], bufs["ovf_rows"],
+                                            bufs["ovf_count"], R_max, ws)
+        unfused_cap = lambda: (tw.tw_gate_dense(x, wg, zbuf),
+                               tw.tw_pack_dense(zbuf, T, C, bu["tw_val"], bu["tw_idx"],
+                                                bu["tw_cnt"], bu["ovf_rows"],
+                                                bu["ovf_count"], R_max, wsp))
+        ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(ga, stream=cap):
+                for _ in range(G):
+                    fused_cap()
+            with torch.cuda.graph(gb, stream=cap):
+                for _ in range(G):
+                    unfused_cap()
+        torch.cuda.current_stream().wait_stream(cap)
 
-            def per_call(g):
+        def per_call(g):
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(max(1, Ks // G)):
                 g.replay()
-                torch.cuda.synchronize()
-                t0 = time.perf_counter()
-                for _ in range(max(1, Ks // G)):
-                    g.replay()
-                torch.cuda.synchronize()
-                return (time.perf_counter() - t0) / (max(1, Ks // G) * G)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) / (max(1, Ks // G) * G)
 
-            t_fu, t_un = per_call(ga), per_call(gb)
-            fusion = {"fused_pack_us": t_fu * 1e6, "unfused_pack_us": t_un * 1e6,
-                      "unfused_over_fused": t_un / t_fu,
-                      "dense_gate_bytes": M * N * 4,
-                      "note": "tw_pack_gate vs tw_gate_dense + tw_pack_dense (dense fp32 gate "
-                              "written, read back and packed), HIP graphs, same outputs"}
-            del zbuf
-
-        # ---- Infinity-Cache-cold steps: an in-place pass over 512 MB (twice
-        # the 256 MB cache) before each step evicts the weights, as in a deep
-        # model where the other layers' weights pass through the cache between
-        # two uses of this one.  Step time = (flush + step) - flush, each the
-        # median of Kc graph replays. ----
-        cold = None
-        if args.cold_steps > 0:
-            flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
-            gf, gfs, gfd = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(gf, stream=cap):
-                    flush.add_(1)
-                with torch.cuda.graph(gfs, stream=cap):
-                    flush.add_(1)
-                    step_cap()
-                with torch.cuda.graph(gfd, stream=cap):
-                    flush.add_(1)
-                    dense_cap()
-            torch.cuda.current_stream().wait_stream(cap)
-
-            def med_replay(g):
-                ts = []
-                for _ in range(args.cold_steps):
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    g.replay()
-                    b.record()
-                    b.synchronize()
-                    ts.append(a.elapsed_time(b) * 1e-3)
-                return float(np.median(ts))
-
-            for g in (gf, gfs, gfd):
-                g.replay()
-            t_f = med_replay(gf)
-            t_cs = med_replay(gfs) - t_f
-            t_cd = med_replay(gfd) - t_f
-            cold = {"ms_per_step": t_cs * 1e3, "value": M / t_cs, "dense_ms_per_step": t_cd * 1e3,
-                    "speedup_vs_dense": t_cd / t_cs, "flush_ms": t_f * 1e3,
-                    "note": f"median of {args.cold_steps} replays of (512 MB in-place pass + step) "
-                            f"minus the pass alone"}
-            del flush
-    else:
-        t_sparse, t_dense = t_sparse_eager, t_dense_eager
-        per_sparse, per_dense, cold, fusion = [t_sparse_eager], [t_dense_eager], None, None
+        t_fu, t_un = per_call(ga), per_call(gb)
+        fusion = {"fused_pack_us": t_fu * 1e6, "unfused_pack_us": t_un * 1e6,
+                  "unfused_over_fused": t_un / t_fu,
+                  "dense_gate_bytes": M * N * 4,
+                  "note": "tw_pack_gate vs tw_gate_dense + tw_pack_dense (dense fp32 gate "
+                          "written, read back and packed), HIP graphs, same outputs"}
+        del zbuf, ga, gb
+    del graphs
 
     hybrid = hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, stream,
-                                  hev, t_dense, step) if args.hybrid else None
+                                  hev, t_dense, step) if (full and args.hybrid) else None
 
-    # ---- sanity line: the same dense FFN on torch.matmul (hipBLASLt) ----
+    # ---- the same dense FFN on torch.matmul (hipBLASLt) ----
     wgu = torch.cat([wg, wu], dim=0)
     wd_row = wdn  # [N, K]: y = h @ W_d
 
@@ -655,6 +694,7 @@ def main():
     for _ in range(3):
         blas_ffn()
     t_blas = timed(lambda i: blas_ffn())
+    del wgu
 
     def avg(evl, i):
         return sum(hev.ms(e[i], e[i + 1]) for e in evl) / len(evl) * 1e-3  # seconds
@@ -682,7 +722,7 @@ def main():
     # it finishes (the split partials it reads are not counted)
     sparse_bytes = (sparse_nnz * (4 * K + 8) + int((~ovf).sum()) * (2 * K + 4 * K + 4 * NT)
                     + R * (4 * NT + 4 * K))
-    work = {  # algorithmic work per launch: (amount, bound, unit)
+    work = {  # algorithmic work per launch: (amount, bound)
         "gate_twell": (2.0 * M * K * N, "mfma"),
         "sparse_updown": (float(sparse_bytes), "hbm"),
         "fallback_gateup": (4.0 * R * K * N, "mfma"),
@@ -707,46 +747,48 @@ def main():
         r["kernel"] = name
         r["avg_us"] = secs * 1e6
         r["traffic"] = _traffic(name, srcs[name], w.name)
+        if r["traffic"] is not None:
+            # the bytes the counters saw leave or enter HBM, per launch, over
+            # the same duration: measured DRAM throughput beside the
+            # algorithmic figure
+            r["counter_GBs"] = r["traffic"] / secs / 1e9
+            r["counter_frac"] = r["counter_GBs"] / PEAK_HBM_GBS
         return r
 
     path_kernels = ["gate_twell", "sparse_updown", "fallback_gateup", "fallback_down"]
     dominant = max(path_kernels, key=lambda k: kern[k])
     stages = {k: roof(k, kern[k]) for k in path_kernels if kern[k] > 0}
     stages.update({k: roof(k, v) for k, v in kern_dense.items()})
-
-    out = {
-        "metric": METRIC,
-        "value": M / t_sparse,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": Ks,
-        "warmup": args.warmup,
-        "ms_per_step": t_sparse * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
+    pct = lambda a: [float(np.percentile(a, q)) * 1e3 for q in (10, 50, 90)]
+    best_dense = min(t_cd, t_blas)
+    rec = {
+        "value": M / t_cs,
+        "ms_per_step": t_cs * 1e3,
+        "ms_per_step_p10_p50_p90": pct(per_cold),
+        "speedup_vs_dense": t_cd / t_cs,
+        "speedup_vs_best_dense": best_dense / t_cs,
         "config": {"workload": w.name, "M": M, "K": K, "N": N, "T": T, "C": C,
                    "density": w.density, "sigma_s": w.sigma_s, "seed": w.seed, "R_max": R_max,
                    "capacity_retries": retries},
         "roofline": roof(dominant, kern[dominant]),
-        "speedup_vs_dense": t_dense / t_sparse,
-        "ms_per_step_p10_p50_p90": [float(np.percentile(per_sparse, q)) * 1e3 for q in (10, 50, 90)],
-        "dense": {"ms_per_step": t_dense * 1e3, "value": M / t_dense,
-                  "ms_per_step_p10_p50_p90": [float(np.percentile(per_dense, q)) * 1e3
-                                              for q in (10, 50, 90)]},
-        "cold": cold,
-        "fusion": fusion,
-        "hybrid_training_forward": hybrid,
+        "cache": ("Infinity-Cache-cold: each step follows a 512 MB in-place pass; step time = "
+                  f"median of {Ks} replays of (pass + step) minus the median pass "
+                  f"({t_f * 1e3:.3f} ms)"),
+        "dense": {"ms_per_step": t_cd * 1e3, "value": M / t_cd, "cache": "cold",
+                  "kernel": "tw_ffn_fwd (our MFMA dense gated FFN)"},
+        "warm": {"ms_per_step": t_sparse * 1e3, "value": M / t_sparse,
+                 "ms_per_step_p10_p50_p90": pct(per_sparse),
+                 "dense_ms_per_step": t_dense * 1e3,
+                 "dense_ms_per_step_p10_p50_p90": pct(per_dense),
+                 "speedup_vs_dense": t_dense / t_sparse,
+                 "timing": f"HIP graphs of {G} consecutive steps, replayed to run {Ks} steps, "
+                           f"back to back (weights stay in the Infinity Cache)"},
         "eager": {"sparse_ms_per_step": t_sparse_eager * 1e3,
                   "dense_ms_per_step": t_dense_eager * 1e3},
-        "timing": (f"HIP graphs of {min(args.graph_steps, Ks)} consecutive steps, "
-                   f"replayed to run {Ks} steps") if not args.no_graph else "eager launches",
         "hipblaslt_dense": {"ms_per_step": t_blas * 1e3,
-                            "speedup_vs": t_blas / t_sparse,
+                            "speedup_vs": t_blas / t_cs,
                             "note": "torch.matmul gate+up GEMM, ReLU*u in torch, bf16 h, "
-                                    "torch.matmul down; sanity reference only"},
+                                    "torch.matmul down, back to back (warm)"},
         "kernels_us": {k: v * 1e6 for k, v in {**kern, **kern_dense}.items()},
         "stages": stages,
         "realized": {"density": float(nnz.sum()) / (M * N), "overflow_rows": R,
@@ -758,8 +800,88 @@ def main():
                          float(nnz.mean()) if M else 0.0,
                          *[float(np.percentile(nnz, q)) if M else 0.0 for q in (50, 95, 99)],
                          int(nnz.max(initial=0))]},
-        "device": torch.cuda.get_device_properties(0).name,
     }
+    if full:
+        rec["fusion"] = fusion
+        rec["hybrid_training_forward"] = hybrid
+    del x, wg, wu, wdn, bufs, ws, y, yd, wsd
+    return rec, d
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ffn-0.5b")
+    ap.add_argument("--density", type=float, default=None, help="override the target density")
+    ap.add_argument("--M", type=int, default=None,
+                    help="override the token count (decode-like batches)")
+    ap.add_argument("--r-max", type=int, default=None,
+                    help="overflow-row capacity (default: an eighth of the batch, grown by "
+                         "the retry rule before timing)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="also run a plain elementwise copy of MB megabytes (fp32, read + "
+                         "write) so that a counter profile can scale FETCH_SIZE/WRITE_SIZE")
+    ap.add_argument("--no-fusion-ablation", dest="fusion_ablation", action="store_false",
+                    help="skip timing the unfused gate + pack path")
+    ap.add_argument("--no-hybrid", dest="hybrid", action="store_false",
+                    help="skip the hybrid training-forward measurement")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="measure the headline workload only (not the other blocks)")
+    ap.add_argument("--graph-steps", type=int, default=5,
+                    help="consecutive steps captured in one HIP graph for the warm line "
+                         "(1: a graph launch per step)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}): the path is data-parallel over tokens with no exchange, so N GPUs "
+              f"run N independent copies; no multi-GPU figure is produced.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from activation_sparse_feed_gate_amd import synth, tw
+
+    w = synth.WORKLOADS[args.workload]
+    if args.density is not None:
+        w = w.with_(density=args.density)
+    if args.M is not None:
+        w = w.with_(M=args.M)
+    hev = HipEvents()
+    clocks = ClockSampler(torch)
+    rec, d = measure(args, w, torch, tw, hev, clocks, full=True)
+    head = {
+        "metric": METRIC,
+        "value": rec["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    out = {**head, **rec}
+    configs = {}
+    if args.configs and args.M is None and args.density is None and args.workload == "ffn-0.5b":
+        for name, dens in SIDE_CONFIGS:
+            wc = synth.WORKLOADS[name] if dens is None else \
+                synth.WORKLOADS[name].with_(density=dens)
+            key = name if dens is None else f"{name}@{dens:g}"
+            rc, _ = measure(args, wc, torch, tw, hev, clocks, full=False)
+            configs[key] = rc
+            torch.cuda.empty_cache()
+    out["configs"] = configs or None
+    out["clocks"] = clocks.summary()
+    out["device"] = torch.cuda.get_device_properties(0).name
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, w, args.cpu_budget)
     else:
