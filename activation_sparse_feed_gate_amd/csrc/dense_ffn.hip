@@ -240,16 +240,18 @@ struct DN {
     static constexpr int LDS = S * STAGE;
     static constexpr int NIA = BM / (16 * NW);          // A direct loads per wave and stage
     static constexpr int BR_PER = 1024 / BROW;          // W_d rows per 1 KB direct load
+    static constexpr int LPR = BROW / 16;               // lanes (16-byte chunks) per W_d row
     static constexpr int NIB = kPK / BR_PER / NW;       // B direct loads per wave and stage
     static constexpr int NI = NIA + NIB;
-    static_assert(BN == 128, "W_d slice layout assumes 16 chunks per row");
+    static_assert(BN == 128 || BN == 256, "W_d slice rows of 16 or 32 chunks");
     static_assert(BM % (16 * NW) == 0 && (kPK / BR_PER) % NW == 0, "stage split");
 };
 
-// W_d slice rows in a stage: 16 chunks of 16 bytes, chunk c at c ^ bsw(row).
-// A transposing fragment read touches 4 consecutive rows x 4 chunks in each
-// half-wave; XOR by 4 (row % 4) puts those 16 chunks in 16 different chunk
-// positions, i.e. all 64 banks once.
+// W_d slice rows in a stage: BN / 8 chunks of 16 bytes, chunk c at
+// c ^ bsw(row).  A transposing fragment read touches 4 consecutive rows x 4
+// chunks in each half-wave; rows 256 or 512 bytes apart start on the same
+// bank, and XOR by 4 (row % 4) puts those 16 chunks in 16 different chunk
+// positions of one 256-byte bank row, i.e. all 64 banks once.
 __device__ __forceinline__ int bsw(int row) { return 4 * (row & 3); }
 
 // PAIRS = 2: y = h W_d + h2 W_d2, the reduction running over the first pair's
@@ -298,11 +300,11 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
             aoff[j] = rows16_voff((uint32_t)(r - m0) * N * 2, lane, row0);
         }
         // B: this lane's W_d row within a 1 KB load and its swizzled chunk
-        const int brl = lane >> 4;  // 0..3
+        const int brl = lane / P::LPR;  // 0 .. BR_PER - 1
 #pragma unroll
         for (int j = 0; j < P::NIB; ++j) {
             const int row = (wave * P::NIB + j) * P::BR_PER + brl;
-            boff[j] = (uint32_t)row * K * 2 + (uint32_t)(((lane & 15) ^ bsw(row)) << 4);
+            boff[j] = (uint32_t)row * K * 2 + (uint32_t)(((lane % P::LPR) ^ bsw(row)) << 4);
         }
         // one pair's stage kk into ring slot st (each call site passes fixed
         // descriptors: the pair is chosen by a uniform branch, not a select)
@@ -640,6 +642,13 @@ hipError_t launch_gu(int grid_cap, const uint16_t *x, const uint16_t *w1, const 
     return hipGetLastError();
 }
 using DnDense = DnCfg<128, 128, 2, 2, 4>;
+// all rows, when its tiles fill the chip: 256 x 256 tiles of 4 waves, one
+// per SIMD, each 128 x 128 (its 256 accumulators leave no room for a second
+// wave; the 8-wave 64 x 128 arrangement spills), a third fewer LDS bytes per
+// flop than 128 x 128 tiles.  Measured at the 2B block: 487 us against 565.
+// The same arrangement for the gate+up GEMM (256 accumulators plus two weight
+// operands) spilled and measured slower (1053 against 951 us).
+using DnBig = DnCfg<256, 256, 2, 2, 4>;
 using DnRows = DnCfg<128, 128, 2, 4, 6>;
 using DnRowsPair = DnCfg<128, 128, 2, 4, 6, 2>;
 static_assert(DnRows::BM_ == kSplitBM && DnRows::BN_ == kSplitBN &&
@@ -780,6 +789,13 @@ hipError_t launch_down(const uint16_t *h, const uint16_t *wd, int K, int N,
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(DnRows::kernel, dim3(kSplitGrid), dim3(DnRows::NTH), DnRows::LDS, s, h,
                            wd, K, N, rowlist, count, R_cap, y, partial, nullptr, nullptr);
+    } else if (!rowlist && K % DnBig::BN_ == 0 &&
+               (R_cap + DnBig::BM_ - 1) / DnBig::BM_ * (K / DnBig::BN_) >= kFillTiles) {
+        hipError_t e = lds_limit_once<DnBig::kernel>(DnBig::LDS);
+        if (e != hipSuccess) return e;
+        const int tiles = (R_cap + DnBig::BM_ - 1) / DnBig::BM_ * (K / DnBig::BN_);
+        hipLaunchKernelGGL(DnBig::kernel, dim3(tiles), dim3(DnBig::NTH), DnBig::LDS, s, h, wd, K,
+                           N, rowlist, count, R_cap, y, partial, nullptr, nullptr);
     } else {
         hipError_t e = lds_limit_once<DnDense::kernel>(DnDense::LDS);
         if (e != hipSuccess) return e;
