@@ -88,10 +88,10 @@ def _traffic(kernel: str, src: str, workload: str):
     when they were taken on the current kernel source and this workload."""
     try:
         with open(PROFILE_TRAFFIC) as f:
-            rec = json.load(f)[kernel]
+            rec = json.load(f)[workload][kernel]
     except (OSError, KeyError, ValueError):
         return None
-    if rec.get("src_sha") != _src_sha(src) or rec.get("workload") != workload:
+    if rec.get("src_sha") != _src_sha(src):
         return None
     return float(rec["bytes_per_launch"])
 
@@ -453,6 +453,35 @@ class ClockSampler:
                         "fractions are against the published peaks, not these clocks"}
 
 
+def eager_record(args, w, M, K, N, T, C, R_max, retries, t_sparse, t_dense, hev, evp, evs, evd,
+                 nnz, ovf, R, sparse_nnz):
+    """The record of an --eager-only run: eager step times and per-kernel
+    durations (what a profiler run's averages are compared with)."""
+    def avg(evl, i):
+        return sum(hev.ms(e[i], e[i + 1]) for e in evl) / len(evl) * 1e-3
+
+    def span(evl, i, j):
+        return sum(hev.ms(e[i], e[j]) for e in evl) / len(evl) * 1e-3
+
+    kern = {"gate_twell": avg(evp, 0), "ovf_compact": avg(evp, 1),
+            "fallback_gateup": span(evs, 0, 1), "fallback_down": span(evs, 1, 2),
+            "sparse_updown": span(evs, 2, 3), "dense_gateup": avg(evd, 0),
+            "dense_down": avg(evd, 1)}
+    for l in (evp, evs, evd):
+        for e in l:
+            hev.destroy(e)
+    return {"value": M / t_sparse, "ms_per_step": t_sparse * 1e3,
+            "speedup_vs_dense": t_dense / t_sparse,
+            "config": {"workload": w.name, "M": M, "K": K, "N": N, "T": T, "C": C,
+                       "density": w.density, "sigma_s": w.sigma_s, "seed": w.seed,
+                       "R_max": R_max, "capacity_retries": retries},
+            "timing": "eager launches with HIP events between kernels (--eager-only)",
+            "dense": {"ms_per_step": t_dense * 1e3},
+            "kernels_us": {k: v * 1e6 for k, v in kern.items()},
+            "realized": {"density": float(nnz.sum()) / (M * N), "overflow_rows": R,
+                         "nnz_per_sparse_row": sparse_nnz / max(1, int((~ovf).sum()))}}
+
+
 def measure(args, w, torch, tw, hev, clocks, full: bool):
     """Everything measured on one workload: the step (Infinity-Cache-cold as
     the headline figure, warm graph replays beside it), the dense
@@ -542,6 +571,10 @@ def measure(args, w, torch, tw, hev, clocks, full: bool):
     evd = [hev.create(3) for _ in range(Ks)]
     t_sparse_eager = timed(lambda i: step(evp[i], evs[i]))
     t_dense_eager = timed(lambda i: dense(evd[i]))
+
+    if args.eager_only:
+        return eager_record(args, w, M, K, N, T, C, R_max, retries, t_sparse_eager,
+                            t_dense_eager, hev, evp, evs, evd, nnz, ovf, R, sparse_nnz), d
 
     # ---- G consecutive steps of each path captured in one HIP graph (as a
     # model forward would chain its layers) ----
@@ -831,6 +864,10 @@ def main():
                     help="skip the hybrid training-forward measurement")
     ap.add_argument("--no-configs", dest="configs", action="store_false",
                     help="measure the headline workload only (not the other blocks)")
+    ap.add_argument("--eager-only", action="store_true",
+                    help="time only the eager launches whose per-kernel durations the roofline "
+                         "uses (for profiler runs: no graph replays, cache-cold steps or "
+                         "comparison lines); implies --no-configs")
     ap.add_argument("--graph-steps", type=int, default=5,
                     help="consecutive steps captured in one HIP graph for the warm line "
                          "(1: a graph launch per step)")
@@ -871,7 +908,8 @@ def main():
     }
     out = {**head, **rec}
     configs = {}
-    if args.configs and args.M is None and args.density is None and args.workload == "ffn-0.5b":
+    if (args.configs and not args.eager_only and args.M is None and args.density is None
+            and args.workload == "ffn-0.5b"):
         for name, dens in SIDE_CONFIGS:
             wc = synth.WORKLOADS[name] if dens is None else \
                 synth.WORKLOADS[name].with_(density=dens)
