@@ -615,15 +615,21 @@ using GuRows = GuCfg<128, 128, 2, 4, 4>;
 // chip: twice the workgroups of 128-column tiles and a quarter of the
 // padded rows
 using GuSmall = GuCfg<64, 64, 2, 2, 4>;
-// row lists of capacity at most kSmallRows (the inference overflow rows):
-// 128 rows x 64 columns of g and of u, exactly 256 tiles at 512 rows of
-// capacity; measured 6% faster than 64 x 64 tiles at the 0.5B block
-// (16.3 against 17.4 us for ~400 rows), 64 x 128 was 17.7 us
+// row lists of capacity above kTinyRows and at most kSmallRows (the
+// inference overflow rows of a batch of thousands): 128 rows x 64 columns of
+// g and of u, exactly 256 tiles at 512 rows of capacity; measured 6% faster
+// than 64 x 64 tiles at the 0.5B block (16.3 against 17.4 us for ~400
+// rows), 64 x 128 was 17.7 us.  A capacity of at most kTinyRows keeps 64 x 64
+// tiles: a 128-row tile would stream 128 (repeated) x rows for a handful of
+// listed ones, which measured 12.6 us for one row at the 0.5B shape.
+constexpr int kTinyRows = 64;
 using GuList = GuCfg<128, 64, 2, 2, 4>;
 using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
 using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
-using GuSmallKeep = GuCfg<128, 64, 2, 2, 4, kKeep>;
-using GuSmallDh = GuCfg<128, 64, 2, 2, 4, kDh>;
+using GuListKeep = GuCfg<128, 64, 2, 2, 4, kKeep>;
+using GuListDh = GuCfg<128, 64, 2, 2, 4, kDh>;
+using GuTinyKeep = GuCfg<64, 64, 2, 2, 4, kKeep>;
+using GuTinyDh = GuCfg<64, 64, 2, 2, 4, kDh>;
 
 // A row-list gate+up configuration G over a grid of at most grid_cap
 // persistent workgroups (sized for the capacity; the rows are counted on the
@@ -710,7 +716,7 @@ hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const u
     const bool small = rowlist
                            ? R_cap <= kSmallRows
                            : (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_) < kFillTiles;
-    if (small && rowlist) {
+    if (small && rowlist && R_cap > kTinyRows) {
         return launch_gu<GuList>(1024, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr,
                                  nullptr, nullptr, nullptr, 0.0f, s);
     } else if (small) {
@@ -761,9 +767,12 @@ hipError_t launch_gateup_keep(const uint16_t *x, int M, const uint16_t *wg_t,
     if (!g_out && !u_out) return launch_gateup(x, M, wg_t, wu_t, K, N, rowlist, count, R_cap, h, s);
     if (R_cap <= 0) return hipSuccess;
     // the tiles of launch_gateup's row-list path
+    if (R_cap <= kTinyRows)
+        return launch_gu<GuTinyKeep>(1024, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h,
+                                     g_out, u_out, nullptr, nullptr, 0.0f, s);
     if (R_cap <= kSmallRows)
-        return launch_gu<GuSmallKeep>(1024, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h,
-                                      g_out, u_out, nullptr, nullptr, 0.0f, s);
+        return launch_gu<GuListKeep>(1024, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h,
+                                     g_out, u_out, nullptr, nullptr, 0.0f, s);
     return launch_gu<GuRowsKeep>(256, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, g_out,
                                  u_out, nullptr, nullptr, 0.0f, s);
 }
@@ -773,9 +782,12 @@ hipError_t launch_backup_dh(const uint16_t *dy, int M, const uint16_t *wd, int K
                             const uint16_t *g_in, const uint16_t *u_in, float l1,
                             uint16_t *du, uint16_t *dz, hipStream_t s) {
     if (R_cap <= 0) return hipSuccess;
+    if (R_cap <= kTinyRows)
+        return launch_gu<GuTinyDh>(1024, dy, wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz,
+                                   nullptr, g_in, u_in, l1, s);
     if (R_cap <= kSmallRows)
-        return launch_gu<GuSmallDh>(1024, dy, wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz,
-                                    nullptr, g_in, u_in, l1, s);
+        return launch_gu<GuListDh>(1024, dy, wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz,
+                                   nullptr, g_in, u_in, l1, s);
     return launch_gu<GuRowsDh>(256, dy, wd, nullptr, K, N, rowlist, count, R_cap, M, du, dz,
                                nullptr, g_in, u_in, l1, s);
 }

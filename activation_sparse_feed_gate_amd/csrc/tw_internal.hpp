@@ -73,8 +73,8 @@ hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const u
                                 hipStream_t s);
 
 // Row-list gate+up GEMMs with a capacity of at most this many rows take
-// 128-row x 64-column tiles (256 of them at this capacity), larger row lists
-// 128 x 128 tiles.  The row count itself is known only on the device; with
+// 128-row x 64-column tiles (256 of them at this capacity; 64 x 64 tiles up
+// to 64 rows of capacity), larger row lists 128 x 128 tiles.  The row count itself is known only on the device; with
 // the usual capacity of an eighth of the batch the small tiles measured
 // faster below about 400 listed rows and 128 x 128 tiles above (at 360-1000
 // rows the larger tiles took 25-40% less time than 64 x 64 ones).
