@@ -647,7 +647,12 @@ hipError_t launch_gu(int grid_cap, const uint16_t *x, const uint16_t *w1, const 
                        l1);
     return hipGetLastError();
 }
-using DnDense = DnCfg<128, 128, 2, 2, 4>;
+// all rows, 128 x 128 tiles of 8 waves (64 x 32 each, two per SIMD): with
+// one tile per CU (the 0.5B block's 256) the 4-wave arrangement leaves a
+// single wave per SIMD to wait out every barrier and fragment read; 8 waves
+// measured 40.1 against 53-54 us there and the same at two and three tiles
+// per CU (paper shape, 1B block)
+using DnDense = DnCfg<128, 128, 2, 4, 4>;
 // all rows, when its tiles fill the chip: 256 x 256 tiles of 4 waves, one
 // per SIMD, each 128 x 128 (its 256 accumulators leave no room for a second
 // wave; the 8-wave 64 x 128 arrangement spills), a third fewer LDS bytes per
