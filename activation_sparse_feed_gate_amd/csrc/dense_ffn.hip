@@ -52,7 +52,9 @@ struct GU {
     static constexpr int STAGE = SR * kPRow;
     static constexpr int LDS = S * STAGE;
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile");
-    static_assert(BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "each load row group in one operand");
+    // each wave's 16-row load slice lies in one operand (the operand is then
+    // wave-uniform), and the stage splits evenly over the waves
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && SR % (16 * NW) == 0, "load slices");
 };
 
 // Epilogue modes:
@@ -108,18 +110,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
         const uint64_t xbytes = (uint64_t)(rowlist ? xrows : rows - m0) * K * 2;
         const uint16_t *gb = wg_t + (size_t)n0 * K;
         const uint16_t *ub = NB == 2 ? wu_t + (size_t)n0 * K : gb;
-        // Load j of a wave fetches stage rows [16 (j NW + wave), +16): since
-        // BM and BN are multiples of 16 NW, j alone decides the operand.
+        // Load j of a wave fetches stage rows [16 (j NW + wave), +16), all in
+        // one operand (BM and BN are multiples of 16), chosen per wave.
         uint32_t voff[P::NI];
 #pragma unroll
         for (int j = 0; j < P::NI; ++j) {
             const int row0 = (j * P::NW + wave) * 16;
             const int sr = row0 + (lane >> 2);
             uint32_t row_off;
-            if (j * P::NW * 16 < BM) {
+            if (row0 < BM) {
                 const int r = min(m0 + sr, rows - 1);
                 row_off = rowlist ? (uint32_t)rowlist[r] * K * 2 : (uint32_t)(r - m0) * K * 2;
-            } else if (NB == 1 || j * P::NW * 16 < BM + BN) {
+            } else if (NB == 1 || row0 < BM + BN) {
                 row_off = (uint32_t)(sr - BM) * K * 2;
             } else {
                 row_off = (uint32_t)(sr - BM - BN) * K * 2;
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
             for (int j = 0; j < P::NI; ++j) {
                 const int row0 = (j * P::NW + wave) * 16;
                 char *dst = st + row0 * kPRow;
-                if (j * P::NW * 16 < BM) dma16(rx, voff[j], soff, dst);
-                else if (NB == 1 || j * P::NW * 16 < BM + BN) dma16(rg, voff[j], soff, dst);
+                if (row0 < BM) dma16(rx, voff[j], soff, dst);
+                else if (NB == 1 || row0 < BM + BN) dma16(rg, voff[j], soff, dst);
                 else dma16(ru, voff[j], soff, dst);
             }
         };
@@ -623,7 +625,7 @@ using GuSmall = GuCfg<64, 64, 2, 2, 4>;
 // tiles: a 128-row tile would stream 128 (repeated) x rows for a handful of
 // listed ones, which measured 12.6 us for one row at the 0.5B shape.
 constexpr int kTinyRows = 64;
-using GuList = GuCfg<128, 64, 2, 2, 4>;
+using GuList = GuCfg<128, 64, 4, 2, 4>;
 using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
 using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
 using GuListKeep = GuCfg<128, 64, 2, 2, 4, kKeep>;
