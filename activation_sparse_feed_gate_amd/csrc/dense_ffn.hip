@@ -621,7 +621,9 @@ using GuSmall = GuCfg<64, 64, 2, 2, 4>;
 // inference overflow rows of a batch of thousands): 128 rows x 64 columns of
 // g and of u, exactly 256 tiles at 512 rows of capacity; measured 6% faster
 // than 64 x 64 tiles at the 0.5B block (16.3 against 17.4 us for ~400
-// rows), 64 x 128 was 17.7 us.  A capacity of at most kTinyRows keeps 64 x 64
+// rows), 64 x 128 was 17.7 us; 8 waves of 32 x 32 (two per SIMD) rather
+// than 4 of 64 x 32: 15.1 against 15.7 us at the 0.5B block, 21.6 against
+// 23.7 at the paper shape.  A capacity of at most kTinyRows keeps 64 x 64
 // tiles: a 128-row tile would stream 128 (repeated) x rows for a handful of
 // listed ones, which measured 12.6 us for one row at the 0.5B shape.
 constexpr int kTinyRows = 64;
