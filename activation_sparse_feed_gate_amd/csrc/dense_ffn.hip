@@ -630,7 +630,10 @@ constexpr int kTinyRows = 64;
 using GuList = GuCfg<128, 64, 4, 2, 4>;
 using GuRowsKeep = GuCfg<128, 128, 2, 4, 4, kKeep>;
 using GuRowsDh = GuCfg<128, 128, 2, 4, 4, kDh>;
-using GuListKeep = GuCfg<128, 64, 2, 2, 4, kKeep>;
+// (the hybrid backup rows' kKeep tiles too: 16.0 against 17.5 us at the
+// 0.5B block; the single-operand kDh stage of 192 rows does not split over
+// 8 waves and keeps 4)
+using GuListKeep = GuCfg<128, 64, 4, 2, 4, kKeep>;
 using GuListDh = GuCfg<128, 64, 2, 2, 4, kDh>;
 using GuTinyKeep = GuCfg<64, 64, 2, 2, 4, kKeep>;
 using GuTinyDh = GuCfg<64, 64, 2, 2, 4, kDh>;
