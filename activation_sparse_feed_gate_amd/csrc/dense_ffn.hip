@@ -57,6 +57,62 @@ struct GU {
     static_assert(BM % 16 == 0 && BN % 16 == 0 && SR % (16 * NW) == 0, "load slices");
 };
 
+// Segment sg of the sparse kernel's heaviest-first row order (RowOrder):
+// one row per thread, its counts read in one round of loads; a block-wide
+// ordered compaction puts the segment's heavy rows first.
+template <int NTH>
+__device__ void row_order_block(const RowOrder &o, int sg, char *smem) {
+    static_assert(NTH >= kOrderSeg, "one row per thread");
+    constexpr int NW = NTH / 64;
+    int *s_w = reinterpret_cast<int *>(smem);  // 2 NW wave counts
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r0 = sg * kOrderSeg;
+    const int nrows = min(kOrderSeg, o.M - r0);
+    const bool in = tid < nrows;
+    bool heavy = false;
+    if (in) {
+        const int32_t *cr = o.tw_cnt + (size_t)(r0 + tid) * o.NT;
+        int tot = 0;
+        bool over = false;
+        if ((o.NT & 3) == 0) {
+#pragma unroll 8
+            for (int t = 0; t < o.NT; t += 4) {
+                const int4 c = *reinterpret_cast<const int4 *>(cr + t);
+                tot += c.x + c.y + c.z + c.w;
+                over |= (c.x > o.C) | (c.y > o.C) | (c.z > o.C) | (c.w > o.C);
+            }
+        } else {
+            for (int t = 0; t < o.NT; ++t) {
+                tot += cr[t];
+                over |= cr[t] > o.C;
+            }
+        }
+        heavy = !over && tot > o.H;
+    }
+    const uint64_t bh = __ballot(heavy), bl = __ballot(in && !heavy);
+    if (lane == 0) {
+        s_w[wave] = __popcll(bh);
+        s_w[NW + wave] = __popcll(bl);
+    }
+    __syncthreads();
+    int hb = 0, lb = 0, ht = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int a = s_w[w], b = s_w[NW + w];
+        hb += w < wave ? a : 0;
+        lb += w < wave ? b : 0;
+        ht += a;
+    }
+    const uint64_t below = (1ull << lane) - 1;
+    int32_t *slots = o.perm + 128 + r0;
+    if (heavy) slots[hb + __popcll(bh & below)] = r0 + tid;
+    else if (in) slots[ht + lb + __popcll(bl & below)] = r0 + tid;
+    if (tid == 0) {
+        o.perm[sg] = ht;
+        o.perm[64 + sg] = nrows - ht;
+    }
+}
+
 // Epilogue modes:
 //   kGU    h = bf16(ReLU(g) u)
 //   kKeep  h, and bf16(ReLU(g)) / bf16(u) into g_out / u_out where given
@@ -72,10 +128,18 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const uint16_t *__restrict__ wu_t, int K, int N, const int32_t *__restrict__ rowlist,
     const int32_t *__restrict__ count, int R_cap, int xrows, uint16_t *__restrict__ h,
     uint16_t *__restrict__ g_out, uint16_t *__restrict__ u_out,
-    const uint16_t *__restrict__ g_in, const uint16_t *__restrict__ u_in, float l1) {
+    const uint16_t *__restrict__ g_in, const uint16_t *__restrict__ u_in, float l1,
+    RowOrder ord) {
     constexpr int NB = MODE == kDh ? 1 : 2;  // weight operands
     using P = GU<BM, BN, WM, WN, S, NB>;
     extern __shared__ __attribute__((aligned(16))) char smem[];
+    // the last workgroups write the sparse kernel's row order, when asked
+    const int nseg = ord.perm ? row_order_segs(ord.M) : 0;
+    const int gridw = gridDim.x - nseg;  // the GEMM's workgroups
+    if ((int)blockIdx.x >= gridw) {
+        row_order_block<P::NTH>(ord, blockIdx.x - gridw, smem);
+        return;
+    }
 
     const int rows = rows_of(count, R_cap);
     const int nrb = (rows + BM - 1) / BM;
@@ -87,12 +151,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gateup_kernel(
     const int KT = K / kPK;
 
     const int ncb = N / BN;
-    for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    for (int t = blockIdx.x; t < ntiles; t += gridw) {
         int rb, cb;
         if (rowlist) {
             // few rows: all row blocks of a weight column block on one XCD
             // (workgroup index % 8), so the weights are fetched once per XCD
-            if ((ncb & 7) == 0 && (gridDim.x & 7) == 0) {
+            if ((ncb & 7) == 0 && (gridw & 7) == 0) {
                 const int local = t >> 3;
                 cb = (local / nrb) * 8 + (t & 7);
                 rb = local % nrb;
@@ -645,13 +709,14 @@ template <typename G>
 hipError_t launch_gu(int grid_cap, const uint16_t *x, const uint16_t *w1, const uint16_t *w2,
                      int K, int N, const int32_t *rowlist, const int32_t *count, int R_cap,
                      int xrows, uint16_t *o1, uint16_t *o2, uint16_t *o3, const uint16_t *g_in,
-                     const uint16_t *u_in, float l1, hipStream_t s) {
+                     const uint16_t *u_in, float l1, hipStream_t s,
+                     const RowOrder &ord = RowOrder()) {
     hipError_t e = lds_limit_once<G::kernel>(G::LDS);
     if (e != hipSuccess) return e;
     const int tiles = (R_cap + G::BM_ - 1) / G::BM_ * (N / G::BN_);
-    hipLaunchKernelGGL(G::kernel, dim3(tiles < grid_cap ? tiles : grid_cap), dim3(G::NTH), G::LDS,
-                       s, x, w1, w2, K, N, rowlist, count, R_cap, xrows, o1, o2, o3, g_in, u_in,
-                       l1);
+    const int grid = (tiles < grid_cap ? tiles : grid_cap) + (ord.perm ? row_order_segs(ord.M) : 0);
+    hipLaunchKernelGGL(G::kernel, dim3(grid), dim3(G::NTH), G::LDS, s, x, w1, w2, K, N, rowlist,
+                       count, R_cap, xrows, o1, o2, o3, g_in, u_in, l1, ord);
     return hipGetLastError();
 }
 // all rows, 128 x 128 tiles of 8 waves (64 x 32 each, two per SIMD): with
@@ -720,52 +785,35 @@ size_t split_partial_bytes() {
 
 hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const uint16_t *wu_t,
                          int K, int N, const int32_t *rowlist, const int32_t *count, int R_cap,
-                         uint16_t *h, hipStream_t s) {
+                         uint16_t *h, hipStream_t s, const RowOrder &ord) {
     if (R_cap <= 0) return hipSuccess;
+    constexpr int kAll = 1 << 30;  // no cap: one workgroup per tile
+    // the sparse kernel's row order rides on the row-list launches only
+    const RowOrder none;
+    const RowOrder &o = rowlist ? ord : none;
     // row list: small tiles up to kSmallRows of capacity (the actual count is
     // on the device; overflow rows are a small share of the batch).  All
     // rows: the largest tiles that still fill the chip.
     const bool small = rowlist
                            ? R_cap <= kSmallRows
                            : (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_) < kFillTiles;
-    if (small && rowlist && R_cap > kTinyRows) {
+    if (small && rowlist && R_cap > kTinyRows)
         return launch_gu<GuList>(1024, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr,
-                                 nullptr, nullptr, nullptr, 0.0f, s);
-    } else if (small) {
-        hipError_t e = lds_limit_once<GuSmall::kernel>(GuSmall::LDS);
-        if (e != hipSuccess) return e;
-        const int tiles = (R_cap + GuSmall::BM_ - 1) / GuSmall::BM_ * (N / GuSmall::BN_);
-        const int grid = tiles < 1024 ? tiles : 1024;
-        hipLaunchKernelGGL(GuSmall::kernel, dim3(grid), dim3(GuSmall::NTH), GuSmall::LDS, s, x,
-                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr,
-                           nullptr, nullptr, 0.0f);
-    } else if (rowlist) {
-        hipError_t e = lds_limit_once<GuRows::kernel>(GuRows::LDS);
-        if (e != hipSuccess) return e;
-        // one workgroup per CU at most: the grid is sized for the capacity
-        // and most of it would find no rows
-        const int tiles = (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_);
-        const int grid = tiles < 256 ? tiles : 256;
-        hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
-                           wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr, nullptr,
-                           nullptr, 0.0f);
-    } else if ((R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_) >= kFillTiles) {
-        hipError_t e = lds_limit_once<GuDense::kernel>(GuDense::LDS);
-        if (e != hipSuccess) return e;
-        const int grid = (R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_);
-        hipLaunchKernelGGL(GuDense::kernel, dim3(grid), dim3(GuDense::NTH), GuDense::LDS, s, x,
-                           wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr,
-                           nullptr, nullptr, 0.0f);
-    } else {
-        // all rows, too few 256-row tiles to fill the chip: 128-row tiles
-        hipError_t e = lds_limit_once<GuRows::kernel>(GuRows::LDS);
-        if (e != hipSuccess) return e;
-        const int grid = (R_cap + GuRows::BM_ - 1) / GuRows::BM_ * (N / GuRows::BN_);
-        hipLaunchKernelGGL(GuRows::kernel, dim3(grid), dim3(GuRows::NTH), GuRows::LDS, s, x, wg_t,
-                           wu_t, K, N, rowlist, count, R_cap, M, h, nullptr, nullptr, nullptr,
-                           nullptr, 0.0f);
-    }
-    return hipGetLastError();
+                                 nullptr, nullptr, nullptr, 0.0f, s, o);
+    if (small)
+        return launch_gu<GuSmall>(1024, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr,
+                                  nullptr, nullptr, nullptr, 0.0f, s, o);
+    // a row list: one workgroup per CU at most (the grid is sized for the
+    // capacity and most of it would find no rows)
+    if (rowlist)
+        return launch_gu<GuRows>(256, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr,
+                                 nullptr, nullptr, nullptr, 0.0f, s, o);
+    if ((R_cap + GuDense::BM_ - 1) / GuDense::BM_ * (N / GuDense::BN_) >= kFillTiles)
+        return launch_gu<GuDense>(kAll, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr,
+                                  nullptr, nullptr, nullptr, 0.0f, s);
+    // all rows, too few 256-row tiles to fill the chip: 128-row tiles
+    return launch_gu<GuRows>(kAll, x, wg_t, wu_t, K, N, rowlist, count, R_cap, M, h, nullptr,
+                             nullptr, nullptr, nullptr, 0.0f, s);
 }
 
 bool dense_down_split(int M, int K) {

@@ -25,14 +25,21 @@
 //   such rows are spread over 16 waves (8 when K > 2048) that take one
 //   entry at a time; 32 to 128 rows, over G = 256 / M workgroups, each
 //   writing a partial row that row_sum_kernel adds up in a fixed order.
+// - Batches of 257 to 8192 rows start their heaviest rows first: a heavy
+//   row's chain (176 entries, 22 gathers per wave deep, in the 0.5B block)
+//   nearly spans the kernel, so one dispatched late sets its end.  The order
+//   (RowOrder in tw_internal.hpp) comes from the extra workgroups of the
+//   overflow rows' gate+up launch; workgroup b takes the b-th row of it.
+//   Every row is still computed once, by the same code, so y does not depend
+//   on the order.
 // - The dot product is reduced across the wave with DPP (no LDS), its
 //   product with g is the scalar h_j, and h_j * W_d[j] is added lane-wise.
 // - The four partial y rows are summed in LDS in a fixed order (the result
 //   does not depend on timing) and written once; the staging is laid out so
 //   that neither its stores nor its loads have bank conflicts.
 // - The overflow rows' dense path runs first.  When its down GEMM split the
-//   reduction, workgroup m also sums the partial tiles of overflow-list
-//   position m (in split order) into that row of y, so no separate
+//   reduction, workgroup b also sums the partial tiles of overflow-list
+//   position b (in split order) into that row of y, so no separate
 //   reduction kernel runs: the rows this kernel computes and the overflow
 //   rows it finishes are disjoint.
 #include "tw_device.hpp"
@@ -56,7 +63,7 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const int32_t *__restrict__ tw_idx, const int32_t *__restrict__ tw_cnt,
     float *__restrict__ y, const float *__restrict__ partial,
     const int32_t *__restrict__ ovf_rows, const int32_t *__restrict__ ovf_count, int R_max,
-    int G, float *__restrict__ rowpart) {
+    int G, float *__restrict__ rowpart, const int32_t *__restrict__ perm) {
     constexpr int kThreads = NWV * 64, kWaves = NWV;
     constexpr int kBatch = NWV >= 8 ? 1 : 2;  // active neurons gathered together per wave
     extern __shared__ __attribute__((aligned(16))) char smem[];  // y staging, fp32
@@ -65,7 +72,41 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
 
     // G workgroups per row (G = 1: one); part gs of row m
     const int M = gridDim.x / G;
-    const int m = blockIdx.x / G, gs = blockIdx.x % G;
+    const int gs = blockIdx.x % G;
+    int m = blockIdx.x / G;
+    if (perm) {
+        // heaviest first (G = 1): workgroup b takes the b-th row of "every
+        // segment's heavy rows, then every segment's other rows"; lane i
+        // scans segment i's two counts
+        const int b = blockIdx.x;
+        const int nseg = (M + kOrderSeg - 1) / kOrderSeg;
+        const int l = threadIdx.x & 63;
+        const int nh = l < nseg ? perm[l] : 0, nl = l < nseg ? perm[64 + l] : 0;
+        int ih = nh, il = nl;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int vh = __shfl_up(ih, d), vl = __shfl_up(il, d);
+            if (l >= d) {
+                ih += vh;
+                il += vl;
+            }
+        }
+        const int NH = __builtin_amdgcn_readlane(ih, 63);
+        int sg, idx;
+        if (b < NH) {
+            sg = (int)__popcll(__ballot(ih <= b));
+            idx = b - (__builtin_amdgcn_readlane(ih, sg) - __builtin_amdgcn_readlane(nh, sg));
+        } else {
+            const int bl = b - NH;
+            sg = (int)__popcll(__ballot(il <= bl));
+            idx = __builtin_amdgcn_readlane(nh, sg) + bl -
+                  (__builtin_amdgcn_readlane(il, sg) - __builtin_amdgcn_readlane(nl, sg));
+        }
+        // a corrupt order could only come from a corrupt count array: clamp
+        sg = min(sg, nseg - 1);
+        idx = min(max(idx, 0), kOrderSeg - 1);
+        m = (int)min((unsigned)perm[128 + sg * kOrderSeg + idx], (unsigned)(M - 1));
+    }
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
 
@@ -258,7 +299,7 @@ hipError_t launch_kw(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd
                      int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
                      const int32_t *tw_cnt, float *y, const float *partial,
                      const int32_t *ovf_rows, const int32_t *ovf_count, int R_max, int G,
-                     float *rowpart, hipStream_t s) {
+                     float *rowpart, const int32_t *perm, hipStream_t s) {
     const size_t lds = (size_t)NWV * KCH * 512 * sizeof(float);  // y staging
     {
         const hipError_t e = lds_limit_once<&sparse_updown_kernel<KCH, NWV>>((int)lds);
@@ -266,7 +307,7 @@ hipError_t launch_kw(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd
     }
     hipLaunchKernelGGL((sparse_updown_kernel<KCH, NWV>), dim3(M * G), dim3(NWV * 64), lds, s, x,
                        wu_t, wd, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial, ovf_rows,
-                       ovf_count, R_max, G, rowpart);
+                       ovf_count, R_max, G, rowpart, G == 1 ? perm : nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || G == 1) return e;
     hipLaunchKernelGGL(row_sum_kernel, dim3(M), dim3(256), 0, s, rowpart, G, K, NT, C, tw_cnt, y);
@@ -280,16 +321,16 @@ hipError_t launch_k(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
                     int N, int NT, int C, const float *tw_val, const int32_t *tw_idx,
                     const int32_t *tw_cnt, float *y, const float *partial,
                     const int32_t *ovf_rows, const int32_t *ovf_count, int R_max,
-                    float *rowpart, hipStream_t s) {
+                    float *rowpart, const int32_t *perm, hipStream_t s) {
     // 16 waves cap a lane at 128 registers and the y staging at 16 KCH KB:
     // wide rows take 8
     constexpr int kSmallWaves = KCH <= 4 ? 16 : 8;
     if (M <= kSmallBatchRows)
         return launch_kw<KCH, kSmallWaves>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt,
                                            y, partial, ovf_rows, ovf_count, R_max,
-                                           sparse_row_parts(M), rowpart, s);
+                                           sparse_row_parts(M), rowpart, perm, s);
     return launch_kw<KCH, 4>(x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial,
-                             ovf_rows, ovf_count, R_max, 1, rowpart, s);
+                             ovf_rows, ovf_count, R_max, 1, rowpart, perm, s);
 }
 
 }  // namespace
@@ -299,11 +340,11 @@ hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const u
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
                                 const float *partial, const int32_t *ovf_rows,
                                 const int32_t *ovf_count, int R_max, float *rowpart,
-                                hipStream_t s) {
+                                const int32_t *perm, hipStream_t s) {
     if (M == 0) return hipSuccess;
     const int NT = N / T;
 #define TW_SPARSE_ARGS x, wu_t, wd, M, K, N, NT, C, tw_val, tw_idx, tw_cnt, y, partial, ovf_rows, \
-                       ovf_count, R_max, rowpart, s
+                       ovf_count, R_max, rowpart, perm, s
     switch ((K + 511) / 512) {
     case 1: return launch_k<1>(TW_SPARSE_ARGS);
     case 2: return launch_k<2>(TW_SPARSE_ARGS);

@@ -81,8 +81,11 @@ size_t overflow_ws(int R_max, int N) {
     if (R_max == 0) return 0;
     return round_up((size_t)R_max * N * 2, 256) + tw::split_partial_bytes();
 }
+// the sparse step's workspace: the overflow rows' h and split partials, the
+// sparse kernel's partial rows (small batches), the heaviest-first row order
 size_t sparse_ws(int M, int K, int R_max, int N) {
-    return overflow_ws(R_max, N) + round_up(tw::sparse_rowpart_bytes(M, K), 256);
+    return overflow_ws(R_max, N) + round_up(tw::sparse_rowpart_bytes(M, K), 256) +
+           round_up(tw::row_order_bytes(M), 256);
 }
 
 tw_status record(void *const *events, int i, hipStream_t s) {
@@ -350,6 +353,19 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     uint16_t *h = reinterpret_cast<uint16_t *>(w);
     float *partial = reinterpret_cast<float *>(w + round_up((size_t)R_max * N * 2, 256));
     float *rowpart = reinterpret_cast<float *>(w + overflow_ws(R_max, N));
+    int32_t *perm = reinterpret_cast<int32_t *>(w + overflow_ws(R_max, N) +
+                                                 round_up(tw::sparse_rowpart_bytes(M, K), 256));
+    // heaviest-first order for the sparse kernel, written beside the
+    // overflow rows' gate+up GEMM (no launch of its own)
+    tw::RowOrder ord;
+    if (R_max > 0 && tw::sparse_heavy_first(M)) {
+        ord.tw_cnt = tw_cnt;
+        ord.M = M;
+        ord.NT = N / T;
+        ord.C = C;
+        ord.H = tw::kHeavyEntries;
+        ord.perm = perm;
+    }
     // All on the caller's stream: the overflow rows' dense path first (its
     // down GEMM leaves split partial tiles when the rows are few), then the
     // sparse kernel, which computes the other rows and sums those partials
@@ -359,7 +375,8 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     // workgroups, and the cross-stream edges cost several microseconds each.
     TW_TRY(record(events, 0, s));
     if (R_max > 0) {
-        TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, s),
+        TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, s,
+                                          ord),
                         "fallback gate+up launch"));
         TW_TRY(record(events, 1, s));
         TW_TRY(launched(tw::launch_down(h, wd, K, N, ovf_rows, ovf_count, R_max, y, partial, s),
@@ -370,7 +387,7 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     }
     TW_TRY(launched(tw::launch_sparse_updown(x, wu_t, wd, M, K, N, T, C, tw_val, tw_idx, tw_cnt,
                                              y, R_max > 0 ? partial : nullptr, ovf_rows,
-                                             ovf_count, R_max, rowpart, s),
+                                             ovf_count, R_max, rowpart, ord.perm, s),
                     "sparse_updown launch"));
     TW_TRY(record(events, 3, s));
     TW_TRY(record(events, 4, s));

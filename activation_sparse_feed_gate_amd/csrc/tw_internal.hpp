@@ -60,17 +60,49 @@ inline size_t sparse_rowpart_bytes(int M, int K) {
     return g > 1 ? (size_t)g * M * K * 4 : 0;
 }
 
+// Heaviest-first dispatch of the sparse kernel.  A row's gathers form a
+// serial chain per wave, so a heavy row that starts late sets the kernel's
+// end.  The rows are cut into segments of kOrderSeg; for each segment one
+// extra workgroup of the overflow rows' gate+up launch (running beside the
+// GEMM) lists its rows with no tile over capacity and more than H entries,
+// then its other rows, each ascending, and counts both.  Workgroup b of the
+// sparse kernel takes the b-th row of the order "every segment's heavy
+// rows, then every segment's other rows", located by a scan of the counts.
+// perm layout: int32 heavy counts [64], other counts [64], then M row slots
+// (segment s at s * kOrderSeg).
+struct RowOrder {
+    const int32_t *tw_cnt = nullptr;  // [M][NT]
+    int M = 0, NT = 0, C = 0, H = 0;
+    int32_t *perm = nullptr;          // null: no ordering
+};
+constexpr int kOrderSeg = 256;
+__host__ __device__ inline int row_order_segs(int M) { return (M + kOrderSeg - 1) / kOrderSeg; }
+inline size_t row_order_bytes(int M) { return 512 + (size_t)M * 4; }
+// Batches that take it: more than 256 rows (one workgroup per row) and at
+// most kHeavyFirstRows.  Measured (sparse kernel, unordered against
+// ordered): 38.4 against 32.8 us at the 0.5B block, 63.5 against 53.9 at
+// the paper shape, 87.9 against 79.9 at the 1B block; at 16384 rows, where
+// the kernel streams near the HBM rate, 236.9 against 242.2 (2B block) and
+// 77.3 against 86.9 (overflow-stress block).
+constexpr int kHeavyFirstRows = 8192;
+static_assert(kHeavyFirstRows <= 64 * kOrderSeg, "the counts of 64 segments");
+inline bool sparse_heavy_first(int M) { return M > 256 && M <= kHeavyFirstRows; }
+// A row is heavy with more than this many entries (measured 32.8 us at the
+// 0.5B block against 33.4 with 32 and 34.4 with 16).
+constexpr int kHeavyEntries = 64;
+
 // Sparse up + down of every non-overflow row into y.  With `partial` (the
 // split partial tiles launch_down left for the overflow list ovf_rows,
 // ovf_count, R_max), it also sums those into the listed rows of y, in place
 // of launch_split_reduce; partial null: overflow rows are left alone.
 // rowpart: sparse_rowpart_bytes(M, K) bytes (unused when that is 0).
+// perm: the heaviest-first row order (RowOrder), or null for row order.
 hipError_t launch_sparse_updown(const uint16_t *x, const uint16_t *wu_t, const uint16_t *wd,
                                 int M, int K, int N, int T, int C, const float *tw_val,
                                 const int32_t *tw_idx, const int32_t *tw_cnt, float *y,
                                 const float *partial, const int32_t *ovf_rows,
                                 const int32_t *ovf_count, int R_max, float *rowpart,
-                                hipStream_t s);
+                                const int32_t *perm, hipStream_t s);
 
 // Row-list gate+up GEMMs with a capacity of at most this many rows take
 // 128-row x 64-column tiles (256 of them at this capacity; 64 x 64 tiles up
@@ -87,9 +119,11 @@ bool dense_down_split(int M, int K);
 // x_r is x[rowlist[r]] (rowlist != nullptr, rows = min(*count, R_cap)) or
 // x[r] (rowlist == nullptr, rows = R_cap).  x has M rows; with a row list
 // M * K * 2 must stay below 4 GiB (32-bit buffer offsets).
+// With ord.perm (row lists only) one more workgroup writes the sparse
+// kernel's heaviest-first row order.
 hipError_t launch_gateup(const uint16_t *x, int M, const uint16_t *wg_t, const uint16_t *wu_t,
                          int K, int N, const int32_t *rowlist, const int32_t *count,
-                         int R_cap, uint16_t *h, hipStream_t s);
+                         int R_cap, uint16_t *h, hipStream_t s, const RowOrder &ord = RowOrder());
 
 // launch_gateup over a row list that also stores g_out[r][n] =
 // bf16(ReLU(x_r . wg_t[n])) and u_out[r][n] = bf16(x_r . wu_t[n]) where

@@ -101,6 +101,12 @@ def test_tiny_all_rows(tw, kw):
     # the sparse kernel spreads a row over 256 / M workgroups for 32 to 128 rows
     dict(M=31, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=44),
     dict(M=129, K=2048, N=8192, T=256, C=16, density=0.003, sigma_s=0.5, seed=45),
+    # heaviest-first order of the sparse kernel from 257 rows (above, and
+    # the 0.5B block sizes) up to 8192, in segments of 256 rows: its last
+    # batch size and the first without it, with a heavy tail (rows of more
+    # than 64 entries and none over capacity)
+    dict(M=8192, K=256, N=4096, T=128, C=8, density=0.01, sigma_s=0.7, seed=46),
+    dict(M=8193, K=256, N=4096, T=128, C=8, density=0.01, sigma_s=0.7, seed=47),
 ])
 def test_route_boundaries(tw, kw):
     _full_check(tw, W["tiny"].with_(**kw))
