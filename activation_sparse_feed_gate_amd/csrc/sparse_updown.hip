@@ -74,6 +74,7 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const int M = gridDim.x / G;
     const int gs = blockIdx.x % G;
     int m = blockIdx.x / G;
+    int lead = 0;  // workgroups before the first light row of the order
     if (perm) {
         // heaviest first (G = 1): workgroup b takes the b-th row of "every
         // segment's heavy rows, then every segment's other rows"; lane i
@@ -92,6 +93,7 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
             }
         }
         const int NH = __builtin_amdgcn_readlane(ih, 63);
+        lead = NH;
         int sg, idx;
         if (b < NH) {
             sg = (int)__popcll(__ballot(ih <= b));
@@ -113,8 +115,12 @@ __global__ __launch_bounds__(NWV * 64) void sparse_updown_kernel(
     const int c = tid < NT ? tw_cnt[(size_t)m * NT + tid] : 0;
     if (partial) {
         // overflow-list position p: its split partial tiles, summed in split
-        // order into its row of y (S = 1: the down GEMM stored the row)
-        const int p = blockIdx.x;
+        // order into its row of y (S = 1: the down GEMM stored the row).  In
+        // the heaviest-first order the duty starts at the first light row
+        // (a rotation of the workgroup index, so every position still has
+        // exactly one workgroup), off the heavy rows' chains.
+        const int p = lead ? (int)(((unsigned)blockIdx.x + (unsigned)(M - lead)) % (unsigned)M)
+                           : (int)blockIdx.x;
         const int rows = __builtin_amdgcn_readfirstlane(min(*ovf_count, R_max));
         if (p < rows) {
             const int S = split_factor(rows, K, N);
