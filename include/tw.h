@@ -208,7 +208,10 @@ tw_status tw_pack_dense(const float *z, int M, int N, int T, int C,
  * depend on timing) into the listed rows.  The two sets of rows are
  * disjoint.  Batches of 32 to 128 rows spread each row over several
  * workgroups, whose partial rows (in the workspace) a last small kernel
- * sums in a fixed order.
+ * sums in a fixed order.  Batches of 257 to 8192 rows (with R_max > 0)
+ * start their heaviest rows first, in an order that extra workgroups of the
+ * gate+up launch write to the workspace from tw_cnt; each row is still
+ * computed once by the same code, so y does not depend on the order.
  */
 tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t,
                             const uint16_t *wu_t, const uint16_t *wd,
