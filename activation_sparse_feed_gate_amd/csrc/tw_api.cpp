@@ -370,9 +370,10 @@ tw_status tw_sparse_ffn_fwd(const uint16_t *x, const uint16_t *wg_t, const uint1
     // down GEMM leaves split partial tiles when the rows are few), then the
     // sparse kernel, which computes the other rows and sums those partials
     // into the overflow rows.  Running the two paths concurrently on a
-    // second stream was measured slower at the smaller shapes: the dense
-    // kernels' large LDS tiles cannot sit beside the sparse kernel's
-    // workgroups, and the cross-stream edges cost several microseconds each.
+    // second stream (the split partials then summed there) was measured: the
+    // sparse kernel's workgroups take the CUs first, so little of the dense
+    // path overlaps; warm steps gained 1-7% but the 0.5B block's cold step
+    // none, and the library would have to hold streams and events.
     TW_TRY(record(events, 0, s));
     if (R_max > 0) {
         TW_TRY(launched(tw::launch_gateup(x, M, wg_t, wu_t, K, N, ovf_rows, ovf_count, R_max, h, s,
