@@ -494,9 +494,11 @@ def measure(args, w, torch, tw, hev, clocks, full: bool):
 
     M, K, N, T, C = w.M, w.K, w.N, w.T, w.C
     # overflow capacity: the static backup capacity of the review §4-3 (an
-    # eighth of the batch); if the batch overflows it, the retry rule there
-    # (read the true count on the host, allocate more) runs before timing
-    R_max = min(M, args.r_max) if args.r_max is not None else max(1, M // 8)
+    # eighth of the batch, rounded down: none below 8 tokens, so a decode
+    # step launches no backup kernels unless it overflows); if the batch
+    # overflows it, the retry rule there (read the true count on the host,
+    # allocate more) runs before timing
+    R_max = min(M, args.r_max) if args.r_max is not None else M // 8
     d = synth.make_inputs(w)
 
     def dev(bits):
