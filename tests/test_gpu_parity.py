@@ -141,6 +141,12 @@ def test_density_extremes(tw, kw):
     (dict(C=12), 8),                                     # ~7 listed rows of 8
     (dict(M=64, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5), 8),  # 0.5B block
     (dict(M=16, K=2048, N=8192, T=256, C=16, density=0.01, sigma_s=0.5, seed=9), 2),
+    # a capacity of none (an eighth of a batch under 8 tokens, rounded down):
+    # no backup kernel runs; without overflow every row is the sparse
+    # kernel's, with overflow the listed rows are left for the retry
+    (dict(M=4, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=52), 0),
+    (dict(M=7, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=51), 0),
+    (dict(M=7, C=4), 0),                                 # every row overflows
 ])
 def test_few_overflow_rows(tw, kw, R_max):
     """A backup capacity of a handful of rows (decode-size batches): the
