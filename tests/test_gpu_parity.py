@@ -126,15 +126,19 @@ def test_maximum_sizes(tw, kw):
 @pytest.mark.parametrize("kw", [
     dict(density=0.0), dict(density=1.0, C=128), dict(density=1.0, C=16),
     dict(density=1.0, T=256, C=256),
+    # 1024 rows take the sparse kernel's heaviest-first order: no heavy row
+    # at all, and every row heavy with none over capacity
+    dict(M=1024, density=0.0), dict(M=1024, density=1.0, C=128),
 ])
 def test_density_extremes(tw, kw):
     g, _ = _full_check(tw, W["tiny"].with_(**kw))
+    M = kw.get("M", 64)
     if kw["density"] == 0.0:
         assert not g["tw_cnt"].any() and g["ovf_count"] == 0 and not g["y"].any()
     elif kw["C"] == kw.get("T", 128):
         assert (g["tw_cnt"] == kw.get("T", 128)).all() and g["ovf_count"] == 0
     else:
-        assert g["ovf_count"] == 64
+        assert g["ovf_count"] == M
 
 
 @pytest.mark.parametrize("kw,R_max", [
