@@ -151,6 +151,9 @@ def test_density_extremes(tw, kw):
     (dict(M=4, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=52), 0),
     (dict(M=7, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=51), 0),
     (dict(M=7, C=4), 0),                                 # every row overflows
+    # the heaviest-first order (1024 rows) with a room smaller than the
+    # overflow list: the rows past it are left for the retry
+    (dict(M=1024, K=1024, N=4096, T=128, C=8, density=0.01, sigma_s=0.5, seed=53), 16),
 ])
 def test_few_overflow_rows(tw, kw, R_max):
     """A backup capacity of a handful of rows (decode-size batches): the
