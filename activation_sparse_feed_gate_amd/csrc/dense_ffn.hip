@@ -320,6 +320,15 @@ struct DN {
 // positions of one 256-byte bank row, i.e. all 64 banks once.
 __device__ __forceinline__ int bsw(int row) { return 4 * (row & 3); }
 
+// Row regions of the unsplit down GEMM's tile grid over the XCDs.  Its A
+// operand h ([rows][N]) is the larger one (4x W_d at the 0.5B and 2B
+// blocks), so 4 row regions x 2 column regions, each h row block read by
+// two XCDs, beat the 2 x 4 regions that suit the gate (each h row block
+// read by four): measured 450.7-453.1 against 467.7-470.3 us at the 2B
+// block and 39.4-39.7 against 40.1-40.3 us at the 0.5B block; 8 x 1
+// regions lay between.
+constexpr int kDownRX = 4;
+
 // PAIRS = 2: y = h W_d + h2 W_d2, the reduction running over the first pair's
 // stages, then the second's (same shapes), in one GEMM.
 template <int BM, int BN, int WM, int WN, int STG, int PAIRS>
@@ -346,9 +355,17 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
     const int g4 = (lane >> 4) & 3, i16 = lane & 15;
 
     for (int wi = blockIdx.x; wi < work; wi += gridDim.x) {
-        const int tile = wi % tiles, sp = wi / tiles;
+        // Work items are dealt to the XCDs round-robin (workgroup index % 8).
+        // Split-major items (sp = wi % S) give each XCD whole splits: the
+        // h and W_d slices of one split, read by all of that split's tiles,
+        // then come into one XCD's L2 once.  Tile-major items put one row
+        // block on each XCD, and every W_d slice came from beyond the L2
+        // once per row block: 40.0 MB fetched per launch at the 0.5B block
+        // against 11.7 MB split-major, the size of the operands (same
+        // results to the bit: only the workgroup of each item changes).
+        const int tile = wi / S, sp = wi % S;
         int rb, cb;
-        if (S == 1 && !rowlist) xcd_tile(tile, nrb, ncb, rb, cb);
+        if (S == 1 && !rowlist) xcd_tile<kDownRX>(tile, nrb, ncb, rb, cb);
         else { rb = tile % nrb; cb = tile / nrb; }
         const int m0 = rb * BM, k0 = cb * BN;
         const int kt0 = sp * (NS / S), kt1 = kt0 + NS / S;
@@ -454,13 +471,16 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
             }
         } else {
             // partial tile of split sp, summed in split order later (split_reduce_kernel,
-            // or the sparse kernels that take the listed rows; tw_split.hpp)
+            // or the sparse kernels that take the listed rows; tw_split.hpp).
+            // Those read only rows below the count, so rows past it are not
+            // stored.
             float *pt = partial + ((size_t)sp * tiles + tile) * (BM * BN);
 #pragma unroll
             for (int a = 0; a < P::FA; ++a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int rl = wm * P::TM + a * 32 + mfma32_row(i, lane);
+                    if (m0 + rl >= rows) continue;
 #pragma unroll
                     for (int b = 0; b < P::FB; ++b)
                         pt[rl * BN + wn * P::TN + b * 32 + l32] = acc[a][b][i];

@@ -69,20 +69,25 @@ __device__ __forceinline__ void settle_scalars(P... p) {
 
 // Output tile (bm, bn) of tile index t in an nbm x nbn grid, XCD-aware.
 // Workgroups are dealt round-robin to the 8 XCDs (index % 8), and each XCD
-// has its own L2.  When the grid splits evenly, XCD x gets one of 2 x 4
-// regions of the grid, walked in groups of up to 8 row blocks column block
-// by column block, so that the ~32 workgroups resident on one XCD share a
-// few A row blocks and B column blocks in its L2.  Otherwise the whole grid
-// is walked in such groups.
+// has its own L2.  When the grid splits evenly, XCD x gets one of RX x (8 /
+// RX) regions of the grid, walked in groups of up to 8 row blocks column
+// block by column block, so that the ~32 workgroups resident on one XCD
+// share a few A row blocks and B column blocks in its L2.  Each A row block
+// then comes into 8 / RX XCDs and each B column block into RX of them, so a
+// GEMM whose A operand is the larger takes more row regions.  Otherwise the
+// whole grid is walked in such groups.
+template <int RX = 2>
 __device__ __forceinline__ void xcd_tile(int t, int nbm, int nbn, int &bm, int &bn) {
+    static_assert(RX == 1 || RX == 2 || RX == 4 || RX == 8, "regions of the 8 XCDs");
+    constexpr int CX = 8 / RX;
     int r0m = 0, r0n = 0, rm = nbm, rn = nbn, local = t;
-    if ((nbm & 1) == 0 && (nbn & 3) == 0) {
+    if (nbm % RX == 0 && nbn % CX == 0) {
         const int x = t & 7;
         local = t >> 3;
-        rm = nbm >> 1;
-        rn = nbn >> 2;
-        r0m = (x >> 2) * rm;
-        r0n = (x & 3) * rn;
+        rm = nbm / RX;
+        rn = nbn / CX;
+        r0m = (x / CX) * rm;
+        r0n = (x % CX) * rn;
     }
     constexpr int G = 8;
     const int group = local / (G * rn);
