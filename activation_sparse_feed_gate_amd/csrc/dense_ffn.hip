@@ -320,14 +320,18 @@ struct DN {
 // positions of one 256-byte bank row, i.e. all 64 banks once.
 __device__ __forceinline__ int bsw(int row) { return 4 * (row & 3); }
 
-// Row regions of the unsplit down GEMM's tile grid over the XCDs.  Its A
-// operand h ([rows][N]) is the larger one (4x W_d at the 0.5B and 2B
-// blocks), so 4 row regions x 2 column regions, each h row block read by
-// two XCDs, beat the 2 x 4 regions that suit the gate (each h row block
-// read by four): measured 450.7-453.1 against 467.7-470.3 us at the 2B
-// block and 39.4-39.7 against 40.1-40.3 us at the 0.5B block; 8 x 1
-// regions lay between.
-constexpr int kDownRX = 4;
+// Row regions of the unsplit down GEMM's tile grid over the XCDs, by tile
+// height.  Its A operand h ([rows][N]) is the larger one (4x W_d at the
+// 0.5B and 2B blocks).  With 256-row tiles (the 2B block), 4 row regions x
+// 2 column regions (each h row block read by two XCDs) beat the 2 x 4 that
+// suit the gate (each read by four): 450.7-453.1 against 467.7-470.3 us,
+// cold dense step 1386.5-1387.8 against 1409.4-1410.0 us.  With 128-row
+// tiles they cost more than they save on a cold step, when every W_d column
+// block then comes from HBM into four XCDs at once: 512.8-516.6 against
+// 499.4-500.2 us at the 1B block, 335.5-338.9 against 318.2-318.6 us at the
+// paper's block width.
+template <int BM>
+constexpr int down_rx() { return BM >= 256 ? 4 : 2; }
 
 // PAIRS = 2: y = h W_d + h2 W_d2, the reduction running over the first pair's
 // stages, then the second's (same shapes), in one GEMM.
@@ -365,7 +369,7 @@ __global__ __launch_bounds__(WM * WN * 64) void down_kernel(
         // results to the bit: only the workgroup of each item changes).
         const int tile = wi / S, sp = wi % S;
         int rb, cb;
-        if (S == 1 && !rowlist) xcd_tile<kDownRX>(tile, nrb, ncb, rb, cb);
+        if (S == 1 && !rowlist) xcd_tile<down_rx<BM>()>(tile, nrb, ncb, rb, cb);
         else { rb = tile % nrb; cb = tile / nrb; }
         const int m0 = rb * BM, k0 = cb * BN;
         const int kt0 = sp * (NS / S), kt1 = kt0 + NS / S;
