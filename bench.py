@@ -96,6 +96,18 @@ def _traffic(kernel: str, src: str, workload: str):
     return float(rec["bytes_per_launch"])
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, w, budget_s: float):
     """The oracle's own TwELL forward (gate, packing, sparse evaluation with
     the dense recompute of overflow rows) on an evenly strided row sample."""
@@ -133,7 +145,7 @@ def cpu_baseline(d, w, budget_s: float):
     orc.dense_ffn(xs[:nd], wg, wu, wd)
     dsecs = time.perf_counter() - t
     return {"value": passes * len(rows) / secs, "unit": "tokens/s", "cores": orc.threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": _cpu_model(),
             "sample": f"{len(rows)} of {w.M} token rows, evenly strided, {passes} pass(es); "
                       f"float64 gate, TwELL packing, sparse up+down with dense recompute of "
                       f"overflow rows; {secs:.1f} s",
