@@ -33,7 +33,9 @@
  *   caller owns.  The library allocates no device memory and keeps no
  *   state between calls, so calls on different streams may run
  *   concurrently as long as their output and workspace buffers are
- *   distinct.
+ *   distinct.  The one exception is tw_pack_gate_noalloc, whose workspace
+ *   is a static device array inside the library, shared by every call on
+ *   one GPU (see its declaration).
  * - All work is enqueued asynchronously on `stream` (a hipStream_t passed as
  *   void*; NULL is the default stream).  Nothing synchronises the host.
  * - Argument and shape errors are detected on the host before any work is

@@ -1,9 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
-Small shapes are compared on every row; the full-size workloads are compared
-on all rows for the packing (the oracle re-packs the GPU's own gate) and on
-sampled rows -- evenly spaced, overflowing and the heaviest sparse rows --
-for the gate, the index sets and the output.
+Every case is compared on every row: the packing bit for bit (the oracle
+re-packs the GPU's own gate), the gate within its dot-product rounding bound,
+the index sets against the oracle's float64 gate, and the output within the
+output tolerance, at small shapes and at every full-size workload.
 """
 import numpy as np
 import pytest
