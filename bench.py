@@ -88,12 +88,16 @@ def _src_sha(name: str) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(kernel: str, src: str, workload: str):
+def _traffic(kernel: str, src: str, w, registered: dict, r_max_override=None):
     """HBM bytes per launch from committed rocprofv3 counter summaries, only
-    when they were taken on the current kernel source and this workload."""
+    when they were taken on the current kernel source and this workload:
+    the profiles cover the registered workloads at the default backup
+    capacity, so a density, batch-size or capacity override gives None."""
+    if r_max_override is not None or registered.get(w.name) != w:
+        return None
     try:
         with open(PROFILE_TRAFFIC) as f:
-            rec = json.load(f)[workload][kernel]
+            rec = json.load(f)[w.name][kernel]
     except (OSError, KeyError, ValueError):
         return None
     if rec.get("src_sha") != _src_sha(src):
@@ -799,7 +803,7 @@ def measure(args, w, torch, tw, hev, clocks, full: bool):
                  "frac": a / PEAK_HBM_GBS}
         r["kernel"] = name
         r["avg_us"] = secs * 1e6
-        r["traffic"] = _traffic(name, srcs[name], w.name)
+        r["traffic"] = _traffic(name, srcs[name], w, synth.WORKLOADS, args.r_max)
         if r["traffic"] is not None:
             # the bytes the counters saw leave or enter HBM, per launch, over
             # the same duration: measured DRAM throughput beside the
