@@ -750,7 +750,19 @@ def measure(args, w, torch, tw, hev, clocks, full: bool):
     for _ in range(3):
         blas_ffn()
     t_blas = timed(lambda i: blas_ffn())
-    del wgu
+    # the two bare hipBLASLt products alone (no ReLU product, no bf16
+    # rounding of h in between): a lower bound for any dense FFN built on
+    # them; the down product reads this batch's own h (as sparse as ours)
+    h_bl = (torch.relu(x @ wg.t()) * (x @ wu.t())).to(torch.bfloat16)
+
+    def blas_gemms():
+        x @ wgu.t()
+        h_bl @ wd_row
+
+    for _ in range(3):
+        blas_gemms()
+    t_blas_bare = timed(lambda i: blas_gemms())
+    del wgu, h_bl
 
     def avg(evl, i):
         return sum(hev.ms(e[i], e[i + 1]) for e in evl) / len(evl) * 1e-3  # seconds
@@ -846,6 +858,12 @@ def measure(args, w, torch, tw, hev, clocks, full: bool):
                             "speedup_vs": t_blas / t_cs,
                             "note": "torch.matmul gate+up GEMM, ReLU*u in torch, bf16 h, "
                                     "torch.matmul down, back to back (warm)"},
+        "hipblaslt_bare_gemms": {"ms_per_step": t_blas_bare * 1e3,
+                                 "speedup_vs_cold_step": t_blas_bare / t_cs,
+                                 "speedup_vs_warm_step": t_blas_bare / t_sparse,
+                                 "note": "the gate+up and down torch.matmul products alone, "
+                                         "back to back (warm): a lower bound for a dense FFN "
+                                         "on hipBLASLt, not a complete FFN"},
         "kernels_us": {k: v * 1e6 for k, v in {**kern, **kern_dense}.items()},
         "stages": stages,
         "realized": {"density": float(nnz.sum()) / (M * N), "overflow_rows": R,
