@@ -389,7 +389,7 @@ def hybrid_backward_bench(args, tw, torch, w, x, wg, wu, wdn, hy, Rh, P, hev):
 # Workloads measured besides the headline (SURVEY's headline set: every block
 # at >= 99% sparsity, and the 2B shape at 0% and 5% density for the crossover).
 SIDE_CONFIGS = [("ffn-1b", None), ("ffn-2b", None), ("ffn-ovf", None), ("ffn-2b", 0.0),
-                ("ffn-2b", 0.05)]
+                ("ffn-2b", 0.05), ("ffn-paper", None)]
 
 
 class ClockSampler:
