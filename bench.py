@@ -386,8 +386,9 @@ def hybrid_backward_bench(args, tw, torch, w, x, wg, wu, wdn, hy, Rh, P, hev):
                     "the same backward on torch.matmul from dense bf16 g and u"}
 
 
-# Workloads measured besides the headline (SURVEY's headline set: every block
-# at >= 99% sparsity, and the 2B shape at 0% and 5% density for the crossover).
+# Workloads measured besides the headline: every other block at >= 99%
+# sparsity, the 2B shape at 0% and 5% density (the crossover), and the pages'
+# own block width.
 SIDE_CONFIGS = [("ffn-1b", None), ("ffn-2b", None), ("ffn-ovf", None), ("ffn-2b", 0.0),
                 ("ffn-2b", 0.05), ("ffn-paper", None)]
 
