@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -207,3 +208,22 @@ def test_pack_gate_noalloc_rejects(tw):
     assert NA(x=P + 8) == 1 and NA(K=192) == 2
     assert NA(M=524287, K=4096, N=65536, T=256, R=0) == 2
     assert b"static scratch" in L.tw_last_error()
+
+
+def test_binding_fails_loudly_without_the_library():
+    """With libtw.so absent the binding raises ImportError naming the build
+    step: there is no fallback path (checked in a child process that hides
+    the built library from the loader's existence check)."""
+    code = ("import os, sys\n"
+            "real = os.path.exists\n"
+            "os.path.exists = lambda p: False if str(p).endswith('libtw.so') else real(p)\n"
+            "try:\n"
+            "    import activation_sparse_feed_gate_amd.tw\n"
+            "except ImportError as e:\n"
+            "    print('IMPORT-ERROR', e)\n"
+            "    sys.exit(0)\n"
+            "sys.exit(3)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "IMPORT-ERROR" in r.stdout and "libtw.so is missing" in r.stdout
