@@ -130,8 +130,14 @@ tw_status check_pack_args(const uint16_t *x, const uint16_t *wg_t, int M, int K,
     TW_NEED_M(tw_val);
     TW_NEED_M(tw_idx);
     TW_NEED_M(tw_cnt);
-    TW_NEED(ovf_rows);
-    TW_NEED(ovf_count);
+    // both NULL: no overflow list is built (callers that route rows from
+    // tw_cnt themselves)
+    if (!ovf_rows != !ovf_count)
+        return fail(TW_EINVAL, "ovf_rows and ovf_count must both be given or both be NULL");
+    if (ovf_rows) {
+        TW_NEED(ovf_rows);
+        TW_NEED(ovf_count);
+    }
     if (z_debug && !aligned16(z_debug)) return fail(TW_EINVAL, "z_debug is not 16-byte aligned");
     return TW_OK;
 }
@@ -152,9 +158,10 @@ tw_status pack_gate_launch(const uint16_t *x, const uint16_t *wg_t, int M, int K
                                           z_debug, part, s),
                     "gate_twell launch"));
     TW_TRY(record(events, 1, s));
-    TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_flag_blocks(M, N, T), tw::row_words(M),
-                                           R_max, ovf_rows, ovf_count, s),
-                    "ovf_compact launch"));
+    if (ovf_rows)
+        TW_TRY(launched(tw::launch_ovf_compact(oflag, tw::gate_flag_blocks(M, N, T),
+                                               tw::row_words(M), R_max, ovf_rows, ovf_count, s),
+                        "ovf_compact launch"));
     TW_TRY(record(events, 2, s));
     return TW_OK;
 }

@@ -146,6 +146,14 @@ class _Args:
         if t is not None:
             self.shape(t, name, dtype, shape)
 
+    def overflow_list(self, ovf_rows, ovf_count, R_max):
+        """The overflow list of tw_pack_gate: both tensors, or both None (no
+        list is built)."""
+        if ovf_rows is None and ovf_count is None:
+            return
+        self.room(ovf_rows, "ovf_rows", _I32, max(R_max, 1))
+        self.room(ovf_count, "ovf_count", _I32, 1)
+
     def room(self, t, name, dtype, n):
         """t must be one-dimensional with at least n elements."""
         if t is None:
@@ -210,8 +218,7 @@ def tw_pack_gate(x, wg_t, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_count, R_m
     a.shape(tw_val, "tw_val", _F32, (M, NT, C))
     a.shape(tw_idx, "tw_idx", _I32, (M, NT, C))
     a.shape(tw_cnt, "tw_cnt", _I32, (M, NT))
-    a.room(ovf_rows, "ovf_rows", _I32, max(R_max, 1))
-    a.room(ovf_count, "ovf_count", _I32, 1)
+    a.overflow_list(ovf_rows, ovf_count, R_max)
     a.opt(z_debug, "z_debug", _F32, (M, N))
     a.bytes(ws, "ws")
     ev = _events(events)
@@ -234,8 +241,7 @@ def tw_pack_gate_noalloc(x, wg_t, T, C, tw_val, tw_idx, tw_cnt, ovf_rows, ovf_co
     a.shape(tw_val, "tw_val", _F32, (M, NT, C))
     a.shape(tw_idx, "tw_idx", _I32, (M, NT, C))
     a.shape(tw_cnt, "tw_cnt", _I32, (M, NT))
-    a.room(ovf_rows, "ovf_rows", _I32, max(R_max, 1))
-    a.room(ovf_count, "ovf_count", _I32, 1)
+    a.overflow_list(ovf_rows, ovf_count, R_max)
     a.opt(z_debug, "z_debug", _F32, (M, N))
     ev = _events(events)
     st = _lib.tw_pack_gate_noalloc(_ptr(x), _ptr(wg_t), M, K, N, T, C, _ptr(tw_val),

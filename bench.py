@@ -182,8 +182,9 @@ def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, st
     def hstep(ev=None, st=stream):
         # st=None: the current stream (the capture stream inside a graph capture)
         e = ev or (None, None, None, None)
+        # no overflow list: the hybrid packing routes rows from the counts
         tw.tw_pack_gate(x, wg, T, C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"],
-                        bufs["ovf_rows"], bufs["ovf_count"], R_max, ws, stream=st, events=e[0])
+                        None, None, R_max, ws, stream=st, events=e[0])
         tw.tw_hybrid_pack(T, C, bufs["tw_val"], bufs["tw_idx"], bufs["tw_cnt"], P, hy["hy_g"],
                           hy["hy_idx"], hy["hy_cnt"], hy["route"], hy["bk_rows"], hy["bk_count"],
                           Rh, stream=st, events=e[1])
@@ -237,7 +238,7 @@ def hybrid_forward_bench(args, tw, torch, w, x, wg, wu, wdn, bufs, ws, R_max, st
     def avg(j, i):
         return sum(hev.ms(e[j][i], e[j][i + 1]) for e in evl) / len(evl) * 1e-3
 
-    kern = {"gate_twell": avg(0, 0), "ovf_compact": avg(0, 1), "hybrid_pack": avg(1, 0),
+    kern = {"gate_twell": avg(0, 0), "hybrid_pack": avg(1, 0),
             "route_compact": avg(1, 1), "hybrid_up": avg(2, 0), "backup_gateup": avg(2, 1),
             "backup_down": avg(3, 0), "hybrid_down": avg(3, 1)}
     for e in evl:

@@ -129,6 +129,11 @@ size_t tw_workspace_bytes(int M, int K, int N, int T, int C, int R_max);
  *   z_debug  [M][N]          fp32 out, or NULL; receives z itself (the same
  *                            values the packing used) -- for tests
  *   ws       workspace of ws_bytes >= tw_workspace_bytes(M, K, N, T, C, R_max)
+ *
+ * ovf_rows and ovf_count may both be NULL (one alone is TW_EINVAL): then no
+ * overflow list is built and the compaction kernel does not run (events[2]
+ * is recorded right after events[1]).  tw_sparse_ffn_fwd needs the list;
+ * the training path does not (tw_hybrid_pack routes rows from tw_cnt).
  */
 tw_status tw_pack_gate(const uint16_t *x, const uint16_t *wg_t,
                        int M, int K, int N, int T, int C,

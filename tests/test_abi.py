@@ -95,6 +95,10 @@ def _pack(tw, M=64, K=256, N=1024, T=128, C=16, R=64, ws=1 << 20, **ptrs):
     (dict(M=-1), 1), (dict(K=0), 1), (dict(x=None), 1), (dict(wg=None), 1), (dict(val=None), 1),
     (dict(n=None), 1), (dict(w=None), 1), (dict(x=P + 8), 1), (dict(z=P + 4), 1), (dict(ws=16), 1),
     (dict(N=128 * 300), 2), (dict(M=1 << 20, K=4096, R=0), 2), (dict(M=1 << 19, K=4096, R=0), 2),
+    # the overflow list: both pointers or neither, and with neither the other
+    # checks still apply
+    (dict(ovf=None), 1), (dict(ovf=P + 4), 1), (dict(ovf=None, n=None, C=0), 1),
+    (dict(ovf=None, n=None, x=None), 1),
 ])
 def test_pack_rejects(tw, kw, code):
     assert _pack(tw, **kw) == code

@@ -38,6 +38,8 @@ def pack_args(**over):
     (dict(tw_cnt=e(M - 1, NT, dtype=I32)), "tw_cnt"),
     (dict(ovf_rows=e(R - 1, dtype=I32)), "ovf_rows"),  # shorter than R_max
     (dict(ovf_count=e(0, dtype=I32)), "ovf_count"),
+    (dict(ovf_rows=None), "ovf_rows is required"),    # the list needs both or neither
+    (dict(ovf_count=None), "ovf_count is required"),
     (dict(wg_t=e(N, K + 128, dtype=BF)), "wg_t"),
     (dict(tw_val=e(M, NT, C, dtype=torch.float64)), "tw_val"),
     (dict(tw_idx=e(M, NT, C, dtype=torch.int64)), "tw_idx"),
@@ -55,6 +57,9 @@ def test_pack_gate_valid_shapes_reach_the_device_check(tw):
     # every shape right: the only complaint left is that these are host tensors
     with pytest.raises(ValueError, match="device tensors"):
         tw.tw_pack_gate(**pack_args())
+    # without an overflow list (both None) likewise
+    with pytest.raises(ValueError, match="device tensors"):
+        tw.tw_pack_gate(**pack_args(ovf_rows=None, ovf_count=None))
 
 
 def sparse_args(**over):

@@ -230,3 +230,35 @@ def test_hybrid_forward_wrapper(tw):
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
     assert int(hy1["bk_count"].cpu()[0]) > 0
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", dict(C=12)),
+    ("ffn-2b", dict(M=16)),      # the small-batch gate's K-sliced route
+    ("ffn-0.5b", dict()),
+])
+def test_pack_gate_without_overflow_list(tw, name, kw):
+    """tw_pack_gate with no overflow list (both pointers NULL, as the
+    training path calls it: tw_hybrid_pack routes from tw_cnt) writes the
+    same TwELL packing, bit for bit, as with the list."""
+    import torch
+
+    w = W[name].with_(**kw)
+    print(f"case {w}", flush=True)
+    dev = parity.upload(synth.make_inputs(w))
+    M, R_max = w.M, w.M
+    a = tw.pack_gate(dev["x"], dev["wg_t"], w.T, w.C, R_max)
+    b = tw.alloc_pack(M, w.N, w.T, w.C, R_max)
+    for k in ("tw_val", "tw_idx"):
+        b[k].fill_(-7)
+    ws = tw.workspace(M, w.K, w.N, w.T, w.C, R_max)
+    tw.tw_pack_gate(dev["x"], dev["wg_t"], w.T, w.C, b["tw_val"], b["tw_idx"], b["tw_cnt"],
+                    None, None, R_max, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a["tw_cnt"], b["tw_cnt"])
+    C = w.C
+    used = (torch.arange(C, device="cuda")[None, None, :] <
+            torch.clamp(a["tw_cnt"], max=C)[:, :, None])
+    assert torch.equal(torch.where(used, a["tw_idx"], -1), torch.where(used, b["tw_idx"], -1))
+    assert torch.equal(torch.where(used, a["tw_val"], 0).view(torch.int32),
+                       torch.where(used, b["tw_val"], 0).view(torch.int32))
