@@ -569,41 +569,36 @@ hipError_t launch_gate_small(const uint16_t *x, const uint16_t *wg_t, int M, int
 }
 
 // Ascending list of the rows whose bit is set in any column block.  One
-// workgroup, 1024 words (32768 rows) at a time: the (word, column block)
-// pairs of a chunk are spread over all threads, each issuing its loads
-// before ORing them into LDS, so the kernel waits for memory about once per
-// chunk; then a block-wide scan of the words' popcounts gives every set bit
-// its list position.
-__global__ __launch_bounds__(1024) void ovf_compact_kernel(const uint32_t *__restrict__ oflag,
-                                                           int NB, int MW, int R_max,
-                                                           int32_t *__restrict__ ovf_rows,
-                                                           int32_t *__restrict__ ovf_count) {
-    __shared__ uint32_t s_or[1024];
-    __shared__ int s_wsum[16];
+// workgroup of 512 threads, 512 words (16384 rows) at a time: thread t ORs
+// word base + t over the column blocks itself (consecutive threads read
+// consecutive words of a block, and up to 32 blocks' loads are in flight
+// before any is used, so a chunk costs one memory round trip up to 32
+// column blocks), then a block-wide scan of the words' popcounts gives every
+// set bit its list position.
+constexpr int kCompactThreads = 512;
+constexpr int kCompactLoads = 32;  // column blocks loaded together
+
+__global__ __launch_bounds__(kCompactThreads) void ovf_compact_kernel(
+    const uint32_t *__restrict__ oflag, int NB, int MW, int R_max,
+    int32_t *__restrict__ ovf_rows, int32_t *__restrict__ ovf_count) {
+    constexpr int kWaves = kCompactThreads / 64;
+    __shared__ int s_wsum[kWaves];
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     int running = 0;
-    for (int base = 0; base < MW; base += 1024) {
-        const int cw = min(1024, MW - base);  // words in this chunk
-        const int pairs = cw * NB;
-        s_or[tid] = 0u;
-        __syncthreads();
-        for (int i0 = tid; i0 < pairs; i0 += 4 * 1024) {
-            uint32_t v[4];
-            int wl[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * 1024;
-                wl[u] = i % cw;
-                v[u] = i < pairs ? oflag[(size_t)(i / cw) * MW + base + wl[u]] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (v[u]) atomicOr(&s_or[wl[u]], v[u]);
-        }
-        __syncthreads();
+    for (int base = 0; base < MW; base += kCompactThreads) {
         const int w = base + tid;
-        uint32_t word = tid < cw ? s_or[tid] : 0u;
+        uint32_t word = 0u;
+        if (w < MW) {
+            for (int b0 = 0; b0 < NB; b0 += kCompactLoads) {
+                uint32_t v[kCompactLoads];
+#pragma unroll
+                for (int u = 0; u < kCompactLoads; ++u)
+                    v[u] = b0 + u < NB ? oflag[(size_t)(b0 + u) * MW + w] : 0u;
+#pragma unroll
+                for (int u = 0; u < kCompactLoads; ++u) word |= v[u];
+            }
+        }
         const int c = __popc(word);
         int incl = c;
 #pragma unroll
@@ -614,7 +609,8 @@ __global__ __launch_bounds__(1024) void ovf_compact_kernel(const uint32_t *__res
         if (lane == 63) s_wsum[wave] = incl;
         __syncthreads();
         int wbase = 0, total = 0;
-        for (int q = 0; q < 16; ++q) {
+#pragma unroll
+        for (int q = 0; q < kWaves; ++q) {
             const int v = s_wsum[q];
             if (q < wave) wbase += v;
             total += v;
@@ -627,7 +623,7 @@ __global__ __launch_bounds__(1024) void ovf_compact_kernel(const uint32_t *__res
             ++pos;
         }
         running += total;
-        __syncthreads();
+        __syncthreads();  // s_wsum is rewritten for the next chunk
     }
     if (tid == 0) *ovf_count = running;
 }
@@ -699,8 +695,8 @@ hipError_t launch_gate_dense(const uint16_t *x, const uint16_t *wg_t, int M, int
 
 hipError_t launch_ovf_compact(const uint32_t *oflag, int NB, int MW, int R_max,
                               int32_t *ovf_rows, int32_t *ovf_count, hipStream_t s) {
-    hipLaunchKernelGGL(ovf_compact_kernel, dim3(1), dim3(1024), 0, s, oflag, NB, MW, R_max,
-                       ovf_rows, ovf_count);
+    hipLaunchKernelGGL(ovf_compact_kernel, dim3(1), dim3(kCompactThreads), 0, s, oflag, NB, MW,
+                       R_max, ovf_rows, ovf_count);
     return hipGetLastError();
 }
 
